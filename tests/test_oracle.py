@@ -1,0 +1,432 @@
+"""Pins for the CPU oracle: each check compares it with something other than itself.
+
+Brute force with Python integers / fractions, closed forms, the pages' printed
+mappings (tests/golden), invariants and negative controls. CPU only.
+"""
+import os
+import struct
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import formats, quant, reference
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden_rows(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+# ------------------------------------------------------------------ decode
+def _digits_base4(b):
+    out = []
+    for _ in range(4):
+        b, d = divmod(b, 4)
+        out.append(d)
+    return out
+
+
+def test_ternary_unpack_all_bytes_matches_base4_digits():
+    plane = np.arange(256, dtype=np.uint8).reshape(256, 1)
+    codes = formats.unpack_ternary(plane, 4)
+    for b in range(256):
+        assert list(codes[b]) == _digits_base4(b)
+
+
+def test_ternary_values_match_add_xor_expansion_all_bytes():
+    # "Kernel experiments", Test 1: spread the four codes to byte lanes, add
+    # 0x7F7F7F7F, XOR 0x80808080 -> signed -1/0/1/2 per byte.
+    plane = np.arange(256, dtype=np.uint8).reshape(256, 1)
+    vals = formats.ternary_value(formats.unpack_ternary(plane, 4))
+    for p in range(256):
+        spread = (p & 3) | ((p << 6) & 0x300) | ((p << 12) & 0x30000) | ((p << 18) & 0x3000000)
+        word = ((spread + 0x7F7F7F7F) & 0xFFFFFFFF) ^ 0x80808080
+        signed = [struct.unpack("b", bytes([(word >> (8 * t)) & 0xFF]))[0] for t in range(4)]
+        assert list(vals[p]) == signed
+
+
+def test_ternary_values_match_byte_select_table_all_bytes():
+    # "Kernel experiments", Test 16 CUDA decoder: byte_perm(0x020100ff) with the code as index.
+    table = (0x020100FF).to_bytes(4, "little")
+    plane = np.arange(256, dtype=np.uint8).reshape(256, 1)
+    vals = formats.ternary_value(formats.unpack_ternary(plane, 4))
+    for b in range(256):
+        sel = [(b >> (2 * t)) & 3 for t in range(4)]
+        expect = [struct.unpack("b", bytes([table[s]]))[0] for s in sel]
+        assert list(vals[b]) == expect
+
+
+def test_golden_code_values():
+    rows = _golden_rows("pq2_code_values.txt")
+    assert len(rows) == 4
+    for code, plus127, table_hex, value in rows:
+        code, plus127, value = int(code), int(plus127), int(value)
+        assert code + 127 == plus127
+        assert struct.unpack("b", bytes([plus127 ^ 0x80]))[0] == value
+        assert struct.unpack("b", bytes([int(table_hex, 16)]))[0] == value
+        assert int(formats.ternary_value(np.array([code], np.uint8))[0]) == value
+
+
+def test_ternary_pack_roundtrip_and_group_position():
+    rng = np.random.default_rng(7)
+    codes = rng.integers(0, 4, size=(5, 256), dtype=np.uint8)
+    plane = formats.pack_ternary(codes)
+    assert plane.shape == (5, 64)
+    np.testing.assert_array_equal(formats.unpack_ternary(plane, 256), codes)
+    # weight k = 128 g + 4 j + t sits in byte 32 g + j at bits 2t
+    for n in range(5):
+        for k in range(256):
+            g, r = divmod(k, 128)
+            j, t = divmod(r, 4)
+            assert (int(plane[n, 32 * g + j]) >> (2 * t)) & 3 == codes[n, k]
+
+
+def test_int4_unpack_all_bytes_matches_divmod():
+    plane = np.arange(256, dtype=np.uint8).reshape(256, 1)
+    codes = formats.unpack_int4(plane, 2)
+    for b in range(256):
+        hi, lo = divmod(b, 16)
+        assert list(codes[b]) == [lo, hi]
+    rng = np.random.default_rng(3)
+    c = rng.integers(0, 16, size=(3, 64), dtype=np.uint8)
+    np.testing.assert_array_equal(formats.unpack_int4(formats.pack_int4(c), 64), c)
+    z = rng.integers(0, 16, size=(3, 5), dtype=np.uint8)
+    np.testing.assert_array_equal(formats.unpack_zeros(formats.pack_zeros(z), 5), z)
+
+
+def test_pq2_block_split_against_struct_encoding():
+    rng = np.random.default_rng(11)
+    n, g = 3, 2
+    raw = bytearray()
+    want_scales, want_codes = [], []
+    for _ in range(n):
+        row_s, row_c = [], []
+        for _ in range(g):
+            s = float(np.float16(rng.uniform(0.005, 0.05)))
+            codes = [int(v) for v in rng.integers(0, 256, size=32)]
+            raw += struct.pack("<e", s) + bytes(codes)
+            row_s.append(s)
+            row_c += codes
+        want_scales.append(row_s)
+        want_codes.append(row_c)
+    arr = np.frombuffer(bytes(raw), np.uint8).reshape(n, g * 34)
+    plane, scales = formats.split_pq2_blocks(arr)
+    np.testing.assert_array_equal(plane, np.array(want_codes, np.uint8))
+    np.testing.assert_array_equal(scales.astype(np.float64), np.array(want_scales))
+    np.testing.assert_array_equal(formats.join_pq2_blocks(plane, scales), arr)
+
+
+# ------------------------------------------------------------------ partials
+def _brute_partials(q, plane, k):
+    m, n, g = q.shape[0], plane.shape[0], k // 128
+    out = np.zeros((m, n, g), dtype=np.int64)
+    for mi in range(m):
+        for ni in range(n):
+            for kk in range(k):
+                byte = int(plane[ni, kk // 4])
+                code = _digits_base4(byte)[kk % 4]
+                out[mi, ni, kk // 128] += int(q[mi, kk]) * (code - 1)
+    return out
+
+
+@pytest.mark.parametrize("m,k,n", [(1, 128, 3), (3, 256, 5), (2, 128, 1)])
+def test_ternary_partials_brute_force(m, k, n):
+    rng = np.random.default_rng(m * 100 + k + n)
+    q = rng.integers(-127, 128, size=(m, k), dtype=np.int8)
+    plane = rng.integers(0, 256, size=(n, k // 4), dtype=np.uint8)   # every code incl. 3
+    p = reference.ternary_partials(q, formats.unpack_ternary(plane, k))
+    np.testing.assert_array_equal(p, _brute_partials(q, plane, k))
+
+
+def test_masked_plane_identity():
+    # "Kernel experiments", Test 21: plane s of a byte is byte & (3 << 2s) = code * 4**s
+    # (plane 3 pre-shifted by 2); plane-ordered activations (position (i%4)*32 + i//4),
+    # shifted products, minus the group sum of q, equal the integer group dot.
+    rng = np.random.default_rng(5)
+    m, n, k = 4, 6, 512
+    q = rng.integers(-127, 128, size=(m, k), dtype=np.int8)
+    plane = rng.integers(0, 256, size=(n, k // 4), dtype=np.uint8)
+    p = reference.ternary_partials(q, formats.unpack_ternary(plane, k))
+    for g in range(k // 128):
+        qg = q[:, 128 * g:128 * (g + 1)].astype(np.int64)
+        qp = np.empty_like(qg)
+        i = np.arange(128)
+        qp[:, (i % 4) * 32 + i // 4] = qg
+        packed = plane[:, 32 * g:32 * (g + 1)].astype(np.int64)
+        q0, q1, q2, q3 = (qp[:, 32 * s:32 * (s + 1)] for s in range(4))
+        part = (packed & 0x03) @ q0.T
+        part += ((packed & 0x0C) @ q1.T) >> 2
+        part += ((packed & 0x30) @ q2.T) >> 4
+        part += (((packed >> 2) & 0x30) @ q3.T) >> 4
+        part -= qg.sum(axis=1)[None, :]
+        np.testing.assert_array_equal(part.T, p[:, :, g])
+
+
+# ------------------------------------------------------------------ float products
+def _fraction_product(x, codes, scales, values_fn):
+    m, k = x.shape
+    n = codes.shape[0]
+    y = [[Fraction(0)] * n for _ in range(m)]
+    for mi in range(m):
+        for ni in range(n):
+            acc = Fraction(0)
+            for kk in range(k):
+                w = Fraction(int(values_fn(codes[ni, kk]))) * Fraction(float(scales[ni, kk // 128]))
+                acc += Fraction(float(x[mi, kk])) * w
+            y[mi][ni] = acc
+    return y
+
+
+def test_ternary_float_product_exact_on_power_of_two_scales():
+    rng = np.random.default_rng(2)
+    m, k, n = 2, 256, 3
+    codes = rng.integers(0, 4, size=(n, k), dtype=np.uint8)
+    scales = np.ldexp(1.0, rng.integers(-8, -2, size=(n, k // 128))).astype(np.float16)
+    x = rng.integers(-40, 41, size=(m, k)).astype(np.float32)
+    y = reference.product(x, reference.weights_ternary(codes, scales))
+    want = _fraction_product(x, codes, scales, lambda c: int(c) - 1)
+    for mi in range(m):
+        for ni in range(n):
+            assert Fraction(float(y[mi, ni])) == want[mi][ni]
+
+
+def test_ternary_float_product_random_within_1e12():
+    rng = np.random.default_rng(9)
+    m, k, n = 2, 256, 3
+    codes = rng.integers(0, 3, size=(n, k), dtype=np.uint8)
+    scales = rng.uniform(0.005, 0.05, size=(n, k // 128)).astype(np.float16)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    y = reference.product(x, reference.weights_ternary(codes, scales))
+    want = _fraction_product(x, codes, scales, lambda c: int(c) - 1)
+    for mi in range(m):
+        for ni in range(n):
+            assert abs(Fraction(float(y[mi, ni])) - want[mi][ni]) <= Fraction(1, 10**12) * abs(want[mi][ni])
+
+
+def test_int8_product_single_group_closed_form():
+    # K = 128: y = xs * ws * P with P the one integer group dot.
+    rng = np.random.default_rng(4)
+    q = rng.integers(-127, 128, size=(2, 128), dtype=np.int8)
+    codes = rng.integers(0, 3, size=(3, 128), dtype=np.uint8)
+    ws = rng.uniform(0.01, 0.05, size=(3, 1)).astype(np.float16)
+    xs = np.array([0.25, 0.0078125], np.float32)
+    p, y = reference.ternary_int8_product(q, xs, codes, ws)
+    for mi in range(2):
+        for ni in range(3):
+            dot = sum(int(q[mi, kk]) * (int(codes[ni, kk]) - 1) for kk in range(128))
+            assert p[mi, ni, 0] == dot
+            assert Fraction(float(y[mi, ni])) == Fraction(float(xs[mi])) * Fraction(float(ws[ni, 0])) * dot
+
+
+def test_int8_product_unit_scales_is_sum_of_partials():
+    rng = np.random.default_rng(6)
+    q = rng.integers(-127, 128, size=(3, 512), dtype=np.int8)
+    codes = rng.integers(0, 3, size=(4, 512), dtype=np.uint8)
+    p, y = reference.ternary_int8_product(q, np.ones(3, np.float32), codes, np.ones((4, 4), np.float16))
+    np.testing.assert_array_equal(y, p.sum(axis=2).astype(np.float64))
+    # and equals the dense integer product with values code - 1
+    dense = q.astype(np.int64) @ (codes.astype(np.int64) - 1).T
+    np.testing.assert_array_equal(p.sum(axis=2), dense)
+
+
+def test_int8_product_group_scale_variant_reduces_to_row_scales():
+    rng = np.random.default_rng(8)
+    q = rng.integers(-127, 128, size=(2, 384), dtype=np.int8)
+    codes = rng.integers(0, 3, size=(3, 384), dtype=np.uint8)
+    ws = rng.uniform(0.01, 0.05, size=(3, 3)).astype(np.float16)
+    xs = np.array([0.5, 0.125], np.float32)
+    _, y1 = reference.ternary_int8_product(q, xs, codes, ws)
+    _, y2 = reference.ternary_int8_product_group_scales(q, np.repeat(xs[:, None], 3, 1), codes, ws)
+    np.testing.assert_array_equal(y1, y2)
+
+
+# ------------------------------------------------------------------ act order / zero points
+def _valid_gidx(rng, k):
+    pi = rng.permutation(k)
+    g = np.empty(k, np.int32)
+    g[pi] = np.arange(k) // 128
+    return g
+
+
+def test_act_order_invariant_exact_on_integer_data():
+    rng = np.random.default_rng(12)
+    m, k, n = 3, 512, 4
+    codes = rng.integers(0, 16, size=(n, k), dtype=np.uint8)
+    zeros = rng.integers(0, 16, size=(n, 4), dtype=np.uint8)
+    scales = np.ldexp(1.0, rng.integers(-9, -5, size=(n, 4))).astype(np.float16)
+    g_idx = _valid_gidx(rng, k)
+    x = rng.integers(-8, 9, size=(m, k)).astype(np.float16)
+    w = reference.weights_int4(codes, scales, zeros, g_idx)
+    perm = reference.act_order_perm(g_idx, k)
+    assert np.array_equal(g_idx[perm], np.arange(k) // 128)
+    # sorted-order weights use group j // 128 for column j
+    w_sorted = reference.weights_int4(codes[:, perm], scales, zeros, None)
+    np.testing.assert_array_equal(w_sorted, w[:, perm])
+    y = reference.product(x, w)
+    y_perm = reference.product(x[:, perm], w_sorted)
+    np.testing.assert_array_equal(y, y_perm)
+    # brute force on one element
+    acc = Fraction(0)
+    for kk in range(k):
+        gi = int(g_idx[kk])
+        acc += Fraction(float(x[1, kk])) * (int(codes[2, kk]) - int(zeros[2, gi])) * Fraction(float(scales[2, gi]))
+    assert Fraction(float(y[1, 2])) == acc
+
+
+def test_act_order_negative_controls():
+    # mate PR: a skipped gather and a k // group scale index both change the answer.
+    wl = synth.int4_zp_actorder("t", 21, 2, 512, 8)
+    x = wl.x.astype(np.float64)
+    w = reference.weights_int4(wl.codes, wl.scales, wl.zeros, wl.g_idx)
+    perm = reference.act_order_perm(wl.g_idx, wl.k)
+    w_sorted = reference.weights_int4(wl.codes[:, perm], wl.scales, wl.zeros, None)
+    y = reference.product(x, w)
+    np.testing.assert_allclose(reference.product(x[:, perm], w_sorted), y, rtol=1e-12, atol=1e-12)
+    skipped = reference.product(x, w_sorted)
+    canonical = reference.product(x, reference.weights_int4(wl.codes, wl.scales, wl.zeros, None))
+    scale = np.abs(y).max()
+    assert np.abs(skipped - y).max() > 0.1 * scale
+    assert np.abs(canonical - y).max() > 0.1 * scale
+
+
+def test_act_order_refuses_malformed_gidx():
+    k = 256
+    g = np.repeat(np.arange(2, dtype=np.int32), 128)
+    reference.act_order_perm(g, k)
+    bad = g.copy()
+    bad[0] = 1          # group 0: 127 members, group 1: 129
+    with pytest.raises(ValueError, match="group 0 has 127 members"):
+        reference.act_order_perm(bad, k)
+    bad = g.copy()
+    bad[5] = 2
+    with pytest.raises(ValueError, match="outside"):
+        reference.act_order_perm(bad, k)
+
+
+def test_zero_point_convention_swap_is_detected():
+    # mate PR: two packed zero-point conventions share shape and value multiset;
+    # reading one as the other must give a visibly wrong product.
+    rng = np.random.default_rng(13)
+    n, k = 6, 512
+    codes = rng.integers(0, 16, size=(n, k), dtype=np.uint8)
+    zeros = rng.integers(0, 16, size=(n, 4), dtype=np.uint8)
+    scales = rng.uniform(0.001, 0.02, size=(n, 4)).astype(np.float16)
+    x = rng.standard_normal((2, k))
+    zp = formats.pack_zeros(zeros)
+    swapped = formats.unpack_int4((zp >> 4) | ((zp & 0x0F) << 4), 4)   # high nibble first
+    assert sorted(swapped.ravel()) != [] and not np.array_equal(swapped, zeros)
+    y = reference.product(x, reference.weights_int4(codes, scales, formats.unpack_zeros(zp, 4)))
+    y_bad = reference.product(x, reference.weights_int4(codes, scales, swapped))
+    assert np.linalg.norm(y_bad - y) / np.linalg.norm(y) > 0.05
+
+
+def test_symmetric_int4_is_zero_point_eight():
+    rng = np.random.default_rng(14)
+    codes = rng.integers(0, 16, size=(3, 256), dtype=np.uint8)
+    scales = rng.uniform(0.001, 0.02, size=(3, 2)).astype(np.float16)
+    np.testing.assert_array_equal(reference.weights_int4(codes, scales),
+                                  reference.weights_int4(codes, scales, np.full((3, 2), 8, np.uint8)))
+
+
+# ------------------------------------------------------------------ rounding
+def test_round_to_matches_library_conversions():
+    rng = np.random.default_rng(15)
+    v = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-6, 4, 20000),
+                        np.array([0.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 2.0 ** -20, 3 * 2.0 ** -25])])
+    np.testing.assert_array_equal(reference.round_to(v, "f16"), v.astype(np.float16).astype(np.float64))
+    v32 = v.astype(np.float32)   # torch's bf16 conversion rounds from fp32: compare on fp32 inputs
+    got = reference.round_to(v32.astype(np.float64), "bf16")
+    want = torch.from_numpy(v32).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(got, want)
+    # ties to even
+    assert reference.round_to(np.array([1 + 2 ** -8]), "bf16")[0] == 1.0
+    assert reference.round_to(np.array([1 + 3 * 2 ** -8]), "bf16")[0] == 1 + 2 ** -6
+
+
+def test_rounded_int4_weights_are_nearest_representable():
+    rng = np.random.default_rng(16)
+    codes = rng.integers(0, 16, size=(4, 256), dtype=np.uint8)
+    scales = synth.f32_to_bf16_bits(rng.uniform(0.001, 0.02, size=(4, 2)).astype(np.float32))
+    s = synth.bf16_bits_to_f32(scales).astype(np.float64)
+    w = reference.weights_int4_rounded(codes, s, None, None, "bf16")
+    exact = reference.weights_int4(codes, s)
+    got = torch.from_numpy(exact.astype(np.float32)).to(torch.bfloat16).double().numpy()  # exact fits fp32
+    np.testing.assert_array_equal(w, got)
+
+
+# ------------------------------------------------------------------ quantiser
+def test_quantizer_scale_rule_and_bounds():
+    rng = np.random.default_rng(17)
+    x = (rng.standard_normal((64, 512)) * rng.uniform(0.01, 100, size=(64, 1))).astype(np.float32)
+    x[3] = 0.0
+    q, s = quant.quantize_rows(x)
+    assert q.dtype == np.int8 and s.dtype == np.float32
+    # scale = fl32(amax * fl32(1/127)): product of two fp32 values is exact in fp64
+    amax = np.abs(x).max(axis=1).astype(np.float64)
+    want_s = (amax * float(np.float32(1) / np.float32(127))).astype(np.float32)
+    np.testing.assert_array_equal(s, want_s)
+    assert np.abs(q.astype(np.int32)).max() <= 127
+    nz = s > 0
+    assert np.all(np.abs(q[nz].astype(np.int32)).max(axis=1) == 127)
+    assert np.all(q[3] == 0) and s[3] == 0
+    # |x/s - q| <= 1/2 exactly for unclamped entries, ties to even (rational check on a sample)
+    for r in range(0, 64, 7):
+        for c in range(0, 512, 37):
+            if s[r] == 0:
+                continue
+            ratio = Fraction(float(x[r, c])) / Fraction(float(s[r]))
+            rq = Fraction(float(np.float32(x[r, c] / s[r])))   # the fp32 quotient the rule rounds
+            assert abs(rq - ratio) <= abs(ratio) * Fraction(1, 2 ** 24)
+            qi = int(q[r, c])
+            if abs(qi) < 127:
+                assert abs(rq - qi) <= Fraction(1, 2)
+                if abs(rq - qi) == Fraction(1, 2):
+                    assert qi % 2 == 0
+
+
+def test_quantizer_ties_to_even_when_scale_is_one():
+    # amax = 127 gives scale fl32(127 * fl32(1/127)) = 1.0 exactly, so q = rint(x).
+    x = np.array([[127.0, 2.5, 3.5, -2.5, -0.5, 126.5, 0.5, 1.5]], np.float32)
+    q, s = quant.quantize_rows(x)
+    assert s[0] == 1.0
+    assert list(q[0]) == [127, 2, 4, -2, 0, 126, 0, 2]
+
+
+def test_group_quantizer_matches_rows_on_each_group():
+    rng = np.random.default_rng(18)
+    x = rng.standard_normal((3, 384)).astype(np.float32)
+    q, s = quant.quantize_groups(x)
+    for g in range(3):
+        qg, sg = quant.quantize_rows(x[:, 128 * g:128 * (g + 1)])
+        np.testing.assert_array_equal(q[:, 128 * g:128 * (g + 1)], qg)
+        np.testing.assert_array_equal(s[:, g], sg)
+
+
+def test_quantizer_reconstruction_error_bound():
+    rng = np.random.default_rng(19)
+    x = rng.standard_normal((8, 1024)).astype(np.float32)
+    q, s = quant.quantize_rows(x)
+    err = np.abs(quant.dequantize_rows(q, s) - x.astype(np.float64))
+    assert np.all(err <= s[:, None].astype(np.float64) * (0.5 + 1e-6))
+
+
+# ------------------------------------------------------------------ generators
+def test_workload_generators_shapes_and_ranges():
+    w = synth.ternary_tiny()
+    assert (w.m, w.k, w.n) == (1, 512, 256) and w.codes.max() <= 2
+    assert w.scales.dtype == np.float16 and 0.01 <= w.scales.min() and w.scales.max() <= 0.05
+    w3 = synth.int4_zp_actorder("t", 2, 2, 512, 16)
+    perm = reference.act_order_perm(w3.g_idx, 512)
+    assert perm.shape == (512,)
+    w4 = synth.int4_sym("t", 3, 4, 256, 8)
+    assert w4.x.dtype == np.uint16 and w4.scales.dtype == np.uint16
