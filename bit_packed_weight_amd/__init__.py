@@ -1,0 +1,326 @@
+"""Python binding of libbpw.so, the bit-packed weight library for MI355X (gfx950).
+
+The names mirror the C ABI in ``include/bpw.h``; this module only marshals
+arguments (torch tensors -> device pointers, the current HIP stream, output and
+workspace allocation through PyTorch). Every step of the computation runs in
+the HIP kernels of the library. There is no CPU fallback: if the library is not
+built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbpw.so")
+
+# status codes
+OK, EINVAL, ESHAPE, EALIGN, EGIDX, EUNSUPPORTED, EHIP = range(7)
+# weight formats
+TERNARY2, INT4_SYM, INT4_ZP = 1, 2, 3
+# element types
+F32, F16, BF16, I8, I32 = 0, 1, 2, 3, 4
+# prepare sources
+SRC_PQ2_BLOCKS, SRC_PLANES, SRC_CODES_U8 = 1, 2, 3
+# partial-sum cores / workspace entries
+PATH_GEMV, PATH_GEMM = 0, 1
+# probes
+PROBE_READ, PROBE_COPY = 0, 1
+
+FORMAT_NAMES = {"ternary": TERNARY2, "int4_sym": INT4_SYM, "int4_zp": INT4_ZP}
+_STATUS_NAMES = {EINVAL: "EINVAL", ESHAPE: "ESHAPE", EALIGN: "EALIGN", EGIDX: "EGIDX",
+                 EUNSUPPORTED: "EUNSUPPORTED", EHIP: "EHIP"}
+
+
+class BpwError(RuntimeError):
+    """A nonzero status from the library; ``status`` holds the code."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class BpwWeights(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("scale_dtype", ctypes.c_int32),
+                ("group", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("zeros", ctypes.c_void_p), ("perm", ctypes.c_void_p)]
+
+
+class BpwSizes(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_size_t), ("scales", ctypes.c_size_t),
+                ("zeros", ctypes.c_size_t), ("perm", ctypes.c_size_t)]
+
+
+EXPORTS = {
+    "bpw_version": (ctypes.c_int, []),
+    "bpw_last_error": (ctypes.c_char_p, []),
+    "bpw_packed_sizes": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                        ctypes.c_int, ctypes.c_int, ctypes.POINTER(BpwSizes)]),
+    "bpw_prepare_packed": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                                          ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "bpw_quantize_rows": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "bpw_workspace_size": (ctypes.c_int, [ctypes.POINTER(BpwWeights), ctypes.c_int64, ctypes.c_int,
+                                          ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]),
+    "bpw_gemv_packed": (ctypes.c_int, [ctypes.POINTER(BpwWeights), ctypes.c_void_p, ctypes.c_int,
+                                       ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "bpw_gemm_packed": (ctypes.c_int, [ctypes.POINTER(BpwWeights), ctypes.c_void_p, ctypes.c_int,
+                                       ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "bpw_partials": (ctypes.c_int, [ctypes.POINTER(BpwWeights), ctypes.c_void_p, ctypes.c_int64,
+                                    ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                    ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                    ctypes.c_void_p]),
+    "bpw_probe": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                 ctypes.c_void_p]),
+    "bpw_probe_blocks": (ctypes.c_int64, [ctypes.c_size_t]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libbpw.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m bit_packed_weight_amd._build` "
+                               "(or __graft_entry__.build()); there is no fallback path")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in EXPORTS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def last_error() -> str:
+    return lib().bpw_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != OK:
+        raise BpwError(status, last_error())
+
+
+def version() -> int:
+    return lib().bpw_version()
+
+
+# ---------------------------------------------------------------- torch glue
+def _torch():
+    import torch  # noqa: PLC0415 (torch is only needed for device calls)
+    return torch
+
+
+def dtype_code(t) -> int:
+    torch = _torch()
+    table = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16, torch.int8: I8,
+             torch.int32: I32}
+    if t not in table:
+        raise ValueError(f"unsupported dtype {t}")
+    return table[t]
+
+
+def torch_dtype(code: int):
+    torch = _torch()
+    return {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16, I8: torch.int8,
+            I32: torch.int32}[code]
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device=None) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+@dataclasses.dataclass
+class PackedWeights:
+    """Prepared planes on the device plus their metadata (see ``bpw_weights``)."""
+
+    fmt: int
+    scale_dtype: int
+    n: int
+    k: int
+    codes: object
+    scales: object
+    zeros: object = None
+    perm: object = None
+
+    def struct(self) -> BpwWeights:
+        return BpwWeights(self.fmt, self.scale_dtype, 128, 0, self.n, self.k, _ptr(self.codes),
+                          _ptr(self.scales), _ptr(self.zeros), _ptr(self.perm))
+
+    @property
+    def logical_bytes(self) -> int:
+        """Weight bytes one product reads: codes + scales (+ zero points)."""
+        total = self.codes.numel() + self.scales.numel() * self.scales.element_size()
+        if self.zeros is not None:
+            total += self.zeros.numel()
+        return total
+
+
+def packed_sizes(fmt: int, n: int, k: int, scale_dtype: int = F16, has_perm: bool = False) -> BpwSizes:
+    out = BpwSizes()
+    _check(lib().bpw_packed_sizes(fmt, scale_dtype, n, k, 128, int(has_perm), ctypes.byref(out)))
+    return out
+
+
+def _np_ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def prepare_packed_host(fmt: int, codes: np.ndarray, scales: Optional[np.ndarray] = None,
+                        zeros: Optional[np.ndarray] = None, g_idx: Optional[np.ndarray] = None,
+                        src_format: int = SRC_CODES_U8, scale_dtype: int = F16,
+                        n: Optional[int] = None, k: Optional[int] = None) -> dict:
+    """Run ``bpw_prepare_packed`` into host numpy planes (no GPU involved)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    if n is None or k is None:
+        n = codes.shape[0]
+        if src_format == SRC_CODES_U8:
+            k = codes.shape[1]
+        elif src_format == SRC_PQ2_BLOCKS:
+            k = codes.shape[1] // 34 * 128
+        else:
+            k = codes.shape[1] * (4 if fmt == TERNARY2 else 2)
+    sizes = packed_sizes(fmt, n, k, scale_dtype, g_idx is not None)
+    g = k // 128
+    out_codes = np.empty(sizes.codes, np.uint8)
+    out_scales = np.empty(sizes.scales, np.uint8)
+    out_zeros = np.empty(sizes.zeros, np.uint8) if sizes.zeros else None
+    out_perm = np.empty(k, np.int32) if g_idx is not None else None
+    if scales is not None:
+        scales = np.ascontiguousarray(scales)
+        if scales.dtype.itemsize != 2:
+            raise ValueError("scales must be 16-bit (fp16 values or bf16 bit patterns)")
+    if zeros is not None:
+        zeros = np.ascontiguousarray(zeros, dtype=np.uint8)
+    if g_idx is not None:
+        g_idx = np.ascontiguousarray(g_idx, dtype=np.int32)
+    _check(lib().bpw_prepare_packed(fmt, src_format, scale_dtype, n, k, 128, _np_ptr(codes),
+                                    _np_ptr(scales), _np_ptr(zeros), _np_ptr(g_idx),
+                                    _np_ptr(out_codes), _np_ptr(out_scales), _np_ptr(out_zeros),
+                                    _np_ptr(out_perm)))
+    cb = k // 4 if fmt == TERNARY2 else k // 2
+    return {"fmt": fmt, "scale_dtype": scale_dtype, "n": n, "k": k,
+            "codes": out_codes.reshape(n, cb), "scales": out_scales.view(np.uint16).reshape(n, g),
+            "zeros": None if out_zeros is None else out_zeros.reshape(n, (g + 1) // 2),
+            "perm": out_perm}
+
+
+def upload(planes: dict, device="cuda") -> PackedWeights:
+    """Copy host planes (from ``prepare_packed_host``) into device tensors."""
+    torch = _torch()
+    sd = torch.float16 if planes["scale_dtype"] == F16 else torch.bfloat16
+
+    def dev(a, dt=None):
+        if a is None:
+            return None
+        t = torch.from_numpy(np.ascontiguousarray(a)).to(device)
+        return t.view(dt) if dt is not None else t
+
+    return PackedWeights(planes["fmt"], planes["scale_dtype"], planes["n"], planes["k"],
+                         dev(planes["codes"]), dev(planes["scales"].view(np.int16), sd),
+                         dev(planes["zeros"]), dev(planes["perm"]))
+
+
+def prepare_packed(fmt: int, codes: np.ndarray, scales=None, zeros=None, g_idx=None,
+                   src_format: int = SRC_CODES_U8, scale_dtype: int = F16, device="cuda") -> PackedWeights:
+    """``bpw_prepare_packed`` on the host, then upload the planes to ``device``."""
+    return upload(prepare_packed_host(fmt, codes, scales, zeros, g_idx, src_format, scale_dtype), device)
+
+
+def quantize_rows(x, q=None, x_scale=None):
+    """int8 row quantiser on the GPU: returns (q [M,K] int8, x_scale [M] fp32)."""
+    torch = _torch()
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [M, K] tensor")
+    m, k = x.shape
+    q = torch.empty((m, k), dtype=torch.int8, device=x.device) if q is None else q
+    x_scale = torch.empty(m, dtype=torch.float32, device=x.device) if x_scale is None else x_scale
+    _check(lib().bpw_quantize_rows(_ptr(x), dtype_code(x.dtype), m, k, _ptr(q), _ptr(x_scale),
+                                   _stream(x.device)))
+    return q, x_scale
+
+
+def workspace_size(w: PackedWeights, m: int, x_dtype: int, entry: int) -> int:
+    out = ctypes.c_size_t()
+    st = w.struct()
+    _check(lib().bpw_workspace_size(ctypes.byref(st), m, x_dtype, entry, ctypes.byref(out)))
+    return out.value
+
+
+def _workspace(w, m, x_dtype, entry, device, workspace):
+    torch = _torch()
+    need = workspace_size(w, m, x_dtype, entry)
+    if need == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return workspace, workspace.numel()
+
+
+def _product(entry: int, w: PackedWeights, x, x_scale=None, out_dtype=None, out=None, workspace=None):
+    torch = _torch()
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [M, K] tensor")
+    m = x.shape[0]
+    xd = dtype_code(x.dtype)
+    if out is None:
+        out_dtype = out_dtype if out_dtype is not None else (torch.float16 if xd == I8 else x.dtype)
+        out = torch.empty((m, w.n), dtype=out_dtype, device=x.device)
+    ws, ws_bytes = _workspace(w, m, xd, entry, x.device, workspace)
+    st = w.struct()
+    fn = lib().bpw_gemv_packed if entry == PATH_GEMV else lib().bpw_gemm_packed
+    _check(fn(ctypes.byref(st), _ptr(x), xd, _ptr(x_scale), m, _ptr(out), dtype_code(out.dtype),
+              _ptr(ws), ws_bytes, _stream(x.device)))
+    return out
+
+
+def gemv_packed(w: PackedWeights, x, x_scale=None, out_dtype=None, out=None, workspace=None):
+    """y = x @ W^T, decode-shaped (bpw_gemv_packed)."""
+    return _product(PATH_GEMV, w, x, x_scale, out_dtype, out, workspace)
+
+
+def gemm_packed(w: PackedWeights, x, x_scale=None, out_dtype=None, out=None, workspace=None):
+    """y = x @ W^T, prefill-shaped (bpw_gemm_packed)."""
+    return _product(PATH_GEMM, w, x, x_scale, out_dtype, out, workspace)
+
+
+def partials(w: PackedWeights, q, path: int, m0: int, m1: int, n0: int, n1: int, workspace=None):
+    """Exact int32 group partials of a window (bpw_partials)."""
+    torch = _torch()
+    m = q.shape[0]
+    g = w.k // 128
+    out = torch.empty((m1 - m0, n1 - n0, g), dtype=torch.int32, device=q.device)
+    ws, ws_bytes = (None, 0)
+    if path == PATH_GEMM:
+        ws, ws_bytes = _workspace(w, m, I8, PATH_GEMM, q.device, workspace)
+    st = w.struct()
+    _check(lib().bpw_partials(ctypes.byref(st), _ptr(q), m, path, m0, m1, n0, n1, _ptr(out),
+                              _ptr(ws), ws_bytes, _stream(q.device)))
+    return out
+
+
+def probe(kind: int, src, dst) -> None:
+    """HBM probe (bpw_probe): streaming read or copy of ``src.nbytes`` bytes."""
+    nbytes = src.numel() * src.element_size()
+    _check(lib().bpw_probe(kind, _ptr(src), _ptr(dst), nbytes, _stream(src.device)))
+
+
+def probe_blocks(nbytes: int) -> int:
+    return lib().bpw_probe_blocks(nbytes)

@@ -1,0 +1,50 @@
+// Host-side launchers implemented next to their kernels. Arguments are already
+// validated by the C-ABI layer (api.cpp); launchers only pick a configuration
+// and launch on the given stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/bpw.h"
+
+namespace bpw {
+
+// Activation operand preparation (quant.hip).
+hipError_t launch_quantize_rows(const void* x, int x_dtype, int64_t m, int64_t k, int8_t* q,
+                                float* x_scale, hipStream_t s);
+// q [M][K] natural order -> plane order inside each 128-group (element 4u+t of a
+// 64-element half-group goes to position 32t + 16*half + u).
+hipError_t launch_int8_planes(const int8_t* q, int64_t m, int64_t k, int8_t* q_planes,
+                              hipStream_t s);
+// x_perm[m][j] = x[m][perm[j]] for 16-bit elements.
+hipError_t launch_gather_cols(const uint16_t* x, const int32_t* perm, int64_t m, int64_t k,
+                              uint16_t* x_perm, hipStream_t s);
+
+// Decode GEMVs (gemv.hip). Return hipErrorInvalidValue when the staged
+// activations do not fit the kernel's LDS budget (caller then routes to GEMM).
+bool gemv_t2_fits(int64_t m, int64_t k);
+hipError_t launch_gemv_t2(const bpw_weights& w, const int8_t* q, const float* x_scale, int64_t m,
+                          void* y, int y_dtype, hipStream_t s);
+hipError_t launch_gemv_t2_partials(const bpw_weights& w, const int8_t* q, int64_t m, int64_t m0,
+                                   int64_t m1, int64_t n0, int64_t n1, int32_t* out,
+                                   hipStream_t s);
+bool gemv_w4_fits(int64_t m, int64_t k);
+hipError_t launch_gemv_w4(const bpw_weights& w, const void* x_sorted, int x_dtype, int64_t m,
+                          void* y, int y_dtype, hipStream_t s);
+
+// Prefill GEMMs (gemm_i8.hip, gemm_w4.hip). x operands already in the order
+// the kernels read (int8: plane order; 16-bit: act-order gathered).
+hipError_t launch_gemm_t2(const bpw_weights& w, const int8_t* q_planes, const float* x_scale,
+                          int64_t m, void* y, int y_dtype, hipStream_t s);
+hipError_t launch_gemm_t2_partials(const bpw_weights& w, const int8_t* q_planes, int64_t m,
+                                   int64_t m0, int64_t m1, int64_t n0, int64_t n1, int32_t* out,
+                                   hipStream_t s);
+hipError_t launch_gemm_w4(const bpw_weights& w, const void* x_sorted, int x_dtype, int64_t m,
+                          void* y, int y_dtype, hipStream_t s);
+
+// Probes (probe.hip).
+int64_t probe_blocks(size_t bytes);
+hipError_t launch_probe(int kind, const void* src, void* dst, size_t bytes, hipStream_t s);
+
+}  // namespace bpw

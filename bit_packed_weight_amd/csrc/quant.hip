@@ -1,0 +1,119 @@
+// Activation operand kernels: int8 row quantiser, int8 plane reorder, act-order
+// column gather.
+//
+// Quantiser rule: "Kernel experiments: recorded evidence", Test 6 (group-128
+// quantiser: absmax / 127, IEEE division, round half to even, clamp to
+// +-127) and Test 8 (the division by 127 is a multiply by the fp32 reciprocal).
+// Plane order of int8 activations: same page, Test 21 (masked-plane MMA: each
+// code plane of a packed byte multiplies a contiguous slice of activations).
+#include "device.h"
+#include "launch.h"
+
+namespace bpw {
+namespace {
+
+__device__ __forceinline__ float ld(const float* p) { return *p; }
+__device__ __forceinline__ float ld(const __half* p) { return __half2float(*p); }
+__device__ __forceinline__ float ld(const uint16_t* p) { return bf16_to_f32(*p); }
+
+constexpr int kQThreads = 256;
+
+template <typename T>
+__global__ __launch_bounds__(kQThreads) void quantize_rows_kernel(const T* __restrict__ x,
+                                                                  int64_t k,
+                                                                  int8_t* __restrict__ q,
+                                                                  float* __restrict__ x_scale) {
+  __shared__ float wmax[kQThreads / 64];
+  const int64_t row = blockIdx.x;
+  const T* xr = x + row * k;
+  int8_t* qr = q + row * k;
+  float amax = 0.0f;
+  for (int64_t i = threadIdx.x; i < k; i += kQThreads) amax = fmaxf(amax, fabsf(ld(xr + i)));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = wmax[0];
+#pragma unroll
+  for (int w = 1; w < kQThreads / 64; ++w) amax = fmaxf(amax, wmax[w]);
+  const float scale = amax * (1.0f / 127.0f);      // fp32 reciprocal constant, one rounding
+  const float div = scale > 0.0f ? scale : 1.0f;
+  for (int64_t i = threadIdx.x; i < k; i += kQThreads) {
+    float r = rintf(ld(xr + i) / div);               // IEEE division, ties to even
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    qr[i] = static_cast<int8_t>(r);
+  }
+  if (threadIdx.x == 0) x_scale[row] = scale;
+}
+
+// One thread per (row, group, half): 64 natural bytes -> four 16-byte plane chunks.
+__global__ __launch_bounds__(256) void int8_planes_kernel(const int8_t* __restrict__ q,
+                                                          int64_t m, int64_t k,
+                                                          int8_t* __restrict__ out) {
+  const int64_t units = m * (k / 64);
+  for (int64_t u = blockIdx.x * 256ll + threadIdx.x; u < units; u += gridDim.x * 256ll) {
+    const int64_t base = u * 64;                     // rows are contiguous: unit u covers [64u, 64u+64)
+    const int hh = static_cast<int>(u & 1);
+    const uint4* src = reinterpret_cast<const uint4*>(q + base);
+    uint4 in[4] = {src[0], src[1], src[2], src[3]};
+    uint4 o[4];
+    to_plane_order(in, o);
+    int8_t* gbase = out + (base - hh * 64);          // start of the 128-group
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      *reinterpret_cast<uint4*>(gbase + 32 * t + 16 * hh) = o[t];
+  }
+}
+
+__global__ __launch_bounds__(256) void gather_cols_kernel(const uint16_t* __restrict__ x,
+                                                          const int32_t* __restrict__ perm,
+                                                          int64_t m, int64_t k,
+                                                          uint16_t* __restrict__ out) {
+  const int64_t total = m * k;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < total; i += gridDim.x * 256ll) {
+    const int64_t row = i / k;
+    const int64_t j = i - row * k;
+    out[i] = x[row * k + perm[j]];
+  }
+}
+
+int grid_for(int64_t items, int per_block) {
+  int64_t b = (items + per_block - 1) / per_block;
+  if (b > 65536) b = 65536;
+  if (b < 1) b = 1;
+  return static_cast<int>(b);
+}
+
+}  // namespace
+
+hipError_t launch_quantize_rows(const void* x, int x_dtype, int64_t m, int64_t k, int8_t* q,
+                                float* x_scale, hipStream_t s) {
+  dim3 grid(static_cast<unsigned>(m)), block(kQThreads);
+  switch (x_dtype) {
+    case BPW_F32:
+      quantize_rows_kernel<float><<<grid, block, 0, s>>>(static_cast<const float*>(x), k, q, x_scale);
+      break;
+    case BPW_F16:
+      quantize_rows_kernel<__half><<<grid, block, 0, s>>>(static_cast<const __half*>(x), k, q, x_scale);
+      break;
+    default:
+      quantize_rows_kernel<uint16_t><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(x), k, q, x_scale);
+      break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_int8_planes(const int8_t* q, int64_t m, int64_t k, int8_t* q_planes,
+                              hipStream_t s) {
+  const int64_t units = m * (k / 64);
+  int8_planes_kernel<<<grid_for(units, 256), 256, 0, s>>>(q, m, k, q_planes);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_cols(const uint16_t* x, const int32_t* perm, int64_t m, int64_t k,
+                              uint16_t* x_perm, hipStream_t s) {
+  gather_cols_kernel<<<grid_for(m * k, 256), 256, 0, s>>>(x, perm, m, k, x_perm);
+  return hipGetLastError();
+}
+
+}  // namespace bpw

@@ -1,0 +1,214 @@
+/*
+ * bpw.h -- C ABI of the bit-packed weight library (AMD Instinct MI355X, gfx950).
+ *
+ * Computes y = x @ W^T for a weight matrix W [N, K] stored group-quantised:
+ * 2-bit ternary codes or 4-bit codes, one fp16/bf16 scale (and optionally one
+ * 4-bit zero point) per group of 128 along K, with an optional act-order
+ * permutation of K. Activations are fp16/bf16, or int8 with one fp32 scale per
+ * row. Sources: "Kernel experiments: recorded evidence" (ternary PQ2 format,
+ * section A and Tests 1, 2, 6-8, 21) and "mate: Marlin-class W4A16 GEMM for
+ * mp_31 (SQMMA int4 x fp16) - #6" (4-bit codes, zero points, act order).
+ *
+ * Conventions for every entry point:
+ *  - "host" pointers are ordinary CPU memory; "device" pointers are GPU memory
+ *    owned by the caller (e.g. allocated through PyTorch). The library never
+ *    allocates or frees device memory and never synchronises a stream, except
+ *    where an entry point says otherwise.
+ *  - Work is launched only on the HIP stream passed in (NULL = default stream).
+ *  - Matrices are dense row-major. Device planes must be 16-byte aligned.
+ *  - Every argument is validated before anything is launched. On failure the
+ *    call returns a nonzero status, touches no output, and bpw_last_error()
+ *    (thread-local) names the violated invariant. A launch failure returns
+ *    BPW_EHIP; faults inside a kernel surface at the caller's next sync.
+ *  - Results are bit-identical from run to run (no atomics, fixed-order sums).
+ */
+#ifndef BPW_H_
+#define BPW_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------- */
+#define BPW_OK 0
+#define BPW_EINVAL 1        /* NULL pointer, unknown enum value, negative size   */
+#define BPW_ESHAPE 2        /* inconsistent sizes (K % 128, window, buffer size) */
+#define BPW_EALIGN 3        /* pointer not aligned as required                   */
+#define BPW_EGIDX 4         /* act-order g_idx malformed                          */
+#define BPW_EUNSUPPORTED 5  /* valid request this library does not implement     */
+#define BPW_EHIP 6          /* HIP runtime reported an error                      */
+
+/* ---- weight formats -------------------------------------------------- */
+#define BPW_TERNARY2 1 /* 2-bit codes, value = code - 1 (code 3 decodes to +2); fp16 scales */
+#define BPW_INT4_SYM 2 /* 4-bit codes, value = code - 8                                     */
+#define BPW_INT4_ZP 3  /* 4-bit codes, value = code - zero[n, group]                        */
+
+/* ---- element types --------------------------------------------------- */
+#define BPW_F32 0
+#define BPW_F16 1
+#define BPW_BF16 2
+#define BPW_I8 3
+#define BPW_I32 4
+
+/* ---- source layouts accepted by bpw_prepare_packed ------------------- */
+#define BPW_SRC_PQ2_BLOCKS 1 /* ternary only: [N][G][34] = fp16 scale (little-endian) + 32 code bytes */
+#define BPW_SRC_PLANES 2     /* packed code plane (layout below) + scales [N][G] (+ zero plane)      */
+#define BPW_SRC_CODES_U8 3   /* one code per byte [N][K] + scales [N][G] (+ zeros one per byte [N][G]) */
+
+/* ---- partial-sum cores for bpw_partials ------------------------------ */
+#define BPW_PATH_GEMV 0
+#define BPW_PATH_GEMM 1
+
+/* ---- HBM probes for bpw_probe ---------------------------------------- */
+#define BPW_PROBE_READ 0 /* read every byte of src (16-byte loads), write one word per block to dst */
+#define BPW_PROBE_COPY 1 /* copy bytes from src to dst (16-byte loads and stores)                   */
+
+/*
+ * Prepared (device) weight layout, "separate planes": one code plane, one
+ * scale plane, optionally one zero-point plane and one permutation.
+ *  codes  : TERNARY2  uint8 [N][K/4]; in each row, byte 32g+j holds weights
+ *                     128g+4j+t at bits 2t..2t+1 (t = 0..3).
+ *           INT4_*    uint8 [N][K/2]; byte b holds weight 2b in the low
+ *                     nibble and 2b+1 in the high nibble.
+ *  scales : [N][G] of scale_dtype (G = K/128).
+ *  zeros  : INT4_ZP only: uint8 [N][ceil(G/2)]; group 2i in the low nibble,
+ *           2i+1 in the high nibble. NULL otherwise.
+ *  perm   : act-order only: int32 [K]; column j of the prepared planes is
+ *           column perm[j] of the original weight, so group j/128 of the
+ *           planes is contiguous. NULL when the weight has no act order.
+ * With act order, y = x[:, perm] @ W_prepared^T, which equals x @ W^T.
+ */
+typedef struct bpw_weights {
+  int32_t fmt;         /* BPW_TERNARY2 | BPW_INT4_SYM | BPW_INT4_ZP          */
+  int32_t scale_dtype; /* BPW_F16 | BPW_BF16 (TERNARY2: BPW_F16 only)        */
+  int32_t group;       /* 128                                                */
+  int32_t reserved;    /* must be 0                                          */
+  int64_t n;           /* output features (rows of W), >= 1                  */
+  int64_t k;           /* input features, a positive multiple of 128         */
+  const void* codes;   /* device                                             */
+  const void* scales;  /* device                                             */
+  const void* zeros;   /* device or NULL                                     */
+  const int32_t* perm; /* device or NULL                                     */
+} bpw_weights;
+
+typedef struct bpw_sizes {
+  size_t codes, scales, zeros, perm; /* bytes of each prepared plane (0 = absent) */
+} bpw_sizes;
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int bpw_version(void);
+
+/* Thread-local text of the last error of this thread ("" after success). */
+const char* bpw_last_error(void);
+
+/*
+ * Byte sizes of the prepared planes for an N x K weight of format fmt.
+ * Logical weight bytes per product = codes + scales + zeros (the perm plane is
+ * K int32 and is read once per call, not per row). Host only; never touches
+ * the GPU.
+ */
+int bpw_packed_sizes(int fmt, int scale_dtype, int64_t n, int64_t k, int group, int has_perm,
+                     bpw_sizes* out);
+
+/*
+ * Repack user weights into the prepared planes (one-time, host only, no GPU).
+ * Source: "Kernel experiments", Test 1 (prepare_pq2 splits 34-byte blocks into
+ * code and scale planes, with the same 34 bytes per 128 weights) and the mate
+ * PR's "Act order" section (sort K by group, keep the permutation, refuse a
+ * g_idx whose sorted groups are not runs of exactly 128).
+ *  src_codes  host, layout per src_format:
+ *               PQ2_BLOCKS [N][G*34] (ternary; src_scales must be NULL),
+ *               PLANES     the prepared code layout above (original K order),
+ *               CODES_U8   [N][K] one code per byte (0..3 ternary, 0..15 int4).
+ *  src_scales host [N][G] of scale_dtype (NULL for PQ2_BLOCKS).
+ *  src_zeros  host, INT4_ZP only: PLANES -> [N][ceil(G/2)] nibbles (low = even
+ *             group), CODES_U8 -> [N][G] one per byte. NULL otherwise.
+ *  g_idx      host int32 [K] group of each original column, or NULL (no act
+ *             order). Every group id must be in 0..G-1 and own exactly 128
+ *             columns, else BPW_EGIDX naming the group and its count.
+ *  dst_*      host buffers sized by bpw_packed_sizes (dst_zeros NULL unless
+ *             INT4_ZP, dst_perm NULL unless g_idx). perm = stable argsort(g_idx).
+ * Codes out of range (ternary > 3, int4 > 15 in CODES_U8) return BPW_EINVAL.
+ */
+int bpw_prepare_packed(int fmt, int src_format, int scale_dtype, int64_t n, int64_t k, int group,
+                       const void* src_codes, const void* src_scales, const uint8_t* src_zeros,
+                       const int32_t* g_idx, void* dst_codes, void* dst_scales, void* dst_zeros,
+                       int32_t* dst_perm);
+
+/*
+ * int8 activation quantiser, one scale per row. Source: "Kernel experiments",
+ * Test 6 (group-128 quantiser) and Test 8 (the fp32 reciprocal-multiply scale):
+ *   scale[m] = fl32(max_k |x[m,k]| * fl32(1/127)),
+ *   q[m,k]   = clamp(round_half_even(x[m,k] / (scale[m] > 0 ? scale[m] : 1)), -127, 127)
+ * with an IEEE fp32 division. x: device [M][K] of x_dtype (F32/F16/BF16);
+ * q: device int8 [M][K]; x_scale: device fp32 [M]. K >= 1, no multiple needed.
+ */
+int bpw_quantize_rows(const void* x, int x_dtype, int64_t m, int64_t k, int8_t* q, float* x_scale,
+                      void* stream);
+
+/*
+ * Device workspace (bytes, 256-byte aligned start) that bpw_gemv_packed /
+ * bpw_gemm_packed need for this weight, M and activation type; 0 if none.
+ * entry: BPW_PATH_GEMV or BPW_PATH_GEMM. Host only.
+ */
+int bpw_workspace_size(const bpw_weights* w, int64_t m, int x_dtype, int entry, size_t* bytes);
+
+/*
+ * y = x @ W^T, decode-shaped (tuned for M <= 16; any M >= 1 accepted).
+ * Supported (fmt, x_dtype): TERNARY2 x I8 (x_scale device fp32 [M] required),
+ * INT4_SYM / INT4_ZP x F16 or BF16 (scale_dtype == x_dtype, x_scale NULL).
+ * Anything else returns BPW_EUNSUPPORTED. y: device [M][N] of y_dtype
+ * (F32, F16 or BF16; round-to-nearest-even from fp32).
+ * Numerics: int8 -> exact int32 group partials, fp32 fold
+ * y = x_scale[m] * sum_g scale[n,g] * P[m,n,g]. 4-bit -> the group partial
+ * sum_k x * (code - zero) is accumulated in fp32 from exact products and the
+ * group scale is applied to it (the weight is never rounded).
+ * workspace: device, at least bpw_workspace_size(..., BPW_PATH_GEMV) bytes, or
+ * NULL when that size is 0. M <= 32 runs the decode kernels; larger M is routed
+ * to the bpw_gemm_packed kernels (and takes their numerics).
+ */
+int bpw_gemv_packed(const bpw_weights* w, const void* x, int x_dtype, const float* x_scale,
+                    int64_t m, void* y, int y_dtype, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/*
+ * y = x @ W^T, prefill-shaped (large M). Same arguments and combinations as
+ * bpw_gemv_packed. Numerics: int8 -> as above (int8 MFMA, exact int32 group
+ * partials). 4-bit -> each weight is dequantised to the activation dtype,
+ * round-to-nearest-even of (code - zero) * scale, then multiplied on MFMA with
+ * fp32 accumulation (the float path of the mate PR: unpack int4 to the
+ * activation type before the matrix instruction).
+ */
+int bpw_gemm_packed(const bpw_weights* w, const void* x, int x_dtype, const float* x_scale,
+                    int64_t m, void* y, int y_dtype, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/*
+ * Verification only: exact int32 group partials
+ *   out[(m-m0)][(n-n0)][g] = sum_{k in group g} q[m,k] * (code[n,k] - 1)
+ * for m0 <= m < m1, n0 <= n < n1, computed by the same kernel core as the
+ * product (path BPW_PATH_GEMV: M <= 32 only; BPW_PATH_GEMM: any M).
+ * TERNARY2 weights without act order only. q: device int8 [M][K].
+ * out: device int32 [(m1-m0)][(n1-n0)][G]. workspace as for the product.
+ */
+int bpw_partials(const bpw_weights* w, const int8_t* q, int64_t m, int path, int64_t m0,
+                 int64_t m1, int64_t n0, int64_t n1, int32_t* out, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
+/*
+ * Memory-system probe used to calibrate byte counters: BPW_PROBE_READ reads
+ * `bytes` from src (device, 16-byte aligned, bytes % 16 == 0) and writes one
+ * uint32 per workgroup into dst (device, at least bpw_probe_blocks(bytes) * 4
+ * bytes); BPW_PROBE_COPY copies `bytes` from src to dst.
+ */
+int bpw_probe(int kind, const void* src, void* dst, size_t bytes, void* stream);
+int64_t bpw_probe_blocks(size_t bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BPW_H_ */

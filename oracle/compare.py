@@ -1,0 +1,46 @@
+"""Parity rule between a GPU output and the fp64 oracle (test infrastructure only).
+
+A product rounded to fp16/bf16 cannot meet an elementwise relative bound of
+1e-3 against the unrounded fp64 reference (bf16 alone is up to 2**-8 relative).
+The rule: each output must be within 1e-3 (relative, with a floor tau for
+results near zero from cancellation) of the reference, plus half a unit in the
+last place of the output dtype at the reference value:
+
+    |y - y_ref| <= 1e-3 * max(|y_ref|, tau) + ulp_out(y_ref) / 2,
+    tau = 1e-3 * rms(y_ref).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+SIG_BITS = {"f32": 24, "f16": 11, "bf16": 8}
+MIN_EXP = {"f32": -126, "f16": -14, "bf16": -126}
+
+
+def ulp(v: np.ndarray, dtype: str) -> np.ndarray:
+    """Spacing of ``dtype`` values at |v| (normal range, with the subnormal floor)."""
+    v = np.abs(np.asarray(v, np.float64))
+    _, e = np.frexp(v)                       # v = m * 2**e, 0.5 <= m < 1
+    e = np.maximum(e - 1, MIN_EXP[dtype])
+    return np.ldexp(1.0, e - (SIG_BITS[dtype] - 1))
+
+
+def compare(y, y_ref, dtype: str, rel: float = 1e-3) -> dict:
+    y = np.asarray(y, np.float64)
+    y_ref = np.asarray(y_ref, np.float64)
+    if y.shape != y_ref.shape:
+        raise ValueError(f"shape {y.shape} != {y_ref.shape}")
+    rms = float(np.sqrt(np.mean(y_ref ** 2))) if y_ref.size else 0.0
+    tau = rel * rms
+    err = np.abs(y - y_ref)
+    bound = rel * np.maximum(np.abs(y_ref), tau) + 0.5 * ulp(y_ref, dtype)
+    finite = bool(np.all(np.isfinite(y)))
+    denom = np.maximum(np.abs(y_ref), tau if tau > 0 else 1e-300)
+    return {
+        "ok": finite and bool(np.all(err <= bound)),
+        "finite": finite,
+        "worst_ratio": float(np.max(err / bound)) if y.size else 0.0,
+        "max_rel": float(np.max(err / denom)) if y.size else 0.0,
+        "normwise": float(np.max(err) / max(np.max(np.abs(y_ref)), 1e-300)) if y.size else 0.0,
+        "rel_rms": float(np.sqrt(np.sum(err ** 2) / max(np.sum(y_ref ** 2), 1e-300))) if y.size else 0.0,
+    }

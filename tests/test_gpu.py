@@ -1,0 +1,254 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle.
+
+Each case names its workload, shape and seed in the test id. Integer results
+(quantised activations, int32 group partials) must match bit for bit; float
+outputs must satisfy oracle.compare's rule (1e-3 relative plus half an output
+ulp). Inputs come from synth; both sides compute from them independently.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bit_packed_weight_amd as bpw
+import synth
+from oracle import compare, formats, quant, reference
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TORCH = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def to_dev(a: np.ndarray, dtype: str):
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64) if t.is_floating_point() else t.cpu().numpy()
+
+
+def assert_close(y, y_ref, dtype, what):
+    r = compare.compare(y, y_ref, dtype)
+    assert r["ok"], f"{what}: {r}"
+    return r
+
+
+def prepare(w: synth.Workload):
+    fmt = bpw.FORMAT_NAMES[w.fmt]
+    sd = bpw.F16 if w.scale_dtype == "f16" else bpw.BF16
+    zeros = w.zeros if w.fmt == "int4_zp" else None
+    return bpw.prepare_packed(fmt, w.codes, w.scales, zeros, w.g_idx, scale_dtype=sd, device=DEV)
+
+
+# ------------------------------------------------------------------ quantiser
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("m,k", [(1, 512), (5, 4096), (3, 1000), (64, 8192)])
+def test_quantize_rows_bit_exact(dtype, m, k):
+    rng = np.random.default_rng(m * 7 + k)
+    x = (rng.standard_normal((m, k)) * rng.uniform(0.01, 50, size=(m, 1))).astype(np.float32)
+    x[0, : min(k, 8)] = [127.0, 2.5, 3.5, -2.5, -0.5, 126.5, 0.5, 1.5][: min(k, 8)]
+    if m > 2:
+        x[2] = 0.0
+    if dtype == "f16":
+        xs = x.astype(np.float16)
+        xf = xs.astype(np.float32)
+    elif dtype == "bf16":
+        xs = synth.f32_to_bf16_bits(x)
+        xf = synth.bf16_bits_to_f32(xs)
+    else:
+        xs = xf = x
+    q, s = bpw.quantize_rows(to_dev(xs, dtype))
+    torch.cuda.synchronize()
+    q_ref, s_ref = quant.quantize_rows(xf)
+    np.testing.assert_array_equal(host(s).astype(np.float32), s_ref)
+    np.testing.assert_array_equal(host(q), q_ref)
+
+
+# ------------------------------------------------------------------ ternary x int8
+def ternary_case(m, k, n, seed, out="f16"):
+    return synth.ternary_int8(f"t{m}x{k}x{n}", seed, m, k, n, 0.005, 0.05, out)
+
+
+def run_ternary(w: synth.Workload, entry: str):
+    pw = prepare(w)
+    x = to_dev(w.x, "f32")
+    q, xs = bpw.quantize_rows(x)
+    fn = bpw.gemv_packed if entry == "gemv" else bpw.gemm_packed
+    y = fn(pw, q, xs, out_dtype=TORCH[w.out_dtype])
+    torch.cuda.synchronize()
+    q_ref, xs_ref = quant.quantize_rows(w.x)
+    np.testing.assert_array_equal(host(q), q_ref)
+    _, y_ref = reference.ternary_int8_product(q_ref, xs_ref, w.codes, w.scales)
+    return pw, q, xs, y, y_ref
+
+
+@pytest.mark.parametrize("m,k,n", [(1, 512, 256), (1, 4096, 1000), (2, 640, 333), (4, 128, 64),
+                                   (7, 1024, 520), (16, 4096, 300), (32, 256, 97), (1, 8192, 130)])
+@pytest.mark.parametrize("out", ["f32", "f16", "bf16"])
+def test_gemv_ternary_parity(m, k, n, out):
+    w = ternary_case(m, k, n, 100 + m + k + n, out)
+    _, _, _, y, y_ref = run_ternary(w, "gemv")
+    assert_close(host(y), y_ref, out, f"gemv ternary m={m} k={k} n={n}")
+
+
+@pytest.mark.parametrize("m,k,n", [(1, 256, 300), (130, 1024, 520), (300, 640, 257), (64, 128, 256)])
+def test_gemm_ternary_parity(m, k, n):
+    w = ternary_case(m, k, n, 200 + m + k + n, "f16")
+    _, _, _, y, y_ref = run_ternary(w, "gemm")
+    assert_close(host(y), y_ref, "f16", f"gemm ternary m={m} k={k} n={n}")
+
+
+@pytest.mark.parametrize("path", [bpw.PATH_GEMV, bpw.PATH_GEMM])
+@pytest.mark.parametrize("m,k,n,win", [(3, 256, 70, (0, 3, 0, 70)), (32, 512, 200, (5, 29, 33, 170)),
+                                       (1, 128, 40, (0, 1, 7, 9))])
+def test_partials_bit_exact(path, m, k, n, win):
+    # stress inputs: full int8 range and every 2-bit code including 3
+    rng = np.random.default_rng(m + k + n)
+    q = synth.random_int8(m + k, m, k)
+    codes = rng.integers(0, 4, size=(n, k), dtype=np.uint8)
+    scales = rng.uniform(0.005, 0.05, size=(n, k // 128)).astype(np.float16)
+    pw = bpw.prepare_packed(bpw.TERNARY2, codes, scales, device=DEV)
+    m0, m1, n0, n1 = win
+    p = bpw.partials(pw, to_dev(q, "i8"), path, m0, m1, n0, n1)
+    torch.cuda.synchronize()
+    p_ref = reference.ternary_partials(q[m0:m1], codes[n0:n1])
+    np.testing.assert_array_equal(host(p), p_ref)
+
+
+def test_ternary_row_independence_and_determinism():
+    w = ternary_case(8, 1024, 300, 7)
+    pw = bpw.prepare_packed(bpw.TERNARY2, w.codes, w.scales, device=DEV)
+    x = to_dev(w.x, "f32")
+    q, xs = bpw.quantize_rows(x)
+    for fn in (bpw.gemv_packed, bpw.gemm_packed):
+        y1 = fn(pw, q, xs)
+        y2 = fn(pw, q, xs)
+        q2 = q.clone()
+        q2[1:] = torch.randint(-127, 128, q2[1:].shape, device=DEV, dtype=torch.int8)
+        y3 = fn(pw, q2, xs)
+        torch.cuda.synchronize()
+        assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+        assert torch.equal(y1[0].view(torch.int16), y3[0].view(torch.int16))
+
+
+def test_outputs_fully_written_over_nan_poison():
+    w = ternary_case(5, 512, 333, 9)
+    pw = bpw.prepare_packed(bpw.TERNARY2, w.codes, w.scales, device=DEV)
+    q, xs = bpw.quantize_rows(to_dev(w.x, "f32"))
+    for fn in (bpw.gemv_packed, bpw.gemm_packed):
+        y = torch.full((5, 333), float("nan"), dtype=torch.float16, device=DEV)
+        fn(pw, q, xs, out=y)
+        torch.cuda.synchronize()
+        assert torch.isfinite(y).all()
+
+
+# ------------------------------------------------------------------ 4-bit x fp16/bf16
+def w4_case(fmt, m, k, n, seed, act_order, x_dtype):
+    if fmt == "int4_zp":
+        return synth.int4_zp_actorder(f"w{m}x{k}x{n}", seed, m, k, n, act_order=act_order, x_dtype=x_dtype)
+    return synth.int4_sym(f"w{m}x{k}x{n}", seed, m, k, n, x_dtype=x_dtype)
+
+
+def w4_reference(w: synth.Workload, rounded: bool):
+    zeros = w.zeros if w.fmt == "int4_zp" else None
+    s = w.scales_f64()
+    if rounded:
+        wt = reference.weights_int4_rounded(w.codes, s, zeros, w.g_idx, w.x_dtype)
+    else:
+        wt = reference.weights_int4(w.codes, s, zeros, w.g_idx)
+    return reference.product(w.x_f32(), wt)
+
+
+@pytest.mark.parametrize("fmt,x_dtype,act_order", [("int4_zp", "f16", True), ("int4_zp", "f16", False),
+                                                   ("int4_sym", "bf16", False), ("int4_sym", "f16", False),
+                                                   ("int4_zp", "bf16", True)])
+@pytest.mark.parametrize("m,k,n", [(1, 640, 333), (3, 128, 64), (8, 5120, 200), (16, 1024, 97), (32, 256, 130)])
+def test_gemv_w4_parity(fmt, x_dtype, act_order, m, k, n):
+    w = w4_case(fmt, m, k, n, 300 + m + k + n, act_order, x_dtype)
+    pw = prepare(w)
+    y = bpw.gemv_packed(pw, to_dev(w.x, x_dtype))
+    torch.cuda.synchronize()
+    assert_close(host(y), w4_reference(w, rounded=False), x_dtype, f"gemv {fmt} {x_dtype} m={m} k={k} n={n}")
+
+
+@pytest.mark.parametrize("fmt,x_dtype,act_order", [("int4_sym", "bf16", False), ("int4_zp", "f16", True),
+                                                   ("int4_sym", "f16", False)])
+@pytest.mark.parametrize("m,k,n", [(1, 256, 300), (200, 512, 260), (129, 1024, 513)])
+def test_gemm_w4_parity(fmt, x_dtype, act_order, m, k, n):
+    w = w4_case(fmt, m, k, n, 400 + m + k + n, act_order, x_dtype)
+    pw = prepare(w)
+    y = bpw.gemm_packed(pw, to_dev(w.x, x_dtype))
+    torch.cuda.synchronize()
+    assert_close(host(y), w4_reference(w, rounded=True), x_dtype, f"gemm {fmt} {x_dtype} m={m} k={k} n={n}")
+
+
+# ------------------------------------------------------------------ named workloads, full size
+def test_workload_ternary_tiny_full():
+    w = synth.ternary_tiny()
+    pw, q, xs, y, y_ref = run_ternary(w, "gemv")
+    assert_close(host(y), y_ref, "f32", "ternary_gemv_tiny")
+    p = bpw.partials(pw, q, bpw.PATH_GEMV, 0, 1, 0, w.n)
+    q_ref, _ = quant.quantize_rows(w.x)
+    np.testing.assert_array_equal(host(p), reference.ternary_partials(q_ref, w.codes))
+
+
+@pytest.mark.parametrize("m", [1, 16])
+def test_workload_ternary_decode_full(m):
+    w = synth.ternary_decode(m)
+    pw, q, xs, y, y_ref = run_ternary(w, "gemv")
+    assert_close(host(y), y_ref, "f16", f"ternary_decode m={m}")
+    # int32 group partials of the whole product, bit-exact
+    p = bpw.partials(pw, q, bpw.PATH_GEMV, 0, m, 0, w.n)
+    q_ref, _ = quant.quantize_rows(w.x)
+    np.testing.assert_array_equal(host(p), reference.ternary_partials(q_ref, w.codes))
+
+
+@pytest.mark.parametrize("m", [1, 8])
+def test_workload_w4a16_decode_full(m):
+    w = synth.w4a16_decode(m)
+    pw = prepare(w)
+    y = bpw.gemv_packed(pw, to_dev(w.x, "f16"))
+    torch.cuda.synchronize()
+    assert_close(host(y), w4_reference(w, rounded=False), "f16", f"w4a16_decode m={m}")
+
+
+def test_workload_w4a16_prefill_sampled():
+    w = synth.w4a16_prefill()
+    pw = prepare(w)
+    y = bpw.gemm_packed(pw, to_dev(w.x, "bf16"))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([[0, w.m - 1], rng.choice(w.m, 30, replace=False)]))
+    cols = np.unique(np.concatenate([np.arange(64), np.arange(w.n - 64, w.n), rng.choice(w.n, 512, replace=False)]))
+    wt = reference.weights_int4_rounded(w.codes[cols], w.scales_f64()[cols], None, None, "bf16")
+    y_ref = reference.product(w.x_f32()[rows], wt)
+    assert_close(host(y)[np.ix_(rows, cols)], y_ref, "bf16", "w4a16_prefill sampled")
+
+
+def test_workload_ternary_prefill_sampled():
+    w = synth.ternary_prefill()
+    pw = bpw.prepare_packed(bpw.TERNARY2, w.codes, w.scales, device=DEV)
+    x = to_dev(w.x, "f32")
+    q, xs = bpw.quantize_rows(x)
+    y = bpw.gemm_packed(pw, q, xs, out_dtype=torch.float16)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([[0, w.m - 1], rng.choice(w.m, 14, replace=False)]))
+    cols = np.unique(np.concatenate([np.arange(32), np.arange(w.n - 32, w.n), rng.choice(w.n, 256, replace=False)]))
+    q_ref, xs_ref = quant.quantize_rows(w.x[rows])
+    np.testing.assert_array_equal(host(q)[rows], q_ref)
+    _, y_ref = reference.ternary_int8_product(q_ref, xs_ref, w.codes[cols], w.scales[cols])
+    assert_close(host(y)[np.ix_(rows, cols)], y_ref, "f16", "ternary_int8_prefill sampled")
+    # int32 group partials on corner and random windows, through the GEMM core
+    wins = [(0, 64, 0, 256), (w.m - 64, w.m, w.n - 256, w.n), (0, 64, w.n - 256, w.n), (w.m - 64, w.m, 0, 256)]
+    for _ in range(2):
+        a, b = int(rng.integers(0, w.m - 64)), int(rng.integers(0, w.n - 256))
+        wins.append((a, a + 64, b, b + 256))
+    for (m0, m1, n0, n1) in wins:
+        p = bpw.partials(pw, q, bpw.PATH_GEMM, m0, m1, n0, n1)
+        torch.cuda.synchronize()
+        q_win, _ = quant.quantize_rows(w.x[m0:m1])        # the oracle quantises its own rows
+        np.testing.assert_array_equal(host(p), reference.ternary_partials(q_win, w.codes[n0:n1]),
+                                      err_msg=f"window {(m0, m1, n0, n1)}")

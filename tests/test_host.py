@@ -1,0 +1,213 @@
+"""Host-side checks of the C ABI (no GPU): exports, sizes, prepare, validation.
+
+Every validation error is detected on the host before any HIP call, so these
+tests force each status from the CPU with placeholder (never dereferenced)
+pointers.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import bit_packed_weight_amd as bpw
+from oracle import formats, reference
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_header_symbol():
+    text = open(os.path.join(ROOT, "include", "bpw.h")).read()
+    declared = set(re.findall(r"\b(bpw_[a-z0-9_]+)\s*\(", text))
+    assert {"bpw_prepare_packed", "bpw_gemv_packed", "bpw_gemm_packed", "bpw_partials"} <= declared
+    lib = bpw.lib()
+    for name in sorted(declared):
+        assert hasattr(lib, name), name
+    assert set(bpw.EXPORTS) == declared
+    assert bpw.version() >= 100
+
+
+def _golden(name):
+    rows = []
+    for line in open(os.path.join(ROOT, "tests", "golden", name)):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            rows.append(line.split())
+    return rows
+
+
+def test_packed_sizes_match_logical_byte_formula():
+    # "Kernel experiments", Test 19: bytes per call = n*k//4 + n*(k//128)*2, which
+    # Test 25 writes as n*(k//128)*34.
+    for name, n, k in _golden("pq2_shapes.txt"):
+        n, k = int(n), int(k)
+        s = bpw.packed_sizes(bpw.TERNARY2, n, k)
+        assert s.codes + s.scales == n * k // 4 + n * (k // 128) * 2 == n * (k // 128) * 34
+        assert s.zeros == 0 and s.perm == 0
+    s = bpw.packed_sizes(bpw.INT4_ZP, 13824, 5120, bpw.F16, True)
+    assert (s.codes, s.scales, s.zeros, s.perm) == (13824 * 2560, 13824 * 40 * 2, 13824 * 20, 5120 * 4)
+    s = bpw.packed_sizes(bpw.INT4_ZP, 3, 384, bpw.F16)     # odd group count: ceil(G/2) zero bytes
+    assert s.zeros == 3 * 2
+
+
+@pytest.mark.parametrize("src", ["codes", "planes", "pq2"])
+def test_prepare_ternary_bit_exact_against_oracle(src):
+    w = synth.ternary_int8("t", 31, 1, 512, 37, 0.005, 0.05, "f16")
+    codes = w.codes.copy()
+    codes[0, :4] = 3                                # every code value, incl. 3
+    plane = formats.pack_ternary(codes)
+    if src == "codes":
+        out = bpw.prepare_packed_host(bpw.TERNARY2, codes, w.scales)
+    elif src == "planes":
+        out = bpw.prepare_packed_host(bpw.TERNARY2, plane, w.scales, src_format=bpw.SRC_PLANES)
+    else:
+        raw = formats.join_pq2_blocks(plane, w.scales)
+        out = bpw.prepare_packed_host(bpw.TERNARY2, raw, None, src_format=bpw.SRC_PQ2_BLOCKS)
+    np.testing.assert_array_equal(out["codes"], plane)
+    np.testing.assert_array_equal(out["scales"], w.scales.view(np.uint16))
+    np.testing.assert_array_equal(formats.unpack_ternary(out["codes"], 512), codes)
+
+
+@pytest.mark.parametrize("fmt", ["int4_zp", "int4_sym"])
+@pytest.mark.parametrize("act_order", [False, True])
+@pytest.mark.parametrize("src", ["codes", "planes"])
+def test_prepare_int4_bit_exact_against_oracle(fmt, act_order, src):
+    k = 640                                        # 5 groups: odd zero-point count
+    w = synth.int4_zp_actorder("t", 41, 2, k, 9, act_order=act_order)
+    zeros = w.zeros if fmt == "int4_zp" else None
+    code = bpw.INT4_ZP if fmt == "int4_zp" else bpw.INT4_SYM
+    if src == "codes":
+        out = bpw.prepare_packed_host(code, w.codes, w.scales, zeros, w.g_idx)
+    else:
+        zp = None if zeros is None else formats.pack_zeros(zeros)
+        out = bpw.prepare_packed_host(code, formats.pack_int4(w.codes), w.scales, zp, w.g_idx,
+                                      src_format=bpw.SRC_PLANES)
+    if act_order:
+        perm = reference.act_order_perm(w.g_idx, k)
+        np.testing.assert_array_equal(out["perm"], perm)
+        sorted_codes = w.codes[:, perm]
+    else:
+        assert out["perm"] is None
+        sorted_codes = w.codes
+    np.testing.assert_array_equal(out["codes"], formats.pack_int4(sorted_codes))
+    np.testing.assert_array_equal(out["scales"], w.scales.view(np.uint16))
+    if zeros is not None:
+        np.testing.assert_array_equal(out["zeros"], formats.pack_zeros(zeros))
+    # the prepared planes reproduce the original product: x[:, perm] @ W_sorted^T == x @ W^T
+    x = w.x.astype(np.float64)
+    w_orig = reference.weights_int4(w.codes, w.scales, zeros, w.g_idx)
+    w_prep = reference.weights_int4(formats.unpack_int4(out["codes"], k), w.scales,
+                                    None if zeros is None else formats.unpack_zeros(out["zeros"], 5))
+    xp = x[:, out["perm"]] if act_order else x
+    np.testing.assert_allclose(reference.product(xp, w_prep), reference.product(x, w_orig), rtol=1e-12, atol=1e-12)
+
+
+def _expect(status, fn, *args, match=None):
+    with pytest.raises(bpw.BpwError) as e:
+        fn(*args)
+    assert e.value.status == status, str(e.value)
+    if match:
+        assert re.search(match, str(e.value)), str(e.value)
+
+
+def test_prepare_refuses_bad_inputs_and_writes_nothing():
+    w = synth.int4_zp_actorder("t", 5, 1, 256, 4)
+    bad = w.g_idx.copy()
+    bad[np.flatnonzero(bad == 0)[0]] = 1
+    _expect(bpw.EGIDX, bpw.prepare_packed_host, bpw.INT4_ZP, w.codes, w.scales, w.zeros, bad,
+            match="group 0 has 127 members")
+    bad = w.g_idx.copy()
+    bad[3] = 7
+    _expect(bpw.EGIDX, bpw.prepare_packed_host, bpw.INT4_ZP, w.codes, w.scales, w.zeros, bad, match="outside")
+    _expect(bpw.ESHAPE, bpw.prepare_packed_host, bpw.TERNARY2, np.zeros((2, 200), np.uint8),
+            np.zeros((2, 1), np.float16))
+    _expect(bpw.EUNSUPPORTED, bpw.prepare_packed_host, bpw.INT4_SYM, np.zeros((2, 34), np.uint8), None,
+            None, None, bpw.SRC_PQ2_BLOCKS)
+    _expect(bpw.EINVAL, bpw.prepare_packed_host, bpw.INT4_ZP, w.codes, w.scales, None)   # zeros missing
+    # out-of-range code: the destination planes keep their previous contents
+    codes = w.codes.copy()
+    codes[1, 100] = 16
+    lib = bpw.lib()
+    dst = np.full(4 * 128, 0xAB, np.uint8)
+    dsc = np.full(4 * 2 * 2, 0xAB, np.uint8)
+    dz = np.full(4, 0xAB, np.uint8)
+    st = lib.bpw_prepare_packed(bpw.INT4_ZP, bpw.SRC_CODES_U8, bpw.F16, 4, 256, 128,
+                                codes.ctypes.data_as(ctypes.c_void_p), w.scales.ctypes.data_as(ctypes.c_void_p),
+                                w.zeros.ctypes.data_as(ctypes.c_void_p), None,
+                                dst.ctypes.data_as(ctypes.c_void_p), dsc.ctypes.data_as(ctypes.c_void_p),
+                                dz.ctypes.data_as(ctypes.c_void_p), None)
+    assert st == bpw.EINVAL and "exceeds 15" in bpw.last_error()
+    assert np.all(dst == 0xAB) and np.all(dsc == 0xAB) and np.all(dz == 0xAB)
+
+
+# --------------------------------------------------------------- product validation
+def _weights(fmt=bpw.TERNARY2, n=64, k=256, scale_dtype=bpw.F16, zeros=False, perm=False, codes=4096):
+    return bpw.BpwWeights(fmt, scale_dtype, 128, 0, n, k, codes, 8192, 12288 if zeros else None,
+                          16384 if perm else None)
+
+
+def _gemv(w, x=65536, x_dtype=bpw.I8, xs=1024, m=1, y=131072, y_dtype=bpw.F16, ws=None, ws_bytes=0):
+    return bpw.lib().bpw_gemv_packed(ctypes.byref(w), x, x_dtype, xs, m, y, y_dtype, ws, ws_bytes, None)
+
+
+def test_product_validation_statuses():
+    assert _gemv(_weights(k=200)) == bpw.ESHAPE
+    assert "multiple of 128" in bpw.last_error()
+    assert _gemv(_weights(), m=0) == bpw.ESHAPE
+    assert _gemv(_weights(), x=None) == bpw.EINVAL
+    assert _gemv(_weights(), xs=None) == bpw.EINVAL                      # int8 needs row scales
+    assert _gemv(_weights(), x_dtype=bpw.F16, xs=None) == bpw.EUNSUPPORTED
+    assert _gemv(_weights(), y_dtype=bpw.I32) == bpw.EUNSUPPORTED
+    assert _gemv(_weights(codes=4100)) == bpw.EALIGN
+    assert _gemv(_weights(), x=65540) == bpw.EALIGN
+    w = _weights()
+    w.group = 64
+    assert _gemv(w) == bpw.EUNSUPPORTED
+    w = _weights()
+    w.reserved = 1
+    assert _gemv(w) == bpw.EINVAL
+    assert _gemv(_weights(scale_dtype=bpw.BF16)) == bpw.EUNSUPPORTED     # ternary: fp16 scales
+    assert _gemv(_weights(perm=True)) == bpw.EUNSUPPORTED                # ternary act order
+    # 4-bit
+    assert _gemv(_weights(bpw.INT4_ZP), x_dtype=bpw.F16, xs=None) == bpw.EINVAL          # zero plane missing
+    assert _gemv(_weights(bpw.INT4_SYM, zeros=True), x_dtype=bpw.F16, xs=None) == bpw.EINVAL
+    assert _gemv(_weights(bpw.INT4_SYM), x_dtype=bpw.BF16, xs=None) == bpw.EUNSUPPORTED    # scale/act dtype
+    assert _gemv(_weights(bpw.INT4_SYM), x_dtype=bpw.F16, xs=1024) == bpw.EINVAL
+    assert _gemv(_weights(bpw.INT4_SYM), x_dtype=bpw.I8) == bpw.EUNSUPPORTED
+    # act order needs a workspace
+    wp = _weights(bpw.INT4_SYM, perm=True)
+    assert _gemv(wp, x_dtype=bpw.F16, xs=None, m=4) == bpw.EINVAL
+    assert "workspace" in bpw.last_error()
+    assert _gemv(wp, x_dtype=bpw.F16, xs=None, m=4, ws=1 << 20, ws_bytes=16) == bpw.ESHAPE
+    assert _gemv(wp, x_dtype=bpw.F16, xs=None, m=4, ws=(1 << 20) + 16, ws_bytes=1 << 20) == bpw.EALIGN
+
+
+def test_workspace_sizes():
+    need = ctypes.c_size_t()
+    lib = bpw.lib()
+    w = _weights(k=4096, n=14336)
+    assert lib.bpw_workspace_size(ctypes.byref(w), 1, bpw.I8, bpw.PATH_GEMV, ctypes.byref(need)) == 0
+    assert need.value == 0
+    assert lib.bpw_workspace_size(ctypes.byref(w), 2048, bpw.I8, bpw.PATH_GEMM, ctypes.byref(need)) == 0
+    assert need.value == 2048 * 4096
+    wp = _weights(bpw.INT4_ZP, k=5120, zeros=True, perm=True)
+    assert lib.bpw_workspace_size(ctypes.byref(wp), 8, bpw.F16, bpw.PATH_GEMV, ctypes.byref(need)) == 0
+    assert need.value == 8 * 5120 * 2
+
+
+def test_partials_and_probe_validation():
+    lib = bpw.lib()
+    w = _weights(n=64, k=256)
+    assert lib.bpw_partials(ctypes.byref(w), 65536, 4, bpw.PATH_GEMV, 0, 5, 0, 8, 4096, None, 0, None) == bpw.ESHAPE
+    assert lib.bpw_partials(ctypes.byref(w), 65536, 4, bpw.PATH_GEMV, 0, 4, 8, 8, 4096, None, 0, None) == bpw.ESHAPE
+    assert lib.bpw_partials(ctypes.byref(w), 65536, 40, bpw.PATH_GEMV, 0, 4, 0, 8, 4096, None, 0, None) == bpw.ESHAPE
+    assert lib.bpw_partials(ctypes.byref(w), 65536, 4, 7, 0, 4, 0, 8, 4096, None, 0, None) == bpw.EINVAL
+    assert lib.bpw_partials(ctypes.byref(w), 65536, 4, bpw.PATH_GEMM, 0, 4, 0, 8, 4096, None, 0, None) == bpw.EINVAL
+    w4 = _weights(bpw.INT4_SYM)
+    assert lib.bpw_partials(ctypes.byref(w4), 65536, 4, bpw.PATH_GEMV, 0, 4, 0, 8, 4096, None, 0, None) == bpw.EUNSUPPORTED
+    assert lib.bpw_probe(9, 4096, 8192, 1024, None) == bpw.EINVAL
+    assert lib.bpw_probe(bpw.PROBE_READ, 4096, 8192, 1000, None) == bpw.ESHAPE
+    assert lib.bpw_quantize_rows(4096, bpw.I8, 1, 16, 8192, 12288, None) == bpw.EUNSUPPORTED
+    assert lib.bpw_quantize_rows(None, bpw.F32, 1, 16, 8192, 12288, None) == bpw.EINVAL
