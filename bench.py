@@ -95,6 +95,16 @@ def bench_ternary_decode(bpw, synth, torch, np, steps, warmup):
     return w, nbytes, ms, ms_full, len(copies)
 
 
+def bench_probe(bpw, torch, nbytes, steps, warmup):
+    """Plain streaming read of nbytes per call over rotated buffers (>= 1 GiB)."""
+    count = math.ceil((1 << 30) / nbytes)
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(i % 251) for i in range(count)]
+    sink = torch.empty(bpw.probe_blocks(nbytes) * 4, dtype=torch.uint8, device="cuda")
+    ms = time_graph(torch, lambda i: bpw.probe(bpw.PROBE_READ, bufs[i % count], sink), steps, warmup)
+    return {"workload": "hbm_read_probe", "bytes": nbytes, "us_per_call": ms * 1e3, "GB_s": nbytes / (ms * 1e6),
+            "copies": count}
+
+
 def bench_w4_decode(bpw, synth, torch, np, steps, warmup):
     w = synth.w4a16_decode(1)
     planes = bpw.prepare_packed_host(bpw.INT4_ZP, w.codes, w.scales, w.zeros, w.g_idx)
@@ -185,6 +195,9 @@ def main():
     gbs = nbytes / (ms * 1e6)
     log(f"[bench] ternary decode: {ms * 1e3:.2f} us/call, {gbs:.0f} GB/s; complete call {ms_full * 1e3:.2f} us")
     extra = []
+    probe = bench_probe(bpw, torch, nbytes, args.steps, args.warmup)
+    log(f"[bench] {json.dumps(probe)}")
+    extra.append(probe)
     if not args.no_extra:
         for fn, steps, warm in ((bench_w4_decode, 900, 300), (bench_w4_prefill, 30, 6), (bench_ternary_prefill, 12, 3)):
             r = fn(bpw, synth, torch, np, steps, warm)

@@ -95,4 +95,13 @@ __device__ __forceinline__ int xcd_swizzle(int bid, int nblocks) {
   return base + local;
 }
 
+// Allow a kernel to launch with more than 64 KB of dynamic LDS (gfx950 has 160 KB
+// per CU). Called on the host before such a launch; cheap after the first call.
+template <typename K>
+inline void allow_lds(K* kernel, size_t bytes) {
+  if (bytes > 64 * 1024)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
+}
+
 }  // namespace bpw

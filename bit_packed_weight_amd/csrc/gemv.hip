@@ -1,11 +1,11 @@
 // Decode-shaped products (M <= 32) on gfx950 MFMA.
 //
-// Workgroup = one tile of 32 weight rows; its NW waves split K into contiguous
-// group ranges; the activations of all M rows are staged once into LDS in the
-// order the matrix instruction reads them; the per-wave fp32 partials are summed
-// across waves in a fixed order. Each weight byte is read from HBM exactly once,
-// with 16-byte loads (two lanes cover one 32-byte ternary group of a row, four
-// 16-byte loads cover one 64-byte 4-bit group).
+// M = 1: each wave streams whole weight rows (every weight byte read from HBM
+// exactly once, with fully coalesced 16-byte / 8-byte loads along the row) and
+// reduces the row with DPP. M <= 32: a workgroup owns 32 weight rows, its waves
+// split K into contiguous group ranges and feed MFMA; activations are staged
+// once into LDS in the order the matrix instruction reads them; the per-wave
+// fp32 partials are summed across waves in a fixed order.
 //
 // Ternary x int8 -- "Kernel experiments: recorded evidence", Test 6 (integer
 // group dots, fp32 scale fold) and Test 21 (code planes of a packed byte
@@ -27,10 +27,111 @@ constexpr int kRows = 32;                    // weight rows per workgroup (MFMA 
 constexpr size_t kLdsBudget = 128 * 1024;    // staged activations per workgroup
 constexpr int kMaxG = 8;                     // groups kept in flight per wave
 
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
 // D layout of a 32x32 MFMA: lane l holds column l % 32 and rows
 // 8*(r/4) + 4*(l/32) + r%4 for its 16 accumulator registers r.
 __device__ __forceinline__ int d_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
+// Sum over the 64 lanes of a wave in a fixed order; every lane gets the total.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+// ---------------------------------------------------------------- ternary, M = 1
+// K a multiple of 4096. Each wave streams R whole rows with one 1 KB load
+// instruction per 4096 columns: lane l holds the 64 codes of columns
+// 64l..64l+63 of each 4096-column chunk (half a 128-group). The lane's 64
+// activation bytes sit in registers in plane order; each code plane of a packed
+// word is one v_dot4 against the matching activation word; the code - 1 offset
+// is minus the half-group sum of q; the half-group partial is folded with its
+// fp32 scale and the row total is a wave reduction.
+template <int R, int CH, typename TOut, bool PARTIALS>
+__global__ __launch_bounds__(256) void gemv_t2_row_kernel(
+    const uint8_t* __restrict__ codes, const __half* __restrict__ wscale,
+    const int8_t* __restrict__ q, const float* __restrict__ x_scale, int N, int K,
+    TOut* __restrict__ y, int32_t* __restrict__ pout, int pn0, int pn1) {
+  const int lane = threadIdx.x & 63;
+  const int row0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * R;
+  if (row0 >= N) return;                        // whole wave; this kernel has no barriers
+  const int KB = K >> 2, G = K >> 7;
+  uint4 cw[R][CH];
+  float sv[R][CH];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const size_t row = static_cast<size_t>(min(row0 + r, N - 1));
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      cw[r][c] = *reinterpret_cast<const uint4*>(codes + row * KB + c * 1024 + lane * 16);
+      sv[r][c] = __half2float(wscale[row * G + 32 * c + (lane >> 1)]);
+    }
+  }
+  uint4 qp[CH][4];
+  int th[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const uint4* src = reinterpret_cast<const uint4*>(q + c * 4096 + lane * 64);
+    uint4 in[4] = {src[0], src[1], src[2], src[3]};
+    to_plane_order(in, qp[c]);
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sum = sum_i8x4(in[i].x, sum);
+      sum = sum_i8x4(in[i].y, sum);
+      sum = sum_i8x4(in[i].z, sum);
+      sum = sum_i8x4(in[i].w, sum);
+    }
+    th[c] = sum;
+  }
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    acc[r] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const uint32_t wv[4] = {cw[r][c].x, cw[r][c].y, cw[r][c].z, cw[r][c].w};
+      const uint32_t qv[4][4] = {{qp[c][0].x, qp[c][0].y, qp[c][0].z, qp[c][0].w},
+                                 {qp[c][1].x, qp[c][1].y, qp[c][1].z, qp[c][1].w},
+                                 {qp[c][2].x, qp[c][2].y, qp[c][2].z, qp[c][2].w},
+                                 {qp[c][3].x, qp[c][3].y, qp[c][3].z, qp[c][3].w}};
+      int p = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          p = __builtin_amdgcn_sdot4(static_cast<int>(code_plane(wv[u], t)), static_cast<int>(qv[t][u]), p, false);
+      p -= th[c];
+      if (PARTIALS) {
+        const int pg = p + __shfl_xor(p, 1);
+        const int row = row0 + r;
+        if ((lane & 1) == 0 && row < N && row >= pn0 && row < pn1)
+          pout[static_cast<size_t>(row - pn0) * G + 32 * c + (lane >> 1)] = pg;
+      } else {
+        acc[r] = fmaf(static_cast<float>(p), sv[r][c], acc[r]);
+      }
+    }
+  }
+  if (PARTIALS) return;
+  const float xs = x_scale[0];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float v = wave_sum(acc[r]);
+    if (lane == r && row0 + r < N) store_out(y + row0 + r, v * xs);
+  }
+}
+
+// ---------------------------------------------------------------- ternary, M <= 32
+// int8 MFMA (i32_32x32x32_i8). Workgroup = 32 weight rows. The rows are first
+// copied whole into LDS with coalesced 16-byte loads along each row; then each
+// wave reads its K-slice in MFMA layout: lane (n, h) takes 16 bytes of row n
+// (half a 32-byte group), whose four code planes are the B operands of four
+// MFMAs; the A operands are the plane-ordered activations, staged once.
 template <int NW, int FOLD, typename TOut, bool PARTIALS>
 __global__ __launch_bounds__(NW * 64) void gemv_t2_kernel(
     const uint8_t* __restrict__ codes, const __half* __restrict__ wscale,
@@ -40,29 +141,50 @@ __global__ __launch_bounds__(NW * 64) void gemv_t2_kernel(
   extern __shared__ __align__(16) uint8_t smem[];
   const int G = K >> 7;
   const int KB = K >> 2;
+  const int CS = KB + 16;                                        // conflict-free row stride
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = (blockIdx.x + tile0) * kRows;
-  uint8_t* qs = smem;                                            // [M][K] plane order
-  int* ts = reinterpret_cast<int*>(smem + static_cast<size_t>(M) * K);   // [M][G] group sums
+  uint8_t* cs = smem;                                            // [32][CS] code rows
+  uint8_t* qs = smem + kRows * CS;                               // [M][K] plane order
+  int* ts = reinterpret_cast<int*>(qs + static_cast<size_t>(M) * K);   // [M][G] group sums
 
   const int gpw = (G + NW - 1) / NW;
   const int gb = min(G, wave * gpw);
   const int ge = min(G, gb + gpw);
   const int n = lane & 31, h = lane >> 5;
   const int row = min(n0 + n, N - 1);
-  const uint8_t* crow = codes + static_cast<size_t>(row) * KB + h * 16;
   const __half* srow = wscale + static_cast<size_t>(row) * G;
 
-  // Issue this wave's first weight loads before staging the activations.
-  uint4 cw[kMaxG];
+  // Copy the tile's code rows into LDS: flat 16-byte chunks, consecutive threads
+  // on consecutive chunks of a row. The first batch is issued before staging q.
+  constexpr int MAXL = 8;
+  const int cpr = KB >> 4, total = kRows * cpr;
+  uint4 cv[MAXL];
+  auto load_batch = [&](int base) {
+#pragma unroll
+    for (int i = 0; i < MAXL; ++i) {
+      const int c = base + tid + NW * 64 * i;
+      if (c < total) {
+        const int r = c / cpr, col = c - r * cpr;
+        cv[i] = *reinterpret_cast<const uint4*>(codes + static_cast<size_t>(min(n0 + r, N - 1)) * KB + col * 16);
+      }
+    }
+  };
+  auto store_batch = [&](int base) {
+#pragma unroll
+    for (int i = 0; i < MAXL; ++i) {
+      const int c = base + tid + NW * 64 * i;
+      if (c < total) {
+        const int r = c / cpr, col = c - r * cpr;
+        *reinterpret_cast<uint4*>(cs + r * CS + col * 16) = cv[i];
+      }
+    }
+  };
+  load_batch(0);
   float sc[kMaxG];
 #pragma unroll
-  for (int u = 0; u < kMaxG; ++u) {
-    if (gb + u < ge) {
-      cw[u] = *reinterpret_cast<const uint4*>(crow + static_cast<size_t>(gb + u) * 32);
-      sc[u] = __half2float(srow[gb + u]);
-    }
-  }
+  for (int u = 0; u < kMaxG; ++u)
+    if (gb + u < ge) sc[u] = __half2float(srow[gb + u]);
 
   // Stage q into plane order and compute exact group sums.
   const int units = M * G * 2;
@@ -87,10 +209,16 @@ __global__ __launch_bounds__(NW * 64) void gemv_t2_kernel(
     sum += __shfl_xor(sum, 1);
     if (hh == 0) ts[m * G + g] = sum;
   }
+  store_batch(0);
+  for (int base = NW * 64 * MAXL; base < total; base += NW * 64 * MAXL) {
+    load_batch(base);
+    store_batch(base);
+  }
   __syncthreads();
 
   const int mA = min(n, M - 1);
   const uint8_t* qa = qs + static_cast<size_t>(mA) * K + h * 16;
+  const uint8_t* cb = cs + n * CS + h * 16;
   float acc[FOLD];
 #pragma unroll
   for (int r = 0; r < FOLD; ++r) acc[r] = 0.0f;
@@ -98,22 +226,19 @@ __global__ __launch_bounds__(NW * 64) void gemv_t2_kernel(
   for (int g0 = gb; g0 < ge; g0 += kMaxG) {
     if (g0 != gb) {
 #pragma unroll
-      for (int u = 0; u < kMaxG; ++u) {
-        if (g0 + u < ge) {
-          cw[u] = *reinterpret_cast<const uint4*>(crow + static_cast<size_t>(g0 + u) * 32);
-          sc[u] = __half2float(srow[g0 + u]);
-        }
-      }
+      for (int u = 0; u < kMaxG; ++u)
+        if (g0 + u < ge) sc[u] = __half2float(srow[g0 + u]);
     }
 #pragma unroll
     for (int u = 0; u < kMaxG; ++u) {
       const int g = g0 + u;
       if (g < ge) {
+        const uint4 cw = *reinterpret_cast<const uint4*>(cb + g * 32);
         v16i d = {};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const v4i b = {static_cast<int>(code_plane(cw[u].x, t)), static_cast<int>(code_plane(cw[u].y, t)),
-                         static_cast<int>(code_plane(cw[u].z, t)), static_cast<int>(code_plane(cw[u].w, t))};
+          const v4i b = {static_cast<int>(code_plane(cw.x, t)), static_cast<int>(code_plane(cw.y, t)),
+                         static_cast<int>(code_plane(cw.z, t)), static_cast<int>(code_plane(cw.w, t))};
           const v4i a = *reinterpret_cast<const v4i*>(qa + g * 128 + 32 * t);
           d = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, d, 0, 0, 0);
         }
@@ -159,7 +284,6 @@ __global__ __launch_bounds__(NW * 64) void gemv_t2_kernel(
 }
 
 // ---------------------------------------------------------------- 4-bit GEMV
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 // Eight codes of one packed dword -> the B operand in the order
 // [c0, c4, c1, c5, c2, c6, c3, c7] minus the zero point, exactly, as fp16.
@@ -300,18 +424,164 @@ __global__ __launch_bounds__(NW * 64) void gemv_w4_kernel(
   }
 }
 
+// ---------------------------------------------------------------- 4-bit, M = 1
+// K a multiple of 1024. Each wave streams R whole rows, one 512-byte load
+// instruction per 1024 columns (lane l holds the 16 codes of columns
+// 16l..16l+15 of each 1024-column chunk, all inside one 128-group). The lane's
+// 16 activations sit in registers; fp16: the codes become the exact fp16
+// values code - zero (magic 1024 trick) and v_dot2_f32_f16 accumulates;
+// bf16: codes and activations go through exact fp32 values and the zero point
+// is applied as zero * sum(x). The group scale multiplies the fp32 partial.
+template <int R, int CH, bool BF, bool ZP, typename TOut>
+__global__ __launch_bounds__(256) void gemv_w4_row_kernel(
+    const uint8_t* __restrict__ codes, const uint16_t* __restrict__ wscale,
+    const uint8_t* __restrict__ zeros, const uint16_t* __restrict__ x, int N, int K,
+    TOut* __restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int row0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * R;
+  if (row0 >= N) return;                        // whole wave; this kernel has no barriers
+  const int KB = K >> 1, G = K >> 7, ZB = (G + 1) >> 1;
+  uint2 cw[R][CH];
+  float sv[R][CH];
+  int zv[R][CH];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const size_t row = static_cast<size_t>(min(row0 + r, N - 1));
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      cw[r][c] = *reinterpret_cast<const uint2*>(codes + row * KB + c * 512 + lane * 8);
+      const int g = 8 * c + (lane >> 3);
+      const uint16_t sb = wscale[row * G + g];
+      sv[r][c] = BF ? bf16_to_f32(sb) : __half2float(__builtin_bit_cast(__half, sb));
+      zv[r][c] = ZP ? ((zeros[row * ZB + (g >> 1)] >> (4 * (g & 1))) & 15) : 8;
+    }
+  }
+  // Activations of this lane: x[1024c + 16 lane + e], e = 0..15.
+  uint4 xv[CH][2];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const uint4* src = reinterpret_cast<const uint4*>(x + c * 1024 + lane * 16);
+    xv[c][0] = src[0];
+    xv[c][1] = src[1];
+  }
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+  if (!BF) {
+    // x pairs in the order the code pairs come out: (x_s, x_{s+4}) of each 8.
+    h2 xp[CH][8];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const uint4 v = xv[c][d];
+        xp[c][4 * d + 0] = __builtin_bit_cast(h2, perm_b32(v.z, v.x, 0x05040100u));
+        xp[c][4 * d + 1] = __builtin_bit_cast(h2, perm_b32(v.z, v.x, 0x07060302u));
+        xp[c][4 * d + 2] = __builtin_bit_cast(h2, perm_b32(v.w, v.y, 0x05040100u));
+        xp[c][4 * d + 3] = __builtin_bit_cast(h2, perm_b32(v.w, v.y, 0x07060302u));
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const uint32_t mz = 0xE400u | static_cast<uint32_t>(zv[r][c]);   // fp16 -(1024 + z)
+        const h2 nz = __builtin_bit_cast(h2, mz | (mz << 16));
+        const uint32_t wv[2] = {cw[r][c].x, cw[r][c].y};
+        float p = 0.0f;
+#pragma unroll
+        for (int d = 0; d < 2; ++d)
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const h2 cz = __builtin_bit_cast(h2, ((wv[d] >> (4 * s)) & 0x000F000Fu) | 0x64006400u) + nz;
+            p = __builtin_amdgcn_fdot2(cz, xp[c][4 * d + s], p, false);
+          }
+        acc[r] = fmaf(sv[r][c], p, acc[r]);
+      }
+    }
+  } else {
+    float xf[CH][16];
+    float xsum[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const uint32_t xw[8] = {xv[c][0].x, xv[c][0].y, xv[c][0].z, xv[c][0].w,
+                              xv[c][1].x, xv[c][1].y, xv[c][1].z, xv[c][1].w};
+      xsum[c] = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        xf[c][2 * e] = __uint_as_float(xw[e] << 16);
+        xf[c][2 * e + 1] = __uint_as_float(xw[e] & 0xFFFF0000u);
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) xsum[c] += xf[c][e];
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const uint32_t wv[2] = {cw[r][c].x, cw[r][c].y};
+        float p = 0.0f;
+#pragma unroll
+        for (int d = 0; d < 2; ++d)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            p = fmaf(static_cast<float>((wv[d] >> (4 * e)) & 15u), xf[c][8 * d + e], p);
+        p = fmaf(-static_cast<float>(zv[r][c]), xsum[c], p);
+        acc[r] = fmaf(sv[r][c], p, acc[r]);
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float v = wave_sum(acc[r]);
+    if (lane == r && row0 + r < N) store_out(y + row0 + r, v);
+  }
+}
+
 int fold_for(int64_t m) { return m <= 1 ? 1 : (m <= 8 ? 4 : (m <= 16 ? 8 : 16)); }
 int waves_for(int64_t groups) { return groups >= 16 ? 8 : 4; }
+
+constexpr int kRowR = 4;   // rows per wave in the M = 1 kernels
+
+bool t2_row_ok(int64_t m, int64_t k) { return m == 1 && k % 4096 == 0 && k / 4096 <= 4; }
+bool w4_row_ok(int64_t m, int64_t k) { return m == 1 && k % 1024 == 0 && k / 1024 <= 8; }
+
+size_t t2_lds(int64_t m, int64_t k) {
+  const size_t stage = static_cast<size_t>(kRows) * (k / 4 + 16) + static_cast<size_t>(m) * k + 4ull * m * (k / 128);
+  const size_t red = 8ull * 16 * 64 * 4;
+  return stage > red ? stage : red;
+}
+
+unsigned row_blocks(int n) { return static_cast<unsigned>(((n + kRowR - 1) / kRowR + 3) / 4); }
+
+template <int CH, typename TOut, bool PARTIALS>
+void t2_row_go(const bpw_weights& w, const int8_t* q, const float* xs, TOut* y, int32_t* pout,
+               int pn0, int pn1, hipStream_t s) {
+  const int n = static_cast<int>(w.n), k = static_cast<int>(w.k);
+  gemv_t2_row_kernel<kRowR, CH, TOut, PARTIALS><<<row_blocks(n), 256, 0, s>>>(
+      static_cast<const uint8_t*>(w.codes), static_cast<const __half*>(w.scales), q, xs, n, k, y,
+      pout, pn0, pn1);
+}
+
+template <typename TOut, bool PARTIALS>
+hipError_t t2_row(const bpw_weights& w, const int8_t* q, const float* xs, TOut* y, int32_t* pout,
+                  int pn0, int pn1, hipStream_t s) {
+  switch (w.k / 4096) {
+    case 1: t2_row_go<1, TOut, PARTIALS>(w, q, xs, y, pout, pn0, pn1, s); break;
+    case 2: t2_row_go<2, TOut, PARTIALS>(w, q, xs, y, pout, pn0, pn1, s); break;
+    case 3: t2_row_go<3, TOut, PARTIALS>(w, q, xs, y, pout, pn0, pn1, s); break;
+    default: t2_row_go<4, TOut, PARTIALS>(w, q, xs, y, pout, pn0, pn1, s); break;
+  }
+  return hipGetLastError();
+}
 
 template <int NW, int FOLD, typename TOut>
 hipError_t t2_go(const bpw_weights& w, const int8_t* q, const float* xs, int m, TOut* y,
                  hipStream_t s) {
-  const int n = static_cast<int>(w.n), k = static_cast<int>(w.k), g = k / 128;
-  const size_t stage = static_cast<size_t>(m) * k + 4ull * m * g;
-  const size_t red = static_cast<size_t>(NW) * FOLD * 64 * 4;
-  const size_t lds = stage > red ? stage : red;
+  const int n = static_cast<int>(w.n), k = static_cast<int>(w.k);
   dim3 grid((n + kRows - 1) / kRows), block(NW * 64);
-  gemv_t2_kernel<NW, FOLD, TOut, false><<<grid, block, lds, s>>>(
+  allow_lds(gemv_t2_kernel<NW, FOLD, TOut, false>, t2_lds(m, k));
+  gemv_t2_kernel<NW, FOLD, TOut, false><<<grid, block, t2_lds(m, k), s>>>(
       static_cast<const uint8_t*>(w.codes), static_cast<const __half*>(w.scales), q, xs, m, n, k,
       y, nullptr, 0, 0, 0, 0, 0);
   return hipGetLastError();
@@ -320,6 +590,7 @@ hipError_t t2_go(const bpw_weights& w, const int8_t* q, const float* xs, int m, 
 template <typename TOut>
 hipError_t t2_dispatch(const bpw_weights& w, const int8_t* q, const float* xs, int m, TOut* y,
                        hipStream_t s) {
+  if (t2_row_ok(m, w.k)) return t2_row<TOut, false>(w, q, xs, y, nullptr, 0, 0, s);
   const int nw = waves_for(w.k / 128);
   const int fold = fold_for(m);
 #define BPW_T2(NW_, F_) \
@@ -337,14 +608,36 @@ hipError_t w4_go(const bpw_weights& w, const uint16_t* x, int m, TOut* y, hipStr
   const size_t red = static_cast<size_t>(NW) * FOLD * 64 * 4;
   const size_t lds = stage > red ? stage : red;
   dim3 grid((n + kRows - 1) / kRows), block(NW * 64);
+  allow_lds(gemv_w4_kernel<NW, FOLD, BF, ZP, TOut>, lds);
   gemv_w4_kernel<NW, FOLD, BF, ZP, TOut><<<grid, block, lds, s>>>(
       static_cast<const uint8_t*>(w.codes), static_cast<const uint16_t*>(w.scales),
       static_cast<const uint8_t*>(w.zeros), x, m, n, k, y);
   return hipGetLastError();
 }
 
+template <int CH, bool BF, bool ZP, typename TOut>
+void w4_row_go(const bpw_weights& w, const uint16_t* x, TOut* y, hipStream_t s) {
+  const int n = static_cast<int>(w.n), k = static_cast<int>(w.k);
+  gemv_w4_row_kernel<kRowR, CH, BF, ZP, TOut><<<row_blocks(n), 256, 0, s>>>(
+      static_cast<const uint8_t*>(w.codes), static_cast<const uint16_t*>(w.scales),
+      static_cast<const uint8_t*>(w.zeros), x, n, k, y);
+}
+
 template <bool BF, bool ZP, typename TOut>
 hipError_t w4_dispatch_f(const bpw_weights& w, const uint16_t* x, int m, TOut* y, hipStream_t s) {
+  if (w4_row_ok(m, w.k)) {
+    switch (w.k / 1024) {
+      case 1: w4_row_go<1, BF, ZP>(w, x, y, s); break;
+      case 2: w4_row_go<2, BF, ZP>(w, x, y, s); break;
+      case 3: w4_row_go<3, BF, ZP>(w, x, y, s); break;
+      case 4: w4_row_go<4, BF, ZP>(w, x, y, s); break;
+      case 5: w4_row_go<5, BF, ZP>(w, x, y, s); break;
+      case 6: w4_row_go<6, BF, ZP>(w, x, y, s); break;
+      case 7: w4_row_go<7, BF, ZP>(w, x, y, s); break;
+      default: w4_row_go<8, BF, ZP>(w, x, y, s); break;
+    }
+    return hipGetLastError();
+  }
   const int nw = waves_for(w.k / 128);
   const int fold = fold_for(m);
 #define BPW_W4(NW_, F_) \
@@ -366,11 +659,12 @@ hipError_t w4_dispatch(const bpw_weights& w, const uint16_t* x, bool bf, int m, 
 }  // namespace
 
 bool gemv_t2_fits(int64_t m, int64_t k) {
-  return m >= 1 && m <= 32 && static_cast<size_t>(m) * k + 4ull * m * (k / 128) <= kLdsBudget;
+  if (m < 1 || m > 32) return false;
+  return t2_row_ok(m, k) || t2_lds(m, k) <= kLdsBudget;
 }
 
 bool gemv_w4_fits(int64_t m, int64_t k) {
-  return m >= 1 && m <= 32 && static_cast<size_t>(m) * k * 2 <= kLdsBudget;
+  return m >= 1 && m <= 32 && (w4_row_ok(m, k) || static_cast<size_t>(m) * k * 2 <= kLdsBudget);
 }
 
 hipError_t launch_gemv_t2(const bpw_weights& w, const int8_t* q, const float* x_scale, int64_t m,
@@ -386,19 +680,22 @@ hipError_t launch_gemv_t2(const bpw_weights& w, const int8_t* q, const float* x_
 hipError_t launch_gemv_t2_partials(const bpw_weights& w, const int8_t* q, int64_t m, int64_t m0,
                                    int64_t m1, int64_t n0, int64_t n1, int32_t* out,
                                    hipStream_t s) {
-  const int n = static_cast<int>(w.n), k = static_cast<int>(w.k), g = k / 128;
+  const int n = static_cast<int>(w.n), k = static_cast<int>(w.k);
   const int mi = static_cast<int>(m);
-  const size_t lds = static_cast<size_t>(mi) * k + 4ull * mi * g;
+  if (t2_row_ok(m, k))   // the product for M = 1 runs the row kernel: verify that core
+    return t2_row<float, true>(w, q, nullptr, nullptr, out, static_cast<int>(n0), static_cast<int>(n1), s);
+  if (t2_lds(m, k) > kLdsBudget) return hipErrorInvalidValue;
   const int t0 = static_cast<int>(n0 / kRows), t1 = static_cast<int>((n1 - 1) / kRows);
-  dim3 grid(t1 - t0 + 1), block(64 * 8);
-  if (waves_for(g) == 8) {
-    gemv_t2_kernel<8, 16, float, true><<<grid, block, lds, s>>>(
+  dim3 grid(t1 - t0 + 1);
+  if (waves_for(k / 128) == 8) {
+    allow_lds(gemv_t2_kernel<8, 16, float, true>, t2_lds(m, k));
+    gemv_t2_kernel<8, 16, float, true><<<grid, 512, t2_lds(m, k), s>>>(
         static_cast<const uint8_t*>(w.codes), static_cast<const __half*>(w.scales), q, nullptr,
         mi, n, k, nullptr, out, static_cast<int>(m0), static_cast<int>(m1), static_cast<int>(n0),
         static_cast<int>(n1), t0);
   } else {
-    block = dim3(64 * 4);
-    gemv_t2_kernel<4, 16, float, true><<<grid, block, lds, s>>>(
+    allow_lds(gemv_t2_kernel<4, 16, float, true>, t2_lds(m, k));
+    gemv_t2_kernel<4, 16, float, true><<<grid, 256, t2_lds(m, k), s>>>(
         static_cast<const uint8_t*>(w.codes), static_cast<const __half*>(w.scales), q, nullptr,
         mi, n, k, nullptr, out, static_cast<int>(m0), static_cast<int>(m1), static_cast<int>(n0),
         static_cast<int>(n1), t0);

@@ -18,17 +18,31 @@ __device__ __forceinline__ float ld(const uint16_t* p) { return bf16_to_f32(*p);
 
 constexpr int kQThreads = 256;
 
-template <typename T>
+// One workgroup per row. ONEPASS (K <= 32 * kQThreads): every value is loaded
+// once into registers, the row max is reduced, and the same registers are
+// quantised; otherwise the row is read twice.
+template <typename T, bool ONEPASS>
 __global__ __launch_bounds__(kQThreads) void quantize_rows_kernel(const T* __restrict__ x,
                                                                   int64_t k,
                                                                   int8_t* __restrict__ q,
                                                                   float* __restrict__ x_scale) {
+  constexpr int V = 32;
   __shared__ float wmax[kQThreads / 64];
   const int64_t row = blockIdx.x;
   const T* xr = x + row * k;
   int8_t* qr = q + row * k;
+  float v[ONEPASS ? V : 1];
   float amax = 0.0f;
-  for (int64_t i = threadIdx.x; i < k; i += kQThreads) amax = fmaxf(amax, fabsf(ld(xr + i)));
+  if (ONEPASS) {
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const int64_t i = threadIdx.x + static_cast<int64_t>(j) * kQThreads;
+      v[j] = i < k ? ld(xr + i) : 0.0f;
+      amax = fmaxf(amax, fabsf(v[j]));
+    }
+  } else {
+    for (int64_t i = threadIdx.x; i < k; i += kQThreads) amax = fmaxf(amax, fabsf(ld(xr + i)));
+  }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
@@ -38,10 +52,18 @@ __global__ __launch_bounds__(kQThreads) void quantize_rows_kernel(const T* __res
   for (int w = 1; w < kQThreads / 64; ++w) amax = fmaxf(amax, wmax[w]);
   const float scale = amax * (1.0f / 127.0f);      // fp32 reciprocal constant, one rounding
   const float div = scale > 0.0f ? scale : 1.0f;
-  for (int64_t i = threadIdx.x; i < k; i += kQThreads) {
-    float r = rintf(ld(xr + i) / div);               // IEEE division, ties to even
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    qr[i] = static_cast<int8_t>(r);
+  if (ONEPASS) {
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const int64_t i = threadIdx.x + static_cast<int64_t>(j) * kQThreads;
+      if (i < k) qr[i] = static_cast<int8_t>(fminf(fmaxf(rintf(v[j] / div), -127.0f), 127.0f));
+    }
+  } else {
+    for (int64_t i = threadIdx.x; i < k; i += kQThreads) {
+      float r = rintf(ld(xr + i) / div);             // IEEE division, ties to even
+      r = fminf(fmaxf(r, -127.0f), 127.0f);
+      qr[i] = static_cast<int8_t>(r);
+    }
   }
   if (threadIdx.x == 0) x_scale[row] = scale;
 }
@@ -86,19 +108,21 @@ int grid_for(int64_t items, int per_block) {
 
 }  // namespace
 
+template <typename T>
+void quantize_go(const void* x, int64_t m, int64_t k, int8_t* q, float* x_scale, hipStream_t s) {
+  dim3 grid(static_cast<unsigned>(m)), block(kQThreads);
+  if (k <= 32 * kQThreads)
+    quantize_rows_kernel<T, true><<<grid, block, 0, s>>>(static_cast<const T*>(x), k, q, x_scale);
+  else
+    quantize_rows_kernel<T, false><<<grid, block, 0, s>>>(static_cast<const T*>(x), k, q, x_scale);
+}
+
 hipError_t launch_quantize_rows(const void* x, int x_dtype, int64_t m, int64_t k, int8_t* q,
                                 float* x_scale, hipStream_t s) {
-  dim3 grid(static_cast<unsigned>(m)), block(kQThreads);
   switch (x_dtype) {
-    case BPW_F32:
-      quantize_rows_kernel<float><<<grid, block, 0, s>>>(static_cast<const float*>(x), k, q, x_scale);
-      break;
-    case BPW_F16:
-      quantize_rows_kernel<__half><<<grid, block, 0, s>>>(static_cast<const __half*>(x), k, q, x_scale);
-      break;
-    default:
-      quantize_rows_kernel<uint16_t><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(x), k, q, x_scale);
-      break;
+    case BPW_F32: quantize_go<float>(x, m, k, q, x_scale, s); break;
+    case BPW_F16: quantize_go<__half>(x, m, k, q, x_scale, s); break;
+    default: quantize_go<uint16_t>(x, m, k, q, x_scale, s); break;
   }
   return hipGetLastError();
 }

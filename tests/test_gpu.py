@@ -102,7 +102,8 @@ def test_gemm_ternary_parity(m, k, n):
 
 @pytest.mark.parametrize("path", [bpw.PATH_GEMV, bpw.PATH_GEMM])
 @pytest.mark.parametrize("m,k,n,win", [(3, 256, 70, (0, 3, 0, 70)), (32, 512, 200, (5, 29, 33, 170)),
-                                       (1, 128, 40, (0, 1, 7, 9))])
+                                       (1, 128, 40, (0, 1, 7, 9)), (1, 4096, 77, (0, 1, 3, 70)),
+                                       (1, 8192, 9, (0, 1, 0, 9))])
 def test_partials_bit_exact(path, m, k, n, win):
     # stress inputs: full int8 range and every 2-bit code including 3
     rng = np.random.default_rng(m + k + n)
@@ -164,7 +165,8 @@ def w4_reference(w: synth.Workload, rounded: bool):
 @pytest.mark.parametrize("fmt,x_dtype,act_order", [("int4_zp", "f16", True), ("int4_zp", "f16", False),
                                                    ("int4_sym", "bf16", False), ("int4_sym", "f16", False),
                                                    ("int4_zp", "bf16", True)])
-@pytest.mark.parametrize("m,k,n", [(1, 640, 333), (3, 128, 64), (8, 5120, 200), (16, 1024, 97), (32, 256, 130)])
+@pytest.mark.parametrize("m,k,n", [(1, 640, 333), (1, 2048, 301), (1, 8192, 66), (3, 128, 64), (8, 5120, 200),
+                                   (16, 1024, 97), (32, 256, 130)])
 def test_gemv_w4_parity(fmt, x_dtype, act_order, m, k, n):
     w = w4_case(fmt, m, k, n, 300 + m + k + n, act_order, x_dtype)
     pw = prepare(w)
