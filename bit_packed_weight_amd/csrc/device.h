@@ -12,7 +12,8 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));   // register-friendly (no union)
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
 // Element-type tags used to instantiate kernels.
 struct F32 { typedef float T; };
@@ -54,7 +55,7 @@ __device__ __forceinline__ void transpose4x4(uint32_t i0, uint32_t i1, uint32_t 
 
 // 64 activation bytes of one half of a 128-group (natural order, as 16 dwords)
 // -> plane order: output chunk t (16 bytes) holds elements 4u + t, u = 0..15.
-__device__ __forceinline__ void to_plane_order(const uint4 in[4], uint4 out[4]) {
+__device__ __forceinline__ void to_plane_order(const v4u in[4], v4u out[4]) {
   uint32_t d[16] = {in[0].x, in[0].y, in[0].z, in[0].w, in[1].x, in[1].y, in[1].z, in[1].w,
                     in[2].x, in[2].y, in[2].z, in[2].w, in[3].x, in[3].y, in[3].z, in[3].w};
   uint32_t o[4][4];
@@ -63,7 +64,7 @@ __device__ __forceinline__ void to_plane_order(const uint4 in[4], uint4 out[4]) 
     transpose4x4(d[4 * v], d[4 * v + 1], d[4 * v + 2], d[4 * v + 3], o[0][v], o[1][v], o[2][v],
                  o[3][v]);
 #pragma unroll
-  for (int t = 0; t < 4; ++t) out[t] = make_uint4(o[t][0], o[t][1], o[t][2], o[t][3]);
+  for (int t = 0; t < 4; ++t) out[t] = v4u{o[t][0], o[t][1], o[t][2], o[t][3]};
 }
 
 // Sum of the four signed bytes of each dword, accumulated into acc.

@@ -66,21 +66,21 @@ __global__ __launch_bounds__(NT, 1) void gemm_t2_kernel(
   const __half* s_src = wscale + static_cast<size_t>(min(n0 + tid, N - 1)) * G;
   const int s_dst = A_BYTES + B_BYTES + tid * 4;
 
-  uint4 ra[4], rb[2];
+  v4u ra[4], rb[2];
   float rs;
-  auto gload = [&](int g) {
+  auto gload = [&](int g) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + g * 128);
+    for (int i = 0; i < 4; ++i) ra[i] = *reinterpret_cast<const v4u*>(a_src[i] + g * 128);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) rb[i] = *reinterpret_cast<const uint4*>(b_src[i] + g * 32);
+    for (int i = 0; i < 2; ++i) rb[i] = *reinterpret_cast<const v4u*>(b_src[i] + g * 32);
     rs = __half2float(s_src[g]);
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int buf) __attribute__((always_inline)) {
     uint8_t* base = smem + buf * STAGE_BYTES;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(base + a_dst[i]) = ra[i];
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<v4u*>(base + a_dst[i]) = ra[i];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(base + b_dst[i]) = rb[i];
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<v4u*>(base + b_dst[i]) = rb[i];
     *reinterpret_cast<float*>(base + s_dst) = rs;
   };
 
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_t2_kernel(
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int nr = 64 * wave + 32 * j + n;
-      const uint4 pk = *reinterpret_cast<const uint4*>(base + A_BYTES + nr * B_STRIDE + 16 * h);
+      const v4u pk = *reinterpret_cast<const v4u*>(base + A_BYTES + nr * B_STRIDE + 16 * h);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
         bop[j][t] = v4i{static_cast<int>(code_plane_signed(pk.x, t)),

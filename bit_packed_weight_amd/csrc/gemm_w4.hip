@@ -2,40 +2,62 @@
 //
 // "mate: Marlin-class W4A16 GEMM for mp_31 (SQMMA int4 x fp16) - #6": the
 // prefill kernel unpacks int4 to the activation type before the matrix
-// instruction. Each workgroup stage dequantises its weight tile once into LDS as
-// round-to-nearest-even of (code - zero) * scale in the activation dtype (the
-// product is exact in fp32 before that single rounding), then all waves feed
-// fp16/bf16 MFMA (32x32x16) with fp32 accumulation.
+// instruction. Each weight is dequantised once per workgroup to
+// round-to-nearest-even of (code - zero) * scale in the activation dtype (exact
+// in fp32 before that single rounding) and fed to fp16/bf16 MFMA (32x32x16)
+// with fp32 accumulation.
 //
-// Workgroup tile 128 (tokens) x 256 (weight rows), 4 waves each 128 x 64; K is
-// walked 32 columns per stage through double-buffered LDS.
+// Workgroup tile 256 (tokens) x 256 (weight rows), 4 waves; wave w owns weight
+// rows [64w, 64w + 64) of the tile and all 256 tokens (8 x 2 MFMA tiles, the
+// accumulators live in AGPRs). The activation tile goes through double-buffered
+// LDS (64 columns per stage); each wave dequantises its own weight rows straight
+// into B-operand registers, so no weight byte touches LDS and no weight is
+// dequantised twice. Within a 64-column stage, lane half h of MFMA step s holds
+// columns 32h + 8s .. 32h + 8s + 7 (any column order works as long as A and B
+// agree); then one 16-byte code load per lane and weight tile feeds all four
+// steps.
 #include "device.h"
 #include "launch.h"
 
 namespace bpw {
 namespace {
 
-constexpr int BM = 128, BN = 256, BK = 32, NT = 256;
-constexpr int ROW_STRIDE = BK * 2 + 16;         // 80 bytes: conflict-free 16-byte reads
-constexpr int A_BYTES = BM * ROW_STRIDE;
-constexpr int B_BYTES = BN * ROW_STRIDE;
-constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+constexpr int BM = 256, BN = 256, BK = 64, NT = 256;
+constexpr int A_STRIDE = BK * 2 + 16;           // 144 bytes: conflict-free 16-byte LDS reads
+constexpr int A_BYTES = BM * A_STRIDE;          // one stage
+constexpr int LDS_BYTES = 2 * A_BYTES;
 
 __device__ __forceinline__ int d_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
-__device__ __forceinline__ uint32_t pack2(float a, float b, bool bf) {
-  if (bf) {
-    const __bf16 x = static_cast<__bf16>(a), y = static_cast<__bf16>(b);
-    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, x)) |
-           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, y)) << 16);
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+// Eight codes of one packed dword (byte b: code 2b in the low nibble, 2b+1 in
+// the high nibble) -> eight 16-bit weights in that order, each the
+// round-to-nearest-even of (code - zero) * scale. A byte select builds the fp32
+// value 128 + code (bits 0x43 0c 00 00); one fma with nzs = -(128 + zero) * scale
+// gives (code - zero) * scale exactly (all products fit fp32), then a packed
+// convert rounds two values at once.
+template <bool BF>
+__device__ __forceinline__ v4u dequant8(uint32_t w, float s, float nzs) {
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  uint32_t o[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const uint32_t sel = 0x07000C0Cu | (static_cast<uint32_t>(b) << 16);
+    const float vl = fmaf(__uint_as_float(perm_b32(0x43000000u, lo, sel)), s, nzs);
+    const float vh = fmaf(__uint_as_float(perm_b32(0x43000000u, hi, sel)), s, nzs);
+    if (BF)
+      o[b] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{vl, vh}, v2bf));
+    else
+      o[b] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{vl, vh}, v2h));
   }
-  const __half x = __float2half_rn(a), y = __float2half_rn(b);
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, x)) |
-         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, y)) << 16);
+  return v4u{o[0], o[1], o[2], o[3]};
 }
 
 template <bool BF, bool ZP, typename TOut>
-__global__ __launch_bounds__(NT, 2) void gemm_w4_kernel(
+__global__ __launch_bounds__(NT, 1) void gemm_w4_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
     const uint16_t* __restrict__ wscale, const uint8_t* __restrict__ zeros, int M, int N, int K,
     TOut* __restrict__ y, int mtiles, int ntiles) {
@@ -48,100 +70,132 @@ __global__ __launch_bounds__(NT, 2) void gemm_w4_kernel(
   const int tile = xcd_swizzle(blockIdx.x, mtiles * ntiles);
   const int mt = tile % mtiles, nt = tile / mtiles;
   const int m0 = mt * BM, n0 = nt * BN;
-
-  // A: 128 rows x 64 bytes per stage = 512 chunks, two per thread.
-  const uint16_t* a_src[2];
-  int a_dst[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = tid + NT * i;
-    const int r = c >> 2, col = c & 3;
-    a_src[i] = x + static_cast<size_t>(min(m0 + r, M - 1)) * K + col * 8;
-    a_dst[i] = r * ROW_STRIDE + col * 16;
-  }
-  // B: one weight row per thread, 16 packed bytes (32 codes) per stage.
-  const int brow = min(n0 + tid, N - 1);
-  const uint8_t* b_src = codes + static_cast<size_t>(brow) * KB;
-  const uint16_t* s_src = wscale + static_cast<size_t>(brow) * G;
-  const uint8_t* z_src = ZP ? zeros + static_cast<size_t>(brow) * ZB : nullptr;
-  const int b_dst = A_BYTES + tid * ROW_STRIDE;
-
-  uint4 ra[2], rb;
-  float rsc, rzs;
-  auto gload = [&](int st) {
-    const int k0 = st * BK;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + k0);
-    rb = *reinterpret_cast<const uint4*>(b_src + k0 / 2);
-    const int g = k0 >> 7;
-    const uint16_t sb = s_src[g];
-    rsc = BF ? bf16_to_f32(sb) : __half2float(__builtin_bit_cast(__half, sb));
-    const int z = ZP ? ((z_src[g >> 1] >> (4 * (g & 1))) & 15) : 8;
-    rzs = static_cast<float>(z) * rsc;     // exact: small integer times a 16-bit float
-  };
-  auto lstore = [&](int buf) {
-    uint8_t* base = smem + buf * STAGE_BYTES;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(base + a_dst[i]) = ra[i];
-    // Dequantise 32 codes: (c - z) * s = fma(c, s, -z*s), exact, then one rounding.
-    const uint32_t wv[4] = {rb.x, rb.y, rb.z, rb.w};
-    uint32_t o[16];
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const uint32_t byte = (wv[d] >> (8 * b)) & 0xFFu;
-        const float lo = fmaf(static_cast<float>(byte & 15u), rsc, -rzs);
-        const float hi = fmaf(static_cast<float>(byte >> 4), rsc, -rzs);
-        o[4 * d + b] = pack2(lo, hi, BF);
-      }
-    }
-    uint4* dst = reinterpret_cast<uint4*>(base + b_dst);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
-  };
-
   const int n = lane & 31, h = lane >> 5;
-  v16f acc[4][2];
+
+  // A: 256 rows x 128 bytes per stage = 2048 chunks, eight per thread.
+  const uint16_t* a_src[8];
+  int a_dst[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i) {
+    const int c = tid + NT * i;
+    const int r = c >> 3, col = c & 7;
+    a_src[i] = x + static_cast<size_t>(min(m0 + r, M - 1)) * K + col * 8;
+    a_dst[i] = r * A_STRIDE + col * 16;
+  }
+  // B: this lane's two weight rows (one per 32-row tile of the wave).
+  const uint8_t* b_src[2];
+  const uint16_t* s_src[2];
+  const uint8_t* z_src[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const size_t row = static_cast<size_t>(min(n0 + 64 * wave + 32 * j + n, N - 1));
+    b_src[j] = codes + row * KB + 16 * h;
+    s_src[j] = wscale + row * G;
+    z_src[j] = ZP ? zeros + row * ZB : nullptr;
+  }
+
+  v4u ra[8];
+  auto a_load = [&](int st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ra[i] = *reinterpret_cast<const v4u*>(a_src[i] + st * BK);
+  };
+  auto a_store = [&](int buf) __attribute__((always_inline)) {
+    uint8_t* base = smem + buf * A_BYTES;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<v4u*>(base + a_dst[i]) = ra[i];
+  };
+  // Raw weights of one stage: two 16-byte code loads, their scales and the
+  // folded zero term, double-buffered so a load never waits for a dequant.
+  struct BRaw {
+    v4u c[2];
+    float s[2], nz[2];
+  };
+  auto b_load = [&](BRaw& r, int st) __attribute__((always_inline)) {
+    const int g = (st * BK) >> 7;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      r.c[j] = *reinterpret_cast<const v4u*>(b_src[j] + st * (BK / 2));
+      const uint16_t sb = s_src[j][g];
+      r.s[j] = BF ? bf16_to_f32(sb) : __half2float(__builtin_bit_cast(__half, sb));
+      const int z = ZP ? ((z_src[j][g >> 1] >> (4 * (g & 1))) & 15) : 8;
+      r.nz[j] = -static_cast<float>(128 + z) * r.s[j];   // exact: 8-bit integer times a 16-bit float
+    }
+  };
+  auto b_dequant_step = [&](const BRaw& r, v4u (&bop)[2][4], int ks) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t w = ks == 0 ? r.c[j].x : ks == 1 ? r.c[j].y : ks == 2 ? r.c[j].z : r.c[j].w;
+      bop[j][ks] = dequant8<BF>(w, r.s[j], r.nz[j]);
+    }
+  };
+
+  v16f acc[8][2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  for (int st = 0; st < S; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < S) gload(st + 1);
-    const uint8_t* base = smem + buf * STAGE_BYTES;
+  // One stage (64 columns): global loads for later stages first; then four
+  // MFMA steps over the A tile in LDS buffer `buf` with weights `cur`, each
+  // interleaved with a quarter of the dequantisation of the next stage's
+  // weights (`raw` -> `nxt`); then the next A tile goes to the other buffer.
+  // Scheduling fences keep the loads at the start and the LDS stores at the
+  // end, so no wait for a fresh load lands among the MFMAs.
+  auto stage = [&](int st, int buf, v4u (&cur)[2][4], v4u (&nxt)[2][4], const BRaw& raw,
+                   BRaw& load_into) __attribute__((always_inline)) {
+    a_load(min(st + 1, S - 1));
+    b_load(load_into, min(st + 2, S - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    const uint8_t* base = smem + buf * A_BYTES + 64 * h;
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      uint4 bop[2];
+    for (int ks = 0; ks < 4; ++ks) {
+      v4u aop[8];
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bop[j] = *reinterpret_cast<const uint4*>(base + A_BYTES + (64 * wave + 32 * j + n) * ROW_STRIDE + 32 * ks + 16 * h);
+      for (int i = 0; i < 8; ++i) aop[i] = *reinterpret_cast<const v4u*>(base + (32 * i + n) * A_STRIDE + 16 * ks);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 aop = *reinterpret_cast<const uint4*>(base + (32 * i + n) * ROW_STRIDE + 32 * ks + 16 * h);
+      for (int i = 0; i < 8; ++i) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           if (BF)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, aop),
-                                                                __builtin_bit_cast(v8bf, bop[j]), acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, aop[i]),
+                                                                __builtin_bit_cast(v8bf, cur[j][ks]), acc[i][j], 0, 0, 0);
           else
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, aop),
-                                                               __builtin_bit_cast(v8h, bop[j]), acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, aop[i]),
+                                                               __builtin_bit_cast(v8h, cur[j][ks]), acc[i][j], 0, 0, 0);
         }
       }
+      b_dequant_step(raw, nxt, ks);
+      // 8 LDS reads, then 16 x (1 MFMA + 3 VALU).
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (st + 1 < S) lstore(buf ^ 1);
+    a_store(buf ^ 1);
+  };
+
+  v4u bop0[2][4], bop1[2][4];
+  BRaw raw0, raw1;
+  a_load(0);
+  b_load(raw0, 0);
+  a_store(0);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) b_dequant_step(raw0, bop0, ks);
+  b_load(raw0, min(1, S - 1));
+  __syncthreads();
+
+  for (int st = 0; st < S; st += 2) {     // S = K / 64 is even
+    stage(st, 0, bop0, bop1, raw0, raw1);       // dequant stage st+1 from raw0, load st+2 into raw1
+    __syncthreads();
+    stage(st + 1, 1, bop1, bop0, raw1, raw0);   // dequant stage st+2 from raw1, load st+3 into raw0
     __syncthreads();
   }
 
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 8; ++i) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int mm = m0 + 32 * i + d_row(r, h);
@@ -160,7 +214,8 @@ template <bool BF, bool ZP, typename TOut>
 hipError_t go(const bpw_weights& w, const uint16_t* x, int m, TOut* y, hipStream_t s) {
   const int n = static_cast<int>(w.n), k = static_cast<int>(w.k);
   const int mtiles = (m + BM - 1) / BM, ntiles = (n + BN - 1) / BN;
-  gemm_w4_kernel<BF, ZP, TOut><<<mtiles * ntiles, NT, 2 * STAGE_BYTES, s>>>(
+  allow_lds(gemm_w4_kernel<BF, ZP, TOut>, LDS_BYTES);
+  gemm_w4_kernel<BF, ZP, TOut><<<mtiles * ntiles, NT, LDS_BYTES, s>>>(
       x, static_cast<const uint8_t*>(w.codes), static_cast<const uint16_t*>(w.scales),
       static_cast<const uint8_t*>(w.zeros), m, n, k, y, mtiles, ntiles);
   return hipGetLastError();

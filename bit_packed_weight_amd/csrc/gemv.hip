@@ -61,23 +61,23 @@ __global__ __launch_bounds__(256) void gemv_t2_row_kernel(
   const int row0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * R;
   if (row0 >= N) return;                        // whole wave; this kernel has no barriers
   const int KB = K >> 2, G = K >> 7;
-  uint4 cw[R][CH];
+  v4u cw[R][CH];
   float sv[R][CH];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const size_t row = static_cast<size_t>(min(row0 + r, N - 1));
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      cw[r][c] = *reinterpret_cast<const uint4*>(codes + row * KB + c * 1024 + lane * 16);
+      cw[r][c] = *reinterpret_cast<const v4u*>(codes + row * KB + c * 1024 + lane * 16);
       sv[r][c] = __half2float(wscale[row * G + 32 * c + (lane >> 1)]);
     }
   }
-  uint4 qp[CH][4];
+  v4u qp[CH][4];
   int th[CH];
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
-    const uint4* src = reinterpret_cast<const uint4*>(q + c * 4096 + lane * 64);
-    uint4 in[4] = {src[0], src[1], src[2], src[3]};
+    const v4u* src = reinterpret_cast<const v4u*>(q + c * 4096 + lane * 64);
+    v4u in[4] = {src[0], src[1], src[2], src[3]};
     to_plane_order(in, qp[c]);
     int sum = 0;
 #pragma unroll
@@ -159,24 +159,24 @@ __global__ __launch_bounds__(NW * 64) void gemv_t2_kernel(
   // on consecutive chunks of a row. The first batch is issued before staging q.
   constexpr int MAXL = 8;
   const int cpr = KB >> 4, total = kRows * cpr;
-  uint4 cv[MAXL];
-  auto load_batch = [&](int base) {
+  v4u cv[MAXL];
+  auto load_batch = [&](int base) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < MAXL; ++i) {
       const int c = base + tid + NW * 64 * i;
       if (c < total) {
         const int r = c / cpr, col = c - r * cpr;
-        cv[i] = *reinterpret_cast<const uint4*>(codes + static_cast<size_t>(min(n0 + r, N - 1)) * KB + col * 16);
+        cv[i] = *reinterpret_cast<const v4u*>(codes + static_cast<size_t>(min(n0 + r, N - 1)) * KB + col * 16);
       }
     }
   };
-  auto store_batch = [&](int base) {
+  auto store_batch = [&](int base) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < MAXL; ++i) {
       const int c = base + tid + NW * 64 * i;
       if (c < total) {
         const int r = c / cpr, col = c - r * cpr;
-        *reinterpret_cast<uint4*>(cs + r * CS + col * 16) = cv[i];
+        *reinterpret_cast<v4u*>(cs + r * CS + col * 16) = cv[i];
       }
     }
   };
@@ -191,13 +191,13 @@ __global__ __launch_bounds__(NW * 64) void gemv_t2_kernel(
   for (int u = tid; u < units; u += NW * 64) {
     const int hh = u & 1, mg = u >> 1;
     const int m = mg / G, g = mg - m * G;
-    const uint4* src = reinterpret_cast<const uint4*>(q + static_cast<size_t>(m) * K + g * 128 + hh * 64);
-    uint4 in[4] = {src[0], src[1], src[2], src[3]};
-    uint4 o[4];
+    const v4u* src = reinterpret_cast<const v4u*>(q + static_cast<size_t>(m) * K + g * 128 + hh * 64);
+    v4u in[4] = {src[0], src[1], src[2], src[3]};
+    v4u o[4];
     to_plane_order(in, o);
     uint8_t* dst = qs + static_cast<size_t>(m) * K + g * 128 + hh * 16;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) *reinterpret_cast<uint4*>(dst + 32 * t) = o[t];
+    for (int t = 0; t < 4; ++t) *reinterpret_cast<v4u*>(dst + 32 * t) = o[t];
     int sum = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -233,7 +233,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_t2_kernel(
     for (int u = 0; u < kMaxG; ++u) {
       const int g = g0 + u;
       if (g < ge) {
-        const uint4 cw = *reinterpret_cast<const uint4*>(cb + g * 32);
+        const v4u cw = *reinterpret_cast<const v4u*>(cb + g * 32);
         v16i d = {};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -336,12 +336,12 @@ __global__ __launch_bounds__(NW * 64) void gemv_w4_kernel(
   const uint8_t* zrow = ZP ? zeros + static_cast<size_t>(row) * ZB : nullptr;
 
   constexpr int MG = kMaxG / 2;                // two 16-byte loads per group
-  uint4 cw[MG][2];
+  v4u cw[MG][2];
   float sc[MG];
   int zc[MG];
-  auto load_group = [&](int u, int g) {
-    cw[u][0] = *reinterpret_cast<const uint4*>(crow + static_cast<size_t>(g) * 64);
-    cw[u][1] = *reinterpret_cast<const uint4*>(crow + static_cast<size_t>(g) * 64 + 32);
+  auto load_group = [&](int u, int g) __attribute__((always_inline)) {
+    cw[u][0] = *reinterpret_cast<const v4u*>(crow + static_cast<size_t>(g) * 64);
+    cw[u][1] = *reinterpret_cast<const v4u*>(crow + static_cast<size_t>(g) * 64 + 32);
     const uint16_t sb = srow[g];
     sc[u] = BF ? bf16_to_f32(sb) : __half2float(__builtin_bit_cast(__half, sb));
     zc[u] = ZP ? ((zrow[g >> 1] >> (4 * (g & 1))) & 15) : 8;
@@ -353,13 +353,13 @@ __global__ __launch_bounds__(NW * 64) void gemv_w4_kernel(
   // Stage activations: each 8-element chunk stored as [0,4,1,5,2,6,3,7].
   const int chunks = M * (K >> 3);
   for (int c = tid; c < chunks; c += NW * 64) {
-    const uint4 v = reinterpret_cast<const uint4*>(x)[c];
-    uint4 o;
+    const v4u v = reinterpret_cast<const v4u*>(x)[c];
+    v4u o;
     o.x = perm_b32(v.z, v.x, 0x05040100u);
     o.y = perm_b32(v.z, v.x, 0x07060302u);
     o.z = perm_b32(v.w, v.y, 0x05040100u);
     o.w = perm_b32(v.w, v.y, 0x07060302u);
-    reinterpret_cast<uint4*>(xs)[c] = o;
+    reinterpret_cast<v4u*>(xs)[c] = o;
   }
   __syncthreads();
 
@@ -388,7 +388,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_w4_kernel(
           const uint32_t wv[4] = {cw[u][L].x, cw[u][L].y, cw[u][L].z, cw[u][L].w};
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
-            const uint4 araw = *reinterpret_cast<const uint4*>(xa + g * 128 + 64 * L + 8 * s);
+            const v4u araw = *reinterpret_cast<const v4u*>(xa + g * 128 + 64 * L + 8 * s);
             if (BF) {
               const v8bf a = __builtin_bit_cast(v8bf, araw);
               const v8bf b = dequant_w4_bf16(wv[s], zf);
@@ -441,7 +441,7 @@ __global__ __launch_bounds__(256) void gemv_w4_row_kernel(
   const int row0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * R;
   if (row0 >= N) return;                        // whole wave; this kernel has no barriers
   const int KB = K >> 1, G = K >> 7, ZB = (G + 1) >> 1;
-  uint2 cw[R][CH];
+  v2u cw[R][CH];
   float sv[R][CH];
   int zv[R][CH];
 #pragma unroll
@@ -449,7 +449,7 @@ __global__ __launch_bounds__(256) void gemv_w4_row_kernel(
     const size_t row = static_cast<size_t>(min(row0 + r, N - 1));
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      cw[r][c] = *reinterpret_cast<const uint2*>(codes + row * KB + c * 512 + lane * 8);
+      cw[r][c] = *reinterpret_cast<const v2u*>(codes + row * KB + c * 512 + lane * 8);
       const int g = 8 * c + (lane >> 3);
       const uint16_t sb = wscale[row * G + g];
       sv[r][c] = BF ? bf16_to_f32(sb) : __half2float(__builtin_bit_cast(__half, sb));
@@ -457,10 +457,10 @@ __global__ __launch_bounds__(256) void gemv_w4_row_kernel(
     }
   }
   // Activations of this lane: x[1024c + 16 lane + e], e = 0..15.
-  uint4 xv[CH][2];
+  v4u xv[CH][2];
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
-    const uint4* src = reinterpret_cast<const uint4*>(x + c * 1024 + lane * 16);
+    const v4u* src = reinterpret_cast<const v4u*>(x + c * 1024 + lane * 16);
     xv[c][0] = src[0];
     xv[c][1] = src[1];
   }
@@ -474,7 +474,7 @@ __global__ __launch_bounds__(256) void gemv_w4_row_kernel(
     for (int c = 0; c < CH; ++c) {
 #pragma unroll
       for (int d = 0; d < 2; ++d) {
-        const uint4 v = xv[c][d];
+        const v4u v = xv[c][d];
         xp[c][4 * d + 0] = __builtin_bit_cast(h2, perm_b32(v.z, v.x, 0x05040100u));
         xp[c][4 * d + 1] = __builtin_bit_cast(h2, perm_b32(v.z, v.x, 0x07060302u));
         xp[c][4 * d + 2] = __builtin_bit_cast(h2, perm_b32(v.w, v.y, 0x05040100u));

@@ -13,15 +13,15 @@ constexpr int kThreads = 256;
 constexpr int kPerThread = 8;   // 16-byte loads per thread
 constexpr size_t kBlockBytes = static_cast<size_t>(kThreads) * kPerThread * 16;
 
-__global__ __launch_bounds__(kThreads) void probe_read_kernel(const uint4* __restrict__ src,
+__global__ __launch_bounds__(kThreads) void probe_read_kernel(const v4u* __restrict__ src,
                                                               size_t n16,
                                                               uint32_t* __restrict__ dst) {
   const size_t base = static_cast<size_t>(blockIdx.x) * kThreads * kPerThread;
-  uint4 v[kPerThread];
+  v4u v[kPerThread];
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
     const size_t idx = base + static_cast<size_t>(i) * kThreads + threadIdx.x;
-    v[i] = idx < n16 ? src[idx] : make_uint4(0, 0, 0, 0);
+    v[i] = idx < n16 ? src[idx] : v4u{0, 0, 0, 0};
   }
   uint32_t x = 0;
 #pragma unroll
@@ -34,11 +34,11 @@ __global__ __launch_bounds__(kThreads) void probe_read_kernel(const uint4* __res
   if (threadIdx.x == 0) dst[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
 }
 
-__global__ __launch_bounds__(kThreads) void probe_copy_kernel(const uint4* __restrict__ src,
+__global__ __launch_bounds__(kThreads) void probe_copy_kernel(const v4u* __restrict__ src,
                                                               size_t n16,
-                                                              uint4* __restrict__ dst) {
+                                                              v4u* __restrict__ dst) {
   const size_t base = static_cast<size_t>(blockIdx.x) * kThreads * kPerThread;
-  uint4 v[kPerThread];
+  v4u v[kPerThread];
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
     const size_t idx = base + static_cast<size_t>(i) * kThreads + threadIdx.x;
@@ -62,10 +62,10 @@ hipError_t launch_probe(int kind, const void* src, void* dst, size_t bytes, hipS
   const int64_t blocks = probe_blocks(bytes);
   if (kind == BPW_PROBE_READ)
     probe_read_kernel<<<static_cast<unsigned>(blocks), kThreads, 0, s>>>(
-        static_cast<const uint4*>(src), n16, static_cast<uint32_t*>(dst));
+        static_cast<const v4u*>(src), n16, static_cast<uint32_t*>(dst));
   else
     probe_copy_kernel<<<static_cast<unsigned>(blocks), kThreads, 0, s>>>(
-        static_cast<const uint4*>(src), n16, static_cast<uint4*>(dst));
+        static_cast<const v4u*>(src), n16, static_cast<v4u*>(dst));
   return hipGetLastError();
 }
 

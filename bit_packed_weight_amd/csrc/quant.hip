@@ -76,14 +76,14 @@ __global__ __launch_bounds__(256) void int8_planes_kernel(const int8_t* __restri
   for (int64_t u = blockIdx.x * 256ll + threadIdx.x; u < units; u += gridDim.x * 256ll) {
     const int64_t base = u * 64;                     // rows are contiguous: unit u covers [64u, 64u+64)
     const int hh = static_cast<int>(u & 1);
-    const uint4* src = reinterpret_cast<const uint4*>(q + base);
-    uint4 in[4] = {src[0], src[1], src[2], src[3]};
-    uint4 o[4];
+    const v4u* src = reinterpret_cast<const v4u*>(q + base);
+    v4u in[4] = {src[0], src[1], src[2], src[3]};
+    v4u o[4];
     to_plane_order(in, o);
     int8_t* gbase = out + (base - hh * 64);          // start of the 128-group
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-      *reinterpret_cast<uint4*>(gbase + 32 * t + 16 * hh) = o[t];
+      *reinterpret_cast<v4u*>(gbase + 32 * t + 16 * hh) = o[t];
   }
 }
 
