@@ -23,8 +23,8 @@ namespace bpw {
 namespace {
 
 constexpr int BM = 256, BN = 256, BK = 64, NT = 256;
-constexpr int A_STRIDE = BK * 2 + 16;           // 144 bytes: conflict-free 16-byte LDS reads
-constexpr int A_BYTES = BM * A_STRIDE;          // one stage
+constexpr int A_ROW = 256;                      // one 128-column group of a row, bytes
+constexpr int A_BYTES = BM * A_ROW;             // one LDS buffer (64 KB)
 constexpr int LDS_BYTES = 2 * A_BYTES;
 
 __device__ __forceinline__ int d_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
@@ -33,15 +33,14 @@ typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
-// Eight codes of one packed dword (byte b: code 2b in the low nibble, 2b+1 in
-// the high nibble) -> eight 16-bit weights in that order, each the
+// Eight codes of one packed dword, given as its low nibbles (lo = w & 0x0f0f0f0f)
+// and high nibbles (hi) (byte b: code 2b in the low nibble, 2b+1 in the high) -> eight 16-bit weights in that order, each the
 // round-to-nearest-even of (code - zero) * scale. A byte select builds the fp32
 // value 128 + code (bits 0x43 0c 00 00); one fma with nzs = -(128 + zero) * scale
 // gives (code - zero) * scale exactly (all products fit fp32), then a packed
 // convert rounds two values at once.
 template <bool BF>
-__device__ __forceinline__ v4u dequant8(uint32_t w, float s, float nzs) {
-  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+__device__ __forceinline__ v4u dequant8(uint32_t lo, uint32_t hi, float s, float nzs) {
   uint32_t o[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
@@ -65,23 +64,29 @@ __global__ __launch_bounds__(NT, 1) void gemm_w4_kernel(
   const int G = K >> 7;
   const int KB = K >> 1;
   const int ZB = (G + 1) >> 1;
-  const int S = K / BK;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tile = xcd_swizzle(blockIdx.x, mtiles * ntiles);
   const int mt = tile % mtiles, nt = tile / mtiles;
   const int m0 = mt * BM, n0 = nt * BN;
   const int n = lane & 31, h = lane >> 5;
 
-  // A: 256 rows x 128 bytes per stage = 2048 chunks, eight per thread.
-  const uint16_t* a_src[8];
-  int a_dst[8];
+  // A: one 128-column group per LDS buffer, 256 rows x 256 bytes, 16-byte chunk
+  // c of row r stored at chunk r*16 + (c ^ (r & 15)) (XOR swizzle: the MFMA
+  // reads of 16 consecutive rows hit 16 different bank groups). Filled by direct
+  // global->LDS loads: instruction t of wave w writes chunks (16w + t)*64 + lane,
+  // i.e. row 64w + 4t + lane/16, and each lane fetches the global chunk that
+  // belongs there.
+  const int x_lane_row = 64 * wave + (lane >> 4);
+  auto a_load_group = [&](int g, int buf) __attribute__((always_inline)) {
+    const uint32_t dst = static_cast<uint32_t>(reinterpret_cast<size_t>(smem)) + buf * A_BYTES + wave * 16 * 1024;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int c = tid + NT * i;
-    const int r = c >> 3, col = c & 7;
-    a_src[i] = x + static_cast<size_t>(min(m0 + r, M - 1)) * K + col * 8;
-    a_dst[i] = r * A_STRIDE + col * 16;
-  }
+    for (int t = 0; t < 16; ++t) {
+      const int lrow = x_lane_row + 4 * t;
+      const int c = (lane & 15) ^ (lrow & 15);
+      const uint16_t* src = x + static_cast<size_t>(min(m0 + lrow, M - 1)) * K + g * 128 + c * 8;
+      lds_dma16(src, __builtin_amdgcn_readfirstlane(dst + t * 1024));
+    }
+  };
   // B: this lane's two weight rows (one per 32-row tile of the wave).
   const uint8_t* b_src[2];
   const uint16_t* s_src[2];
@@ -94,39 +99,48 @@ __global__ __launch_bounds__(NT, 1) void gemm_w4_kernel(
     z_src[j] = ZP ? zeros + row * ZB : nullptr;
   }
 
-  v4u ra[8];
-  auto a_load = [&](int st) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ra[i] = *reinterpret_cast<const v4u*>(a_src[i] + st * BK);
+  // Raw weights of one 128-column group: per 32-row tile j and 64-column half
+  // u, 16 code bytes; plus the scale and zero bits of the group. They are
+  // loaded two groups ahead, so nothing inside a group waits on a load issued
+  // in that group (mixing these loads with the LDS-direct A loads would
+  // otherwise force full waits).
+  struct GRaw {
+    v4u c[2][2];          // [u][j]
+    uint32_t sb[2], zb[2];
   };
-  auto a_store = [&](int buf) __attribute__((always_inline)) {
-    uint8_t* base = smem + buf * A_BYTES;
+  auto graw_load = [&](GRaw& r, int g) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<v4u*>(base + a_dst[i]) = ra[i];
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        r.c[u][j] = *reinterpret_cast<const v4u*>(b_src[j] + g * (2 * BK / 2) + u * (BK / 2));
+      r.sb[j] = s_src[j][g];
+      r.zb[j] = ZP ? (static_cast<uint32_t>(z_src[j][g >> 1]) >> (4 * (g & 1))) : 8u;
+    }
   };
-  // Raw weights of one stage: two 16-byte code loads, their scales and the
-  // folded zero term, double-buffered so a load never waits for a dequant.
-  struct BRaw {
-    v4u c[2];
+  // Per-stage dequant inputs: nibble-separated code words, scale, -(128+z)*s.
+  struct BPrep {
+    uint32_t lo[2][4], hi[2][4];
     float s[2], nz[2];
   };
-  auto b_load = [&](BRaw& r, int st) __attribute__((always_inline)) {
-    const int g = (st * BK) >> 7;
+  auto b_prep = [&](const GRaw& r, int u, BPrep& p) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      r.c[j] = *reinterpret_cast<const v4u*>(b_src[j] + st * (BK / 2));
-      const uint16_t sb = s_src[j][g];
-      r.s[j] = BF ? bf16_to_f32(sb) : __half2float(__builtin_bit_cast(__half, sb));
-      const int z = ZP ? ((z_src[j][g >> 1] >> (4 * (g & 1))) & 15) : 8;
-      r.nz[j] = -static_cast<float>(128 + z) * r.s[j];   // exact: 8-bit integer times a 16-bit float
+      const uint32_t w[4] = {r.c[u][j].x, r.c[u][j].y, r.c[u][j].z, r.c[u][j].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        p.lo[j][q] = w[q] & 0x0F0F0F0Fu;
+        p.hi[j][q] = (w[q] >> 4) & 0x0F0F0F0Fu;
+      }
+      p.s[j] = BF ? bf16_to_f32(static_cast<uint16_t>(r.sb[j]))
+                  : __half2float(__builtin_bit_cast(__half, static_cast<uint16_t>(r.sb[j])));
+      // exact: an 8-bit integer times a 16-bit float
+      p.nz[j] = -static_cast<float>(128 + static_cast<int>(r.zb[j] & 15u)) * p.s[j];
     }
   };
-  auto b_dequant_step = [&](const BRaw& r, v4u (&bop)[2][4], int ks) __attribute__((always_inline)) {
+  auto b_dequant_step = [&](const BPrep& p, v4u (&bop)[2][4], int ks) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint32_t w = ks == 0 ? r.c[j].x : ks == 1 ? r.c[j].y : ks == 2 ? r.c[j].z : r.c[j].w;
-      bop[j][ks] = dequant8<BF>(w, r.s[j], r.nz[j]);
-    }
+    for (int j = 0; j < 2; ++j) bop[j][ks] = dequant8<BF>(p.lo[j][ks], p.hi[j][ks], p.s[j], p.nz[j]);
   };
 
   v16f acc[8][2];
@@ -135,63 +149,82 @@ __global__ __launch_bounds__(NT, 1) void gemm_w4_kernel(
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
 
-  // One stage (64 columns): global loads for later stages first; then four
-  // MFMA steps over the A tile in LDS buffer `buf` with weights `cur`, each
-  // interleaved with a quarter of the dequantisation of the next stage's
-  // weights (`raw` -> `nxt`); then the next A tile goes to the other buffer.
-  // Scheduling fences keep the loads at the start and the LDS stores at the
-  // end, so no wait for a fresh load lands among the MFMAs.
-  auto stage = [&](int st, int buf, v4u (&cur)[2][4], v4u (&nxt)[2][4], const BRaw& raw,
-                   BRaw& load_into) __attribute__((always_inline)) {
-    a_load(min(st + 1, S - 1));
-    b_load(load_into, min(st + 2, S - 1));
+  // One 64-column half (u) of group g in LDS buffer g & 1: four MFMA steps with
+  // weights `cur`, each interleaved with the next step's A reads and a quarter
+  // of the next stage's dequant (`prep` -> `nxt`).
+  const int nsw = n & 15;
+  auto half_stage = [&](int buf, int u, v4u (&cur)[2][4], v4u (&nxt)[2][4], const BPrep& prep)
+      __attribute__((always_inline)) {
+    const uint8_t* base = smem + buf * A_BYTES + n * A_ROW;
+    auto chunk = [&](int ks) __attribute__((always_inline)) { return 16 * ((8 * u + 4 * h + ks) ^ nsw); };
+    v4u aop[2][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) aop[0][i] = *reinterpret_cast<const v4u*>(base + i * 32 * A_ROW + chunk(0));
     __builtin_amdgcn_sched_barrier(0);
-    const uint8_t* base = smem + buf * A_BYTES + 64 * h;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      v4u aop[8];
+      if (ks < 3) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) aop[i] = *reinterpret_cast<const v4u*>(base + (32 * i + n) * A_STRIDE + 16 * ks);
+        for (int i = 0; i < 8; ++i)
+          aop[(ks + 1) & 1][i] = *reinterpret_cast<const v4u*>(base + i * 32 * A_ROW + chunk(ks + 1));
+      }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           if (BF)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, aop[i]),
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, aop[ks & 1][i]),
                                                                 __builtin_bit_cast(v8bf, cur[j][ks]), acc[i][j], 0, 0, 0);
           else
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, aop[i]),
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, aop[ks & 1][i]),
                                                                __builtin_bit_cast(v8h, cur[j][ks]), acc[i][j], 0, 0, 0);
         }
       }
-      b_dequant_step(raw, nxt, ks);
-      // 8 LDS reads, then 16 x (1 MFMA + 3 VALU).
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+      b_dequant_step(prep, nxt, ks);
+      // 16 x (1 MFMA + 2 VALU), with the next step's 8 LDS reads spread in.
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
+      for (int q = 0; q < 8; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    a_store(buf ^ 1);
   };
 
   v4u bop0[2][4], bop1[2][4];
-  BRaw raw0, raw1;
-  a_load(0);
-  b_load(raw0, 0);
-  a_store(0);
+  GRaw r0, r1, r2;
+  a_load_group(0, 0);
+  graw_load(r0, 0);
+  graw_load(r1, min(1, G - 1));
+  __builtin_amdgcn_s_waitcnt(0);
+  {
+    BPrep p0;
+    b_prep(r0, 0, p0);
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) b_dequant_step(raw0, bop0, ks);
-  b_load(raw0, min(1, S - 1));
+    for (int ks = 0; ks < 4; ++ks) b_dequant_step(p0, bop0, ks);
+  }
   __syncthreads();
 
-  for (int st = 0; st < S; st += 2) {     // S = K / 64 is even
-    stage(st, 0, bop0, bop1, raw0, raw1);       // dequant stage st+1 from raw0, load st+2 into raw1
+  for (int g = 0; g < G; ++g) {
+    // The next group streams into the other buffer while this one is used;
+    // every register read below was loaded at least one group earlier and
+    // waited for at the previous barrier.
+    graw_load(r2, min(g + 2, G - 1));
+    BPrep pa, pb;
+    b_prep(r0, 1, pa);                 // second half of this group
+    b_prep(r1, 0, pb);                 // first half of the next group
+    __builtin_amdgcn_sched_barrier(0);
+    a_load_group(min(g + 1, G - 1), (g + 1) & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    half_stage(g & 1, 0, bop0, bop1, pa);
+    half_stage(g & 1, 1, bop1, bop0, pb);
+    __builtin_amdgcn_s_waitcnt(0);     // the direct A loads and raw weights have landed
     __syncthreads();
-    stage(st + 1, 1, bop1, bop0, raw1, raw0);   // dequant stage st+2 from raw1, load st+3 into raw0
-    __syncthreads();
+    r0 = r1;
+    r1 = r2;
   }
 
 #pragma unroll
