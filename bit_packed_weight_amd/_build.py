@@ -24,6 +24,9 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-variable", "-Wno-u
           "-Wno-pass-failed", "-I", os.path.join(ROOT, "include")]
 # Packed fp32 instructions stay off: the compiler must not form v_pk_*_f32.
 DEVICE = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# The int8 GEMM folds every MFMA result with VALU instructions, which cannot
+# read AGPRs: its MFMA results must be allocated in VGPRs.
+EXTRA = {"gemm_i8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc() -> str:
@@ -37,7 +40,7 @@ def _compile(src: str) -> str:
     out = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
     cmd = [hipcc(), *COMMON]
     if src.endswith(".hip"):
-        cmd += DEVICE
+        cmd += DEVICE + EXTRA.get(src, [])
     cmd += ["-c", os.path.join(CSRC, src), "-o", out]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:

@@ -9,10 +9,17 @@
 // P[m,n,g] and the fold is acc += float(P) * w_scale[n,g]; x_scale[m] is applied
 // once at the end.
 //
-// Workgroup tile 128 (tokens) x 256 (weight rows), 4 waves each 128 x 64; K is
-// walked one 128-group per stage through double-buffered LDS. Activations are
-// read in plane order (a reorder pass runs first when the caller passes the
-// natural order).
+// Workgroup tile 128 (tokens) x 256 (weight rows), 4 waves; wave w owns weight
+// rows [64w, 64w + 64) of the tile and all 128 tokens: 4 x 2 output tiles of
+// 32 x 32, i.e. eight "chains" of four MFMAs (one per code plane) per 128-group.
+// The fold of one chain (16 conversions + 16 fmas per lane) runs while the next
+// chain's MFMAs execute, so the VALU and the matrix core work side by side.
+//
+// Activations (plane order, 128 bytes per row and group) stream global -> LDS
+// by direct loads into a double buffer; each wave reads its A operands from LDS
+// one 32-row tile ahead. Weights never touch LDS: each lane loads its own 16
+// code bytes per 32-row weight tile and group one group ahead and decodes them
+// straight into B operands.
 #include "device.h"
 #include "launch.h"
 
@@ -20,14 +27,43 @@ namespace bpw {
 namespace {
 
 constexpr int BM = 128, BN = 256, NT = 256;
-constexpr int A_STRIDE = 144;   // 128 bytes + 16 pad: conflict-free 16-byte LDS reads
-constexpr int B_STRIDE = 48;    // 32 bytes + 16 pad
-constexpr int A_BYTES = BM * A_STRIDE;
-constexpr int B_BYTES = BN * B_STRIDE;
-constexpr int S_BYTES = BN * 4;
-constexpr int STAGE_BYTES = A_BYTES + B_BYTES + S_BYTES;
+constexpr int A_ROW = 128;                      // one 128-group of a row, plane order
+constexpr int A_BYTES = BM * A_ROW;             // one LDS buffer (16 KB)
+constexpr int LDS_BYTES = 2 * A_BYTES;
+constexpr int GROUP_M = 4;                      // tile raster: 4 token tiles per column sweep
 
 __device__ __forceinline__ int d_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
+// 16-byte LDS read straight into AGPRs (the MFMA reads its A operand from
+// there), leaving the VGPRs to the accumulators, group partials and B
+// operands. The compiler does not track this read: ds_wait_agpr must run
+// before the registers are used.
+template <int OFF>
+__device__ __forceinline__ void ds_read_agpr(v4i& dst, uint32_t addr) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=a"(dst) : "v"(addr), "i"(OFF));
+}
+// Wait for every outstanding LDS read; the operands are tied to the wait so
+// that no use of them can be scheduled before it.
+__device__ __forceinline__ void ds_wait_agpr(v4i (&a)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]));
+}
+
+// Logical tile -> (token tile, weight tile): runs of GROUP_M token tiles sweep
+// the weight tiles, so workgroups that run together share activation and code
+// slices in L2.
+__device__ __forceinline__ void tile_coords(int t, int mtiles, int ntiles, int& mt, int& nt) {
+  const int per = GROUP_M * ntiles;
+  const int first = (t / per) * GROUP_M;
+  const int gs = min(mtiles - first, GROUP_M);
+  const int r = t % per;
+  mt = first + r % gs;
+  nt = r / gs;
+}
 
 template <typename TOut, bool PARTIALS>
 __global__ __launch_bounds__(NT, 1) void gemm_t2_kernel(
@@ -39,109 +75,193 @@ __global__ __launch_bounds__(NT, 1) void gemm_t2_kernel(
   const int G = K >> 7;
   const int KB = K >> 2;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ntile_all = mtiles * ntiles;
-  const int tile = xcd_swizzle(blockIdx.x, ntile_all);
-  const int mt = mt0 + tile % mtiles, nt = nt0 + tile / mtiles;
+  int mt, nt;
+  tile_coords(xcd_swizzle(blockIdx.x, mtiles * ntiles), mtiles, ntiles, mt, nt);
+  mt += mt0;
+  nt += nt0;
   const int m0 = mt * BM, n0 = nt * BN;
-
-  // Global -> register staging assignments.
-  const int8_t* a_src[4];
-  int a_dst[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + NT * i;           // 1024 chunks of 16 bytes
-    const int r = c >> 3, col = c & 7;
-    a_src[i] = qp + static_cast<size_t>(min(m0 + r, M - 1)) * K + col * 16;
-    a_dst[i] = r * A_STRIDE + col * 16;
-  }
-  const uint8_t* b_src[2];
-  int b_dst[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = tid + NT * i;           // 512 chunks
-    const int r = c >> 1, half = c & 1;
-    b_src[i] = codes + static_cast<size_t>(min(n0 + r, N - 1)) * KB + half * 16;
-    b_dst[i] = A_BYTES + r * B_STRIDE + half * 16;
-  }
-  const __half* s_src = wscale + static_cast<size_t>(min(n0 + tid, N - 1)) * G;
-  const int s_dst = A_BYTES + B_BYTES + tid * 4;
-
-  v4u ra[4], rb[2];
-  float rs;
-  auto gload = [&](int g) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ra[i] = *reinterpret_cast<const v4u*>(a_src[i] + g * 128);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) rb[i] = *reinterpret_cast<const v4u*>(b_src[i] + g * 32);
-    rs = __half2float(s_src[g]);
-  };
-  auto lstore = [&](int buf) __attribute__((always_inline)) {
-    uint8_t* base = smem + buf * STAGE_BYTES;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<v4u*>(base + a_dst[i]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) *reinterpret_cast<v4u*>(base + b_dst[i]) = rb[i];
-    *reinterpret_cast<float*>(base + s_dst) = rs;
-  };
-
   const int n = lane & 31, h = lane >> 5;
+
+  // A: row r of a buffer is 8 chunks of 16 bytes; chunk c sits in slot
+  // c ^ (r & 7), so the 32 rows of one MFMA read hit distinct bank groups.
+  // Direct load t (0..3) of wave w fills LDS bytes [(4w + t) * 1024, +1024):
+  // rows 8 (4w + t) + lane / 8, slot lane % 8.
+  const int a_row0 = 32 * wave + (lane >> 3);
+  const int a_chunk = (lane & 7) ^ (a_row0 & 7);   // (row & 7) is the same for all t
+  const int8_t* a_base = qp + a_chunk * 16;
+  int a_row[4];                                      // token rows past the end are clamped
+#pragma unroll
+  for (int t = 0; t < 4; ++t) a_row[t] = min(m0 + a_row0 + 8 * t, M - 1);
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<size_t>(smem)) + wave * 4096;
+  auto a_load = [&](int g, int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int8_t* src = a_base + static_cast<size_t>(a_row[t]) * K + g * 128;
+      lds_dma16(src, __builtin_amdgcn_readfirstlane(lds0 + buf * A_BYTES + t * 1024));
+    }
+  };
+  // A operand reads (into AGPRs, see ds_read_agpr): plane t of token row
+  // 32 i + n is chunk 2t + h; the buffer and token tile are immediate offsets.
+  uint32_t a_addr[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    a_addr[t] = static_cast<uint32_t>(reinterpret_cast<size_t>(smem)) + n * A_ROW + 16 * ((2 * t + h) ^ (n & 7));
+  auto a_read = [&](auto BUFC, auto IC, v4i (&dst)[4]) __attribute__((always_inline)) {
+    constexpr int OFF = decltype(BUFC)::value * A_BYTES + decltype(IC)::value * 32 * A_ROW;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) ds_read_agpr<OFF>(dst[t], a_addr[t]);
+  };
+
+  // B: this lane's two weight rows (one per 32-row tile of the wave).
+  const uint8_t* b_src[2];
+  const __half* s_src[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const size_t row = static_cast<size_t>(min(n0 + 64 * wave + 32 * j + n, N - 1));
+    b_src[j] = codes + row * KB + 16 * h;
+    s_src[j] = wscale + row * G;
+  }
+  // Raw bytes only (the scale is converted a group later, so that nothing
+  // waits on these loads before it has to).
+  struct Raw {
+    v4u c[2];
+    __half s[2];
+  };
+  auto raw_load = [&](Raw& r, int g) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      r.c[j] = *reinterpret_cast<const v4u*>(b_src[j] + g * 32);
+      r.s[j] = s_src[j][g];
+    }
+  };
+  // 16 code bytes -> the four code planes as signed MFMA B operands. Lane half
+  // h, plane t, byte 4q + p holds the weight at 64h + 16q + 4p + t of the
+  // group, matching plane-ordered activations at offset 32t + 16h + 4q + p.
+  auto decode = [&](const v4u& c, v4i (&b)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      b[t] = v4i{static_cast<int>(code_plane_signed(c.x, t)), static_cast<int>(code_plane_signed(c.y, t)),
+                 static_cast<int>(code_plane_signed(c.z, t)), static_cast<int>(code_plane_signed(c.w, t))};
+  };
+
   v16f acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  for (int g = 0; g < G; ++g) {
-    const int buf = g & 1;
-    if (g + 1 < G) gload(g + 1);
-    const uint8_t* base = smem + buf * STAGE_BYTES;
-    // B operands of this wave's two 32-row weight tiles, decoded to signed bytes.
-    v4i bop[2][4];
-    float sj[2];
+  // Fold (or, for the partials entry, store) the int32 result of chain (i, j)
+  // of group g.
+  auto fold = [&](const v16i& d, int i, int j, float s, int g) __attribute__((always_inline)) {
+    if (PARTIALS) {
+      const int nn = n0 + 64 * wave + 32 * j + n;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int nr = 64 * wave + 32 * j + n;
-      const v4u pk = *reinterpret_cast<const v4u*>(base + A_BYTES + nr * B_STRIDE + 16 * h);
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        bop[j][t] = v4i{static_cast<int>(code_plane_signed(pk.x, t)),
-                        static_cast<int>(code_plane_signed(pk.y, t)),
-                        static_cast<int>(code_plane_signed(pk.z, t)),
-                        static_cast<int>(code_plane_signed(pk.w, t))};
-      sj[j] = *reinterpret_cast<const float*>(base + A_BYTES + B_BYTES + nr * 4);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v4i aop[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        aop[t] = *reinterpret_cast<const v4i*>(base + (32 * i + n) * A_STRIDE + 32 * t + 16 * h);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        v16i d = {};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) d = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop[t], bop[j][t], d, 0, 0, 0);
-        if (PARTIALS) {
-          const int nn = n0 + 64 * wave + 32 * j + n;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int mm = m0 + 32 * i + d_row(r, h);
-            if (mm >= pm0 && mm < pm1 && nn >= pn0 && nn < pn1)
-              pout[(static_cast<size_t>(mm - pm0) * (pn1 - pn0) + (nn - pn0)) * G + g] = d[r];
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(static_cast<float>(d[r]), sj[j], acc[i][j][r]);
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int mm = m0 + 32 * i + d_row(r, h);
+        if (mm >= pm0 && mm < pm1 && nn >= pn0 && nn < pn1)
+          pout[(static_cast<size_t>(mm - pm0) * (pn1 - pn0) + (nn - pn0)) * G + g] = d[r];
       }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(static_cast<float>(d[r]), s, acc[i][j][r]);
     }
-    if (g + 1 < G) lstore(buf ^ 1);
+  };
+  auto chain = [&](const v4i (&a)[4], const v4i (&b)[4]) __attribute__((always_inline)) {
+    v16i d = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[0], b[0], v16i{}, 0, 0, 0);
+#pragma unroll
+    for (int t = 1; t < 4; ++t) d = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[t], b[t], d, 0, 0, 0);
+    return d;
+  };
+
+  v4i aop[2][4];        // A operands (AGPRs) of the current and next 32-row token tile
+  v4i bop[2][4];        // B operands of the wave's two weight tiles
+  v16i dprev = {};      // the chain whose fold is pending (none before group 0)
+  float sprev = 0.0f;
+  Raw raw;
+
+  a_load(0, 0);
+  raw_load(raw, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  decode(raw.c[0], bop[0]);
+  float s0 = __half2float(raw.s[0]), s1 = __half2float(raw.s[1]);
+
+  // One 128-group in LDS buffer BUF. On entry: bop[0] holds this group's first
+  // weight tile, raw its raw bytes, dprev/sprev the previous group's last chain
+  // (zero before group 0). An AGPR read is always waited for inside the same
+  // group, so no register copy of a value still in flight can be placed at the
+  // loop edge. The
+  // body has no branches: after the last group the loads and decodes of
+  // "group g + 1" repeat the last group and are not used.
+  auto group = [&](int g, auto BUFC) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(BUFC)::value;
+    const int gn = min(g + 1, G - 1);
+    a_read(IntC<BUF>{}, IntC<0>{}, aop[0]);
+    // The other buffer was last read before the previous barrier.
+    a_load(gn, BUF ^ 1);
+    if (!PARTIALS || g > 0) fold(dprev, 3, 1, sprev, g - 1);
+    ds_wait_agpr(aop[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    // chain (0,0); decode this group's second weight tile; read token tile 1.
+    {
+      const v16i d = chain(aop[0], bop[0]);
+      decode(raw.c[1], bop[1]);
+      a_read(IntC<BUF>{}, IntC<1>{}, aop[1]);
+      dprev = d;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 11, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    Raw nraw;
+    raw_load(nraw, gn);
+    __builtin_amdgcn_sched_barrier(0);
+    // Chains (0,1) (1,0) (1,1) ... (3,1); each folds its predecessor. Token
+    // tile i + 1 is read during chain (i, 0), into the registers that chain
+    // (i - 1, 1) used, and waited for before chain (i + 1, 0).
+    auto slot = [&](auto CC) __attribute__((always_inline)) {
+      constexpr int c = decltype(CC)::value, i = c >> 1, j = c & 1;
+      if (j == 0) ds_wait_agpr(aop[i & 1]);
+      const v16i d = chain(aop[i & 1], bop[j]);
+      constexpr int pi = (c - 1) >> 1, pj = (c - 1) & 1;
+      fold(dprev, pi, pj, pj ? s1 : s0, g);
+      if (j == 0 && i < 3) a_read(IntC<BUF>{}, IntC<i + 1>{}, aop[(i + 1) & 1]);
+      // this group's first weight tile is free after chain (3,0): decode the next one
+      if (c == 7) decode(nraw.c[0], bop[0]);
+      dprev = d;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (c == 7)
+          __builtin_amdgcn_sched_group_barrier(0x002, 19, 0);
+        else
+          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    slot(IntC<1>{});
+    slot(IntC<2>{});
+    slot(IntC<3>{});
+    slot(IntC<4>{});
+    slot(IntC<5>{});
+    slot(IntC<6>{});
+    slot(IntC<7>{});
+    sprev = s1;
+    raw = nraw;
+    s0 = __half2float(nraw.s[0]);
+    s1 = __half2float(nraw.s[1]);
+    __builtin_amdgcn_s_waitcnt(0);     // the direct A loads and raw weights have landed
     __syncthreads();
+  };
+  int g = 0;
+  for (; g + 1 < G; g += 2) {
+    group(g, IntC<0>{});
+    group(g + 1, IntC<1>{});
   }
+  if (g < G) group(g, IntC<0>{});
+  fold(dprev, 3, 1, sprev, G - 1);
   if (PARTIALS) return;
 
 #pragma unroll
@@ -166,7 +286,7 @@ hipError_t go(const bpw_weights& w, const int8_t* qp, const float* xs, int m, TO
               hipStream_t s) {
   const int n = static_cast<int>(w.n), k = static_cast<int>(w.k);
   const int mtiles = (m + BM - 1) / BM, ntiles = (n + BN - 1) / BN;
-  gemm_t2_kernel<TOut, false><<<mtiles * ntiles, NT, 2 * STAGE_BYTES, s>>>(
+  gemm_t2_kernel<TOut, false><<<mtiles * ntiles, NT, LDS_BYTES, s>>>(
       qp, xs, static_cast<const uint8_t*>(w.codes), static_cast<const __half*>(w.scales), m, n, k,
       y, nullptr, 0, 0, 0, 0, 0, mtiles, 0, ntiles);
   return hipGetLastError();
@@ -191,7 +311,7 @@ hipError_t launch_gemm_t2_partials(const bpw_weights& w, const int8_t* q_planes,
   const int mt0 = static_cast<int>(m0 / BM), mt1 = static_cast<int>((m1 - 1) / BM);
   const int nt0 = static_cast<int>(n0 / BN), nt1 = static_cast<int>((n1 - 1) / BN);
   const int mtiles = mt1 - mt0 + 1, ntiles = nt1 - nt0 + 1;
-  gemm_t2_kernel<float, true><<<mtiles * ntiles, NT, 2 * STAGE_BYTES, s>>>(
+  gemm_t2_kernel<float, true><<<mtiles * ntiles, NT, LDS_BYTES, s>>>(
       q_planes, nullptr, static_cast<const uint8_t*>(w.codes),
       static_cast<const __half*>(w.scales), static_cast<int>(m), n, k, nullptr, out,
       static_cast<int>(m0), static_cast<int>(m1), static_cast<int>(n0), static_cast<int>(n1),
