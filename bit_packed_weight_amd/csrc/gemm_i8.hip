@@ -34,6 +34,29 @@ constexpr int GROUP_M = 4;                      // tile raster: 4 token tiles pe
 
 __device__ __forceinline__ int d_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
+// Four consecutive outputs (the address is 4-element aligned), each rounded to
+// nearest even as store_out does.
+__device__ __forceinline__ void store_out4(float* p, const float (&v)[4]) {
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  *reinterpret_cast<v4f*>(p) = v4f{v[0], v[1], v[2], v[3]};
+}
+__device__ __forceinline__ void store_out4(__half* p, const float (&v)[4]) {
+  uint32_t w[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+    w[e] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, __float2half_rn(v[2 * e]))) |
+           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, __float2half_rn(v[2 * e + 1]))) << 16);
+  *reinterpret_cast<v2u*>(p) = v2u{w[0], w[1]};
+}
+__device__ __forceinline__ void store_out4(uint16_t* p, const float (&v)[4]) {
+  uint32_t w[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+    w[e] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v[2 * e]))) |
+           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v[2 * e + 1]))) << 16);
+  *reinterpret_cast<v2u*>(p) = v2u{w[0], w[1]};
+}
+
 template <int V>
 struct IntC {
   static constexpr int value = V;
@@ -264,20 +287,46 @@ __global__ __launch_bounds__(NT, 1) void gemm_t2_kernel(
   fold(dprev, 3, 1, sprev, G - 1);
   if (PARTIALS) return;
 
+  // Epilogue: each 32 x 64 block of the wave goes through LDS (8 KB per wave,
+  // the A buffers are free once every wave is past this barrier) so that the
+  // output leaves in row segments of 4 values per lane instead of single
+  // 2-byte stores.
+  __syncthreads();
+  float* stage = reinterpret_cast<float*>(smem + wave * 8192);
+  const bool vec = (N & 3) == 0;
+  // Row scales of the 32 rows this lane stores, loaded together up front.
+  float xsv[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) xsv[i][q] = x_scale[min(m0 + 32 * i + 4 * q + (lane >> 4), M - 1)];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int mm = m0 + 32 * i + d_row(r, h);
-      if (mm < M) {
-        const float xs = x_scale[mm];
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int nn = n0 + 64 * wave + 32 * j + n;
-          if (nn < N) store_out(y + static_cast<size_t>(mm) * N + nn, acc[i][j][r] * xs);
+      for (int r = 0; r < 16; ++r) stage[d_row(r, h) * 64 + 32 * j + n] = acc[i][j][r];
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int row = 4 * q + (lane >> 4), c4 = 4 * (lane & 15);
+      const v4u raw4 = *reinterpret_cast<const v4u*>(stage + row * 64 + c4);
+      const int mm = m0 + 32 * i + row, nn = n0 + 64 * wave + c4;
+      if (mm < M) {
+        const float xs = xsv[i][q];
+        const float v[4] = {__uint_as_float(raw4.x) * xs, __uint_as_float(raw4.y) * xs,
+                            __uint_as_float(raw4.z) * xs, __uint_as_float(raw4.w) * xs};
+        TOut* dst = y + static_cast<size_t>(mm) * N + nn;
+        if (vec && nn + 3 < N) {
+          store_out4(dst, v);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (nn + e < N) store_out(dst + e, v[e]);
         }
       }
     }
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
