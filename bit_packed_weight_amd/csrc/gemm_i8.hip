@@ -22,6 +22,7 @@
 // straight into B operands.
 #include "device.h"
 #include "launch.h"
+#include "store.h"
 
 namespace bpw {
 namespace {
@@ -33,29 +34,6 @@ constexpr int LDS_BYTES = 2 * A_BYTES;
 constexpr int GROUP_M = 4;                      // tile raster: 4 token tiles per column sweep
 
 __device__ __forceinline__ int d_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
-
-// Four consecutive outputs (the address is 4-element aligned), each rounded to
-// nearest even as store_out does.
-__device__ __forceinline__ void store_out4(float* p, const float (&v)[4]) {
-  typedef float v4f __attribute__((ext_vector_type(4)));
-  *reinterpret_cast<v4f*>(p) = v4f{v[0], v[1], v[2], v[3]};
-}
-__device__ __forceinline__ void store_out4(__half* p, const float (&v)[4]) {
-  uint32_t w[2];
-#pragma unroll
-  for (int e = 0; e < 2; ++e)
-    w[e] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, __float2half_rn(v[2 * e]))) |
-           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, __float2half_rn(v[2 * e + 1]))) << 16);
-  *reinterpret_cast<v2u*>(p) = v2u{w[0], w[1]};
-}
-__device__ __forceinline__ void store_out4(uint16_t* p, const float (&v)[4]) {
-  uint32_t w[2];
-#pragma unroll
-  for (int e = 0; e < 2; ++e)
-    w[e] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v[2 * e]))) |
-           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v[2 * e + 1]))) << 16);
-  *reinterpret_cast<v2u*>(p) = v2u{w[0], w[1]};
-}
 
 template <int V>
 struct IntC {

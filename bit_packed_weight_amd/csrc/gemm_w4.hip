@@ -18,6 +18,7 @@
 // steps.
 #include "device.h"
 #include "launch.h"
+#include "store.h"
 
 namespace bpw {
 namespace {
@@ -227,19 +228,39 @@ __global__ __launch_bounds__(NT, 1) void gemm_w4_kernel(
     r1 = r2;
   }
 
+  // Epilogue: each 32 x 64 block of the wave goes through LDS (8 KB per wave;
+  // the A buffers are free once every wave is past this barrier) so that the
+  // output leaves in row segments of 4 values per lane instead of single
+  // 2-byte stores.
+  __syncthreads();
+  float* stage = reinterpret_cast<float*>(smem + wave * 8192);
+  const bool vec = (N & 3) == 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int mm = m0 + 32 * i + d_row(r, h);
-      if (mm < M) {
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int nn = n0 + 64 * wave + 32 * j + n;
-          if (nn < N) store_out(y + static_cast<size_t>(mm) * N + nn, acc[i][j][r]);
+      for (int r = 0; r < 16; ++r) stage[d_row(r, h) * 64 + 32 * j + n] = acc[i][j][r];
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int row = 4 * q + (lane >> 4), c4 = 4 * (lane & 15);
+      const v4u raw4 = *reinterpret_cast<const v4u*>(stage + row * 64 + c4);
+      const int mm = m0 + 32 * i + row, nn = n0 + 64 * wave + c4;
+      if (mm < M) {
+        const float v[4] = {__uint_as_float(raw4.x), __uint_as_float(raw4.y), __uint_as_float(raw4.z),
+                            __uint_as_float(raw4.w)};
+        TOut* dst = y + static_cast<size_t>(mm) * N + nn;
+        if (vec && nn + 3 < N) {
+          store_out4(dst, v);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (nn + e < N) store_out(dst + e, v[e]);
         }
       }
     }
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
