@@ -541,7 +541,11 @@ __global__ __launch_bounds__(256) void gemv_w4_row_kernel(
 int fold_for(int64_t m) { return m <= 1 ? 1 : (m <= 8 ? 4 : (m <= 16 ? 8 : 16)); }
 int waves_for(int64_t groups) { return groups >= 16 ? 8 : 4; }
 
-constexpr int kRowR = 4;   // rows per wave in the M = 1 kernels
+// Rows per wave in the M = 1 kernels (measured on the decode shapes: fewer rows
+// per wave put more waves in flight; one row per wave pays the activation
+// transpose too often).
+constexpr int kRowT2 = 2;
+constexpr int kRowW4 = 2;
 
 bool t2_row_ok(int64_t m, int64_t k) { return m == 1 && k % 4096 == 0 && k / 4096 <= 4; }
 bool w4_row_ok(int64_t m, int64_t k) { return m == 1 && k % 1024 == 0 && k / 1024 <= 8; }
@@ -552,13 +556,15 @@ size_t t2_lds(int64_t m, int64_t k) {
   return stage > red ? stage : red;
 }
 
-unsigned row_blocks(int n) { return static_cast<unsigned>(((n + kRowR - 1) / kRowR + 3) / 4); }
+unsigned row_blocks(int n, int rows_per_wave) {
+  return static_cast<unsigned>(((n + rows_per_wave - 1) / rows_per_wave + 3) / 4);
+}
 
 template <int CH, typename TOut, bool PARTIALS>
 void t2_row_go(const bpw_weights& w, const int8_t* q, const float* xs, TOut* y, int32_t* pout,
                int pn0, int pn1, hipStream_t s) {
   const int n = static_cast<int>(w.n), k = static_cast<int>(w.k);
-  gemv_t2_row_kernel<kRowR, CH, TOut, PARTIALS><<<row_blocks(n), 256, 0, s>>>(
+  gemv_t2_row_kernel<kRowT2, CH, TOut, PARTIALS><<<row_blocks(n, kRowT2), 256, 0, s>>>(
       static_cast<const uint8_t*>(w.codes), static_cast<const __half*>(w.scales), q, xs, n, k, y,
       pout, pn0, pn1);
 }
@@ -618,7 +624,7 @@ hipError_t w4_go(const bpw_weights& w, const uint16_t* x, int m, TOut* y, hipStr
 template <int CH, bool BF, bool ZP, typename TOut>
 void w4_row_go(const bpw_weights& w, const uint16_t* x, TOut* y, hipStream_t s) {
   const int n = static_cast<int>(w.n), k = static_cast<int>(w.k);
-  gemv_w4_row_kernel<kRowR, CH, BF, ZP, TOut><<<row_blocks(n), 256, 0, s>>>(
+  gemv_w4_row_kernel<kRowW4, CH, BF, ZP, TOut><<<row_blocks(n, kRowW4), 256, 0, s>>>(
       static_cast<const uint8_t*>(w.codes), static_cast<const uint16_t*>(w.scales),
       static_cast<const uint8_t*>(w.zeros), x, n, k, y);
 }
