@@ -141,16 +141,31 @@ def bench_probe(bpw, torch, kind, nbytes, steps, warmup):
             "GB_s": moved / (ms * 1e6), "copies": count}
 
 
-def bench_w4_decode(bpw, synth, torch, np, steps, warmup):
-    w = synth.w4a16_decode(1)
+def bench_ternary_decode_m(bpw, synth, torch, np, steps, warmup, m=16):
+    """Skinny ternary decode (M rows of int8 activations) through the MFMA GEMV."""
+    w = synth.ternary_decode(m)
+    planes = bpw.prepare_packed_host(bpw.TERNARY2, w.codes, w.scales)
+    copies = rotated_copies(bpw, planes, 1 << 30)
+    x = to_dev(w.x, "f32", torch, np)
+    q, xs = bpw.quantize_rows(x)
+    y = torch.empty((m, w.n), dtype=torch.float16, device="cuda")
+    nbytes = copies[0].logical_bytes
+    ms = time_graph(torch, lambda i: bpw.gemv_packed(copies[i % len(copies)], q, xs, out=y), steps, warmup)
+    return {"workload": "ternary_decode_gemv", "M": m, "K": w.k, "N": w.n, "weight_bytes": nbytes,
+            "us_per_call": ms * 1e3, "GB_s": nbytes / (ms * 1e6), "frac_hbm_peak": nbytes / (ms * 1e6) / HBM_PEAK_GBS,
+            "copies": len(copies)}
+
+
+def bench_w4_decode(bpw, synth, torch, np, steps, warmup, m=1):
+    w = synth.w4a16_decode(m)
     planes = bpw.prepare_packed_host(bpw.INT4_ZP, w.codes, w.scales, w.zeros, w.g_idx)
     copies = rotated_copies(bpw, planes, 1 << 30)
     x = to_dev(w.x, "f16", torch, np)
-    y = torch.empty((1, w.n), dtype=torch.float16, device="cuda")
-    ws = torch.empty(bpw.workspace_size(copies[0], 1, bpw.F16, bpw.PATH_GEMV), dtype=torch.uint8, device="cuda")
+    y = torch.empty((m, w.n), dtype=torch.float16, device="cuda")
+    ws = torch.empty(bpw.workspace_size(copies[0], m, bpw.F16, bpw.PATH_GEMV), dtype=torch.uint8, device="cuda")
     nbytes = copies[0].logical_bytes
     ms = time_graph(torch, lambda i: bpw.gemv_packed(copies[i % len(copies)], x, out=y, workspace=ws), steps, warmup)
-    return {"workload": "w4a16_decode_gemv", "M": 1, "K": w.k, "N": w.n, "act_order": True,
+    return {"workload": "w4a16_decode_gemv", "M": m, "K": w.k, "N": w.n, "act_order": True,
             "weight_bytes": nbytes, "us_per_call": ms * 1e3, "GB_s": nbytes / (ms * 1e6),
             "frac_hbm_peak": nbytes / (ms * 1e6) / HBM_PEAK_GBS, "copies": len(copies)}
 
@@ -237,8 +252,10 @@ def main():
         extra.append(probe)
         torch.cuda.empty_cache()
     if not args.no_extra:
-        for fn, steps, warm in ((bench_w4_decode, 900, 300), (bench_w4_prefill, 30, 6), (bench_ternary_prefill, 12, 3)):
-            r = fn(bpw, synth, torch, np, steps, warm)
+        runs = ((bench_ternary_decode_m, 900, 300, {"m": 16}), (bench_w4_decode, 900, 300, {"m": 1}),
+                (bench_w4_decode, 900, 300, {"m": 8}), (bench_w4_prefill, 30, 6, {}), (bench_ternary_prefill, 12, 3, {}))
+        for fn, steps, warm, kw in runs:
+            r = fn(bpw, synth, torch, np, steps, warm, **kw)
             log(f"[bench] {json.dumps(r)}")
             extra.append(r)
             torch.cuda.empty_cache()

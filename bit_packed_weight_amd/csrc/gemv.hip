@@ -283,6 +283,119 @@ __global__ __launch_bounds__(NW * 64) void gemv_t2_kernel(
   }
 }
 
+// ---------------------------------------------------------------- ternary, 2 <= M <= 32, K <= 4096
+// Skinny products stream the weights like the M = 1 kernel but feed int8 MFMA.
+// One workgroup per CU owns a contiguous slice of weight rows (processed as
+// tiles of 32 rows); its 8 waves split K, GPW groups each. A wave keeps the
+// A operands of its K slice (activations in plane order, all M rows) in
+// registers, loaded once, and streams its slice of each weight row straight
+// from HBM into B operands: lane (n, h) reads 16 bytes of row n per group, and
+// the two lanes of a row together cover its 32-byte group, so the wave reads
+// whole 128-byte lines. Codes are decoded signed (the {0xff, 0x00, 0x01, 0x02}
+// byte table), so each chain of four MFMAs is the exact partial P[m,n,g]. The
+// eight per-wave fp32 results of a tile are summed in a fixed order through LDS.
+constexpr int kSkinnyWaves = 8;
+
+template <int GPW, int MAXT, int FR, typename TOut, bool PARTIALS>
+__global__ __launch_bounds__(kSkinnyWaves * 64) void gemv_t2_skinny_kernel(
+    const uint8_t* __restrict__ codes, const __half* __restrict__ wscale,
+    const int8_t* __restrict__ q, const float* __restrict__ x_scale, int M, int N, int K, int rpw,
+    TOut* __restrict__ y, int32_t* __restrict__ pout, int pm0, int pm1, int pn0, int pn1, int wg0) {
+  // FR: accumulator registers that can hold a token row < M (registers 0..7
+  // hold rows 0..15, so 8 when M <= 16, else 16).
+  __shared__ float red[2 * kSkinnyWaves * FR * 64];       // [tile of a pair][wave][reg][lane]
+  const int G = K >> 7, KB = K >> 2;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 31, h = lane >> 5;
+  const int r0 = (blockIdx.x + wg0) * rpw;
+  const int r1 = min(r0 + rpw, N);
+  const int gb = wave * GPW;
+
+  // Weights first (the long-latency loads): every tile and group of this wave.
+  v4u cw[MAXT][GPW];
+  float sc[MAXT][GPW];
+#pragma unroll
+  for (int t = 0; t < MAXT; ++t) {
+    const size_t row = static_cast<size_t>(min(r0 + 32 * t + n, N - 1));
+#pragma unroll
+    for (int u = 0; u < GPW; ++u) {
+      const int g = min(gb + u, G - 1);
+      cw[t][u] = *reinterpret_cast<const v4u*>(codes + row * KB + g * 32 + 16 * h);
+      sc[t][u] = __half2float(wscale[row * G + g]);
+    }
+  }
+  // A operands: token row m = n (clamped), half h of each group, plane order.
+  v4i a[GPW][4];
+  const int mA = min(n, M - 1);
+#pragma unroll
+  for (int u = 0; u < GPW; ++u) {
+    const int g = min(gb + u, G - 1);
+    const v4u* src = reinterpret_cast<const v4u*>(q + static_cast<size_t>(mA) * K + g * 128 + 64 * h);
+    v4u in[4] = {src[0], src[1], src[2], src[3]};
+    v4u o[4];
+    to_plane_order(in, o);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) a[u][t] = __builtin_bit_cast(v4i, o[t]);
+  }
+
+  const int ntile = (r1 - r0 + 31) >> 5;
+  // Tiles in pairs: compute both, then one fixed-order reduction through LDS.
+#pragma unroll
+  for (int t0 = 0; t0 < MAXT; t0 += 2) {
+    if (t0 >= ntile) break;                                 // uniform over the workgroup
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int t = t0 + tt;
+      if (t >= ntile) break;
+      float acc[FR];
+#pragma unroll
+      for (int r = 0; r < FR; ++r) acc[r] = 0.0f;
+#pragma unroll
+      for (int u = 0; u < GPW; ++u) {
+        const int g = gb + u;
+        if (g < G) {                                        // uniform over the wave
+          const v4u c = cw[t][u];
+          v16i d = {};
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const v4i b = {static_cast<int>(code_plane_signed(c.x, p)), static_cast<int>(code_plane_signed(c.y, p)),
+                           static_cast<int>(code_plane_signed(c.z, p)), static_cast<int>(code_plane_signed(c.w, p))};
+            d = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[u][p], b, d, 0, 0, 0);
+          }
+          if (PARTIALS) {
+            const int nn = r0 + 32 * t + n;
+#pragma unroll
+            for (int r = 0; r < FR; ++r) {
+              const int mm = d_row(r, h);
+              if (mm < M && mm >= pm0 && mm < pm1 && nn < r1 && nn >= pn0 && nn < pn1)
+                pout[(static_cast<size_t>(mm - pm0) * (pn1 - pn0) + (nn - pn0)) * G + g] = d[r];
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < FR; ++r) acc[r] = fmaf(static_cast<float>(d[r]), sc[t][u], acc[r]);
+          }
+        }
+      }
+      if (!PARTIALS) {
+#pragma unroll
+        for (int r = 0; r < FR; ++r) red[((tt * kSkinnyWaves + wave) * FR + r) * 64 + lane] = acc[r];
+      }
+    }
+    if (PARTIALS) continue;
+    __syncthreads();
+    const int np = min(2, ntile - t0);
+    for (int o = tid; o < np * FR * 64; o += kSkinnyWaves * 64) {
+      const int tt = o / (FR * 64), rl = o - tt * FR * 64, r = rl >> 6, l = rl & 63;
+      float v = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kSkinnyWaves; ++w) v += red[((tt * kSkinnyWaves + w) * FR + r) * 64 + l];
+      const int mm = d_row(r, l >> 5), nn = r0 + 32 * (t0 + tt) + (l & 31);
+      if (mm < M && nn < r1) store_out(y + static_cast<size_t>(mm) * N + nn, v * x_scale[mm]);
+    }
+    __syncthreads();
+  }
+}
+
 // ---------------------------------------------------------------- 4-bit GEMV
 
 // Eight codes of one packed dword -> the B operand in the order
@@ -593,10 +706,71 @@ hipError_t t2_go(const bpw_weights& w, const int8_t* q, const float* xs, int m, 
   return hipGetLastError();
 }
 
+// Compute units of the current device (the skinny kernel runs one workgroup per
+// CU); queried once per device.
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+    cached[dev] = c;
+  }
+  return cached[dev];
+}
+
+bool t2_skinny_ok(int64_t m, int64_t k) { return m >= 2 && m <= 32 && k <= 128 * kSkinnyWaves * 4; }
+
+// Rows per workgroup: the rows split evenly over the CUs, at least 16, at most
+// four 32-row tiles.
+int skinny_rpw(int n) {
+  const int cus = cu_count();
+  int rpw = (n + cus - 1) / cus;
+  rpw = max(16, (rpw + 7) & ~7);
+  return min(rpw, 128);
+}
+
+template <int GPW, int MAXT, typename TOut, bool PARTIALS>
+void t2_skinny_go(const bpw_weights& w, const int8_t* q, const float* xs, int m, int rpw, TOut* y,
+                  int32_t* pout, int pm0, int pm1, int pn0, int pn1, int wg0, int nwg, hipStream_t s) {
+  const uint8_t* codes = static_cast<const uint8_t*>(w.codes);
+  const __half* sc = static_cast<const __half*>(w.scales);
+  const int n = static_cast<int>(w.n), k = static_cast<int>(w.k);
+  if (m <= 16)
+    gemv_t2_skinny_kernel<GPW, MAXT, 8, TOut, PARTIALS><<<nwg, kSkinnyWaves * 64, 0, s>>>(
+        codes, sc, q, xs, m, n, k, rpw, y, pout, pm0, pm1, pn0, pn1, wg0);
+  else
+    gemv_t2_skinny_kernel<GPW, MAXT, 16, TOut, PARTIALS><<<nwg, kSkinnyWaves * 64, 0, s>>>(
+        codes, sc, q, xs, m, n, k, rpw, y, pout, pm0, pm1, pn0, pn1, wg0);
+}
+
+template <typename TOut, bool PARTIALS>
+hipError_t t2_skinny(const bpw_weights& w, const int8_t* q, const float* xs, int m, TOut* y,
+                     int32_t* pout, int pm0, int pm1, int pn0, int pn1, hipStream_t s) {
+  const int n = static_cast<int>(w.n), g = static_cast<int>(w.k / 128);
+  const int rpw = skinny_rpw(n);
+  const int gpw = (g + kSkinnyWaves - 1) / kSkinnyWaves;
+  // workgroups covering weight rows [pn0, pn1) (the whole matrix for a product)
+  const int wg0 = PARTIALS ? pn0 / rpw : 0;
+  const int nwg = PARTIALS ? (pn1 - 1) / rpw - wg0 + 1 : (n + rpw - 1) / rpw;
+  const bool two = rpw <= 64;
+#define BPW_SK(GPW_)                                                                              \
+  if (gpw == GPW_) {                                                                              \
+    if (two) t2_skinny_go<GPW_, 2, TOut, PARTIALS>(w, q, xs, m, rpw, y, pout, pm0, pm1, pn0, pn1, wg0, nwg, s); \
+    else t2_skinny_go<GPW_, 4, TOut, PARTIALS>(w, q, xs, m, rpw, y, pout, pm0, pm1, pn0, pn1, wg0, nwg, s);     \
+    return hipGetLastError();                                                                     \
+  }
+  BPW_SK(1) BPW_SK(2) BPW_SK(3) BPW_SK(4)
+#undef BPW_SK
+  return hipErrorInvalidValue;
+}
+
 template <typename TOut>
 hipError_t t2_dispatch(const bpw_weights& w, const int8_t* q, const float* xs, int m, TOut* y,
                        hipStream_t s) {
   if (t2_row_ok(m, w.k)) return t2_row<TOut, false>(w, q, xs, y, nullptr, 0, 0, s);
+  if (t2_skinny_ok(m, w.k)) return t2_skinny<TOut, false>(w, q, xs, m, y, nullptr, 0, 0, 0, 0, s);
   const int nw = waves_for(w.k / 128);
   const int fold = fold_for(m);
 #define BPW_T2(NW_, F_) \
@@ -666,7 +840,7 @@ hipError_t w4_dispatch(const bpw_weights& w, const uint16_t* x, bool bf, int m, 
 
 bool gemv_t2_fits(int64_t m, int64_t k) {
   if (m < 1 || m > 32) return false;
-  return t2_row_ok(m, k) || t2_lds(m, k) <= kLdsBudget;
+  return t2_row_ok(m, k) || t2_skinny_ok(m, k) || t2_lds(m, k) <= kLdsBudget;
 }
 
 bool gemv_w4_fits(int64_t m, int64_t k) {
@@ -690,6 +864,9 @@ hipError_t launch_gemv_t2_partials(const bpw_weights& w, const int8_t* q, int64_
   const int mi = static_cast<int>(m);
   if (t2_row_ok(m, k))   // the product for M = 1 runs the row kernel: verify that core
     return t2_row<float, true>(w, q, nullptr, nullptr, out, static_cast<int>(n0), static_cast<int>(n1), s);
+  if (t2_skinny_ok(m, k))   // and the skinny kernel for 2 <= M <= 32, K <= 4096
+    return t2_skinny<float, true>(w, q, nullptr, mi, static_cast<float*>(nullptr), out, static_cast<int>(m0),
+                                  static_cast<int>(m1), static_cast<int>(n0), static_cast<int>(n1), s);
   if (t2_lds(m, k) > kLdsBudget) return hipErrorInvalidValue;
   const int t0 = static_cast<int>(n0 / kRows), t1 = static_cast<int>((n1 - 1) / kRows);
   dim3 grid(t1 - t0 + 1);
