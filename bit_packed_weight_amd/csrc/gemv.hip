@@ -286,24 +286,22 @@ __global__ __launch_bounds__(NW * 64) void gemv_t2_kernel(
 // ---------------------------------------------------------------- ternary, 2 <= M <= 32, K <= 4096
 // Skinny products stream the weights like the M = 1 kernel but feed int8 MFMA.
 // One workgroup per CU owns a contiguous slice of weight rows (processed as
-// tiles of 32 rows); its 8 waves split K, GPW groups each. A wave keeps the
+// tiles of 32 rows); its NW waves split K, GPW groups each. A wave keeps the
 // A operands of its K slice (activations in plane order, all M rows) in
 // registers, loaded once, and streams its slice of each weight row straight
 // from HBM into B operands: lane (n, h) reads 16 bytes of row n per group, and
 // the two lanes of a row together cover its 32-byte group, so the wave reads
 // whole 128-byte lines. Codes are decoded signed (the {0xff, 0x00, 0x01, 0x02}
 // byte table), so each chain of four MFMAs is the exact partial P[m,n,g]. The
-// eight per-wave fp32 results of a tile are summed in a fixed order through LDS.
-constexpr int kSkinnyWaves = 8;
-
-template <int GPW, int MAXT, int FR, typename TOut, bool PARTIALS>
-__global__ __launch_bounds__(kSkinnyWaves * 64) void gemv_t2_skinny_kernel(
+// per-wave fp32 results of a tile are summed in a fixed order through LDS.
+template <int NW, int GPW, int MAXT, int FR, typename TOut, bool PARTIALS>
+__global__ __launch_bounds__(NW * 64) void gemv_t2_skinny_kernel(
     const uint8_t* __restrict__ codes, const __half* __restrict__ wscale,
     const int8_t* __restrict__ q, const float* __restrict__ x_scale, int M, int N, int K, int rpw,
     TOut* __restrict__ y, int32_t* __restrict__ pout, int pm0, int pm1, int pn0, int pn1, int wg0) {
   // FR: accumulator registers that can hold a token row < M (registers 0..7
   // hold rows 0..15, so 8 when M <= 16, else 16).
-  __shared__ float red[2 * kSkinnyWaves * FR * 64];       // [tile of a pair][wave][reg][lane]
+  extern __shared__ float red[];                           // [tile of a pair][wave][reg][lane]
   const int G = K >> 7, KB = K >> 2;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, h = lane >> 5;
@@ -311,49 +309,79 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void gemv_t2_skinny_kernel(
   const int r1 = min(r0 + rpw, N);
   const int gb = wave * GPW;
 
-  // Weights first (the long-latency loads): every tile and group of this wave.
-  v4u cw[MAXT][GPW];
-  float sc[MAXT][GPW];
-#pragma unroll
-  for (int t = 0; t < MAXT; ++t) {
-    const size_t row = static_cast<size_t>(min(r0 + 32 * t + n, N - 1));
-#pragma unroll
-    for (int u = 0; u < GPW; ++u) {
-      const int g = min(gb + u, G - 1);
-      cw[t][u] = *reinterpret_cast<const v4u*>(codes + row * KB + g * 32 + 16 * h);
-      sc[t][u] = __half2float(wscale[row * G + g]);
-    }
-  }
-  // A operands: token row m = n (clamped), half h of each group, plane order.
-  v4i a[GPW][4];
+  // Loads in the order they are consumed (the hardware counts them in issue
+  // order): activations, group scales and row scales first (small, mostly L2
+  // hits), then the code stream, tile by tile, group by group.
+  v4u ain[GPW][4];
   const int mA = min(n, M - 1);
 #pragma unroll
   for (int u = 0; u < GPW; ++u) {
     const int g = min(gb + u, G - 1);
     const v4u* src = reinterpret_cast<const v4u*>(q + static_cast<size_t>(mA) * K + g * 128 + 64 * h);
-    v4u in[4] = {src[0], src[1], src[2], src[3]};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ain[u][i] = src[i];
+  }
+  __half sc[MAXT][GPW];                                    // converted at use, not at load
+  const uint8_t* crow[MAXT];
+#pragma unroll
+  for (int t = 0; t < MAXT; ++t) {
+    // rows past this workgroup's share read its last row again (same address
+    // across the wave: no extra traffic) and are never stored
+    const size_t row = static_cast<size_t>(min(r0 + 32 * t + n, r1 - 1));
+    crow[t] = codes + row * KB + 16 * h;
+#pragma unroll
+    for (int u = 0; u < GPW; ++u) sc[t][u] = wscale[row * G + min(gb + u, G - 1)];
+  }
+  // Row scales of the outputs this thread stores (the same rows for every tile).
+  constexpr int OPT = (2 * FR + NW - 1) / NW;               // outputs per thread per tile pair
+  float xsv[OPT];
+  if (!PARTIALS) {
+#pragma unroll
+    for (int k = 0; k < OPT; ++k) {
+      const int rl = (tid + k * NW * 64) % (FR * 64);
+      xsv[k] = x_scale[min(d_row(rl >> 6, (rl & 63) >> 5), M - 1)];
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  v4u cw[MAXT][GPW];
+#pragma unroll
+  for (int t = 0; t < MAXT; ++t)
+#pragma unroll
+    for (int u = 0; u < GPW; ++u) {
+      cw[t][u] = *reinterpret_cast<const v4u*>(crow[t] + min(gb + u, G - 1) * 32);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  // Keep the transposes below the code loads (an empty asm on their inputs).
+#pragma unroll
+  for (int u = 0; u < GPW; ++u)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(ain[u][i]));
+  // A operands: token row m = n (clamped), half h of each group, plane order.
+  v4i a[GPW][4];
+#pragma unroll
+  for (int u = 0; u < GPW; ++u) {
     v4u o[4];
-    to_plane_order(in, o);
+    to_plane_order(ain[u], o);
 #pragma unroll
     for (int t = 0; t < 4; ++t) a[u][t] = __builtin_bit_cast(v4i, o[t]);
   }
-
-  const int ntile = (r1 - r0 + 31) >> 5;
   // Tiles in pairs: compute both, then one fixed-order reduction through LDS.
+  // Every tile is computed (no branch, so every load above stays hoisted);
+  // the stores drop rows past the workgroup's share.
 #pragma unroll
   for (int t0 = 0; t0 < MAXT; t0 += 2) {
-    if (t0 >= ntile) break;                                 // uniform over the workgroup
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const int t = t0 + tt;
-      if (t >= ntile) break;
       float acc[FR];
 #pragma unroll
       for (int r = 0; r < FR; ++r) acc[r] = 0.0f;
 #pragma unroll
       for (int u = 0; u < GPW; ++u) {
+        // Groups past the end (the last wave of a ragged K) run on clamped
+        // data and count for nothing: no branch, so the loads stay hoisted.
         const int g = gb + u;
-        if (g < G) {                                        // uniform over the wave
+        {
           const v4u c = cw[t][u];
           v16i d = {};
 #pragma unroll
@@ -367,30 +395,35 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void gemv_t2_skinny_kernel(
 #pragma unroll
             for (int r = 0; r < FR; ++r) {
               const int mm = d_row(r, h);
-              if (mm < M && mm >= pm0 && mm < pm1 && nn < r1 && nn >= pn0 && nn < pn1)
+              if (g < G && mm < M && mm >= pm0 && mm < pm1 && nn < r1 && nn >= pn0 && nn < pn1)
                 pout[(static_cast<size_t>(mm - pm0) * (pn1 - pn0) + (nn - pn0)) * G + g] = d[r];
             }
           } else {
+            const float sg = g < G ? __half2float(sc[t][u]) : 0.0f;
 #pragma unroll
-            for (int r = 0; r < FR; ++r) acc[r] = fmaf(static_cast<float>(d[r]), sc[t][u], acc[r]);
+            for (int r = 0; r < FR; ++r) acc[r] = fmaf(static_cast<float>(d[r]), sg, acc[r]);
           }
         }
       }
       if (!PARTIALS) {
 #pragma unroll
-        for (int r = 0; r < FR; ++r) red[((tt * kSkinnyWaves + wave) * FR + r) * 64 + lane] = acc[r];
+        for (int r = 0; r < FR; ++r) red[((tt * NW + wave) * FR + r) * 64 + lane] = acc[r];
       }
     }
     if (PARTIALS) continue;
     __syncthreads();
-    const int np = min(2, ntile - t0);
-    for (int o = tid; o < np * FR * 64; o += kSkinnyWaves * 64) {
+#pragma unroll
+    for (int k = 0; k < OPT; ++k) {
+      // The sum and the scaling run unconditionally (the row-scale load is
+      // then not sunk behind the barrier); only the store is guarded.
+      const int o0 = tid + k * NW * 64, o = min(o0, 2 * FR * 64 - 1);
       const int tt = o / (FR * 64), rl = o - tt * FR * 64, r = rl >> 6, l = rl & 63;
       float v = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kSkinnyWaves; ++w) v += red[((tt * kSkinnyWaves + w) * FR + r) * 64 + l];
+      for (int w = 0; w < NW; ++w) v += red[((tt * NW + w) * FR + r) * 64 + l];
+      v *= xsv[k];
       const int mm = d_row(r, l >> 5), nn = r0 + 32 * (t0 + tt) + (l & 31);
-      if (mm < M && nn < r1) store_out(y + static_cast<size_t>(mm) * N + nn, v * x_scale[mm]);
+      if (o0 == o && mm < M && nn < r1) store_out(y + static_cast<size_t>(mm) * N + nn, v);
     }
     __syncthreads();
   }
@@ -720,7 +753,7 @@ int cu_count() {
   return cached[dev];
 }
 
-bool t2_skinny_ok(int64_t m, int64_t k) { return m >= 2 && m <= 32 && k <= 128 * kSkinnyWaves * 4; }
+bool t2_skinny_ok(int64_t m, int64_t k) { return m >= 2 && m <= 32 && k <= 128 * 16 * 4; }
 
 // Rows per workgroup: the rows split evenly over the CUs, at least 16, at most
 // four 32-row tiles.
@@ -731,18 +764,23 @@ int skinny_rpw(int n) {
   return min(rpw, 128);
 }
 
-template <int GPW, int MAXT, typename TOut, bool PARTIALS>
+template <int NW, int GPW, int MAXT, typename TOut, bool PARTIALS>
 void t2_skinny_go(const bpw_weights& w, const int8_t* q, const float* xs, int m, int rpw, TOut* y,
                   int32_t* pout, int pm0, int pm1, int pn0, int pn1, int wg0, int nwg, hipStream_t s) {
   const uint8_t* codes = static_cast<const uint8_t*>(w.codes);
   const __half* sc = static_cast<const __half*>(w.scales);
   const int n = static_cast<int>(w.n), k = static_cast<int>(w.k);
-  if (m <= 16)
-    gemv_t2_skinny_kernel<GPW, MAXT, 8, TOut, PARTIALS><<<nwg, kSkinnyWaves * 64, 0, s>>>(
-        codes, sc, q, xs, m, n, k, rpw, y, pout, pm0, pm1, pn0, pn1, wg0);
-  else
-    gemv_t2_skinny_kernel<GPW, MAXT, 16, TOut, PARTIALS><<<nwg, kSkinnyWaves * 64, 0, s>>>(
-        codes, sc, q, xs, m, n, k, rpw, y, pout, pm0, pm1, pn0, pn1, wg0);
+  if (m <= 16) {
+    auto kern = gemv_t2_skinny_kernel<NW, GPW, MAXT, 8, TOut, PARTIALS>;
+    const size_t lds = 2ull * NW * 8 * 64 * 4;
+    allow_lds(kern, lds);
+    kern<<<nwg, NW * 64, lds, s>>>(codes, sc, q, xs, m, n, k, rpw, y, pout, pm0, pm1, pn0, pn1, wg0);
+  } else {
+    auto kern = gemv_t2_skinny_kernel<NW, GPW, MAXT, 16, TOut, PARTIALS>;
+    const size_t lds = 2ull * NW * 16 * 64 * 4;
+    allow_lds(kern, lds);
+    kern<<<nwg, NW * 64, lds, s>>>(codes, sc, q, xs, m, n, k, rpw, y, pout, pm0, pm1, pn0, pn1, wg0);
+  }
 }
 
 template <typename TOut, bool PARTIALS>
@@ -750,18 +788,20 @@ hipError_t t2_skinny(const bpw_weights& w, const int8_t* q, const float* xs, int
                      int32_t* pout, int pm0, int pm1, int pn0, int pn1, hipStream_t s) {
   const int n = static_cast<int>(w.n), g = static_cast<int>(w.k / 128);
   const int rpw = skinny_rpw(n);
-  const int gpw = (g + kSkinnyWaves - 1) / kSkinnyWaves;
+  // waves split K: 16 waves of up to 4 groups from 64 groups down, 8 below 16 groups
+  const int nw = g >= 16 ? 16 : 8;
+  const int gpw = (g + nw - 1) / nw;
   // workgroups covering weight rows [pn0, pn1) (the whole matrix for a product)
   const int wg0 = PARTIALS ? pn0 / rpw : 0;
   const int nwg = PARTIALS ? (pn1 - 1) / rpw - wg0 + 1 : (n + rpw - 1) / rpw;
   const bool two = rpw <= 64;
-#define BPW_SK(GPW_)                                                                              \
-  if (gpw == GPW_) {                                                                              \
-    if (two) t2_skinny_go<GPW_, 2, TOut, PARTIALS>(w, q, xs, m, rpw, y, pout, pm0, pm1, pn0, pn1, wg0, nwg, s); \
-    else t2_skinny_go<GPW_, 4, TOut, PARTIALS>(w, q, xs, m, rpw, y, pout, pm0, pm1, pn0, pn1, wg0, nwg, s);     \
+#define BPW_SK(NW_, GPW_)                                                                          \
+  if (nw == NW_ && gpw == GPW_) {                                                                 \
+    if (two) t2_skinny_go<NW_, GPW_, 2, TOut, PARTIALS>(w, q, xs, m, rpw, y, pout, pm0, pm1, pn0, pn1, wg0, nwg, s); \
+    else t2_skinny_go<NW_, GPW_, 4, TOut, PARTIALS>(w, q, xs, m, rpw, y, pout, pm0, pm1, pn0, pn1, wg0, nwg, s);     \
     return hipGetLastError();                                                                     \
   }
-  BPW_SK(1) BPW_SK(2) BPW_SK(3) BPW_SK(4)
+  BPW_SK(8, 1) BPW_SK(8, 2) BPW_SK(16, 1) BPW_SK(16, 2) BPW_SK(16, 3) BPW_SK(16, 4)
 #undef BPW_SK
   return hipErrorInvalidValue;
 }
@@ -864,7 +904,7 @@ hipError_t launch_gemv_t2_partials(const bpw_weights& w, const int8_t* q, int64_
   const int mi = static_cast<int>(m);
   if (t2_row_ok(m, k))   // the product for M = 1 runs the row kernel: verify that core
     return t2_row<float, true>(w, q, nullptr, nullptr, out, static_cast<int>(n0), static_cast<int>(n1), s);
-  if (t2_skinny_ok(m, k))   // and the skinny kernel for 2 <= M <= 32, K <= 4096
+  if (t2_skinny_ok(m, k))   // and the skinny kernel for 2 <= M <= 32, K <= 8192
     return t2_skinny<float, true>(w, q, nullptr, mi, static_cast<float*>(nullptr), out, static_cast<int>(m0),
                                   static_cast<int>(m1), static_cast<int>(n0), static_cast<int>(n1), s);
   if (t2_lds(m, k) > kLdsBudget) return hipErrorInvalidValue;
