@@ -39,9 +39,23 @@ __device__ __forceinline__ float wave_sum(float v) {
   v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
   v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
   v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  // Every row of 16 lanes now holds its row total; the four totals are read
+  // into scalar registers and added in the order (row0 + row1) + (row2 + row3).
+  const int vi = __builtin_bit_cast(int, v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(vi, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(vi, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(vi, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(vi, 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+// Weight codes are read once per call: streaming (non-temporal) loads, for
+// kernels whose load instructions take whole 128-byte lines. Where a line is
+// read in 32-byte pieces by several instructions, a streaming load lets the
+// cache drop it after the first piece and the rest is fetched again.
+template <typename T>
+__device__ __forceinline__ T load_stream(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
 }
 
 // ---------------------------------------------------------------- ternary, M = 1
@@ -68,7 +82,7 @@ __global__ __launch_bounds__(256) void gemv_t2_row_kernel(
     const size_t row = static_cast<size_t>(min(row0 + r, N - 1));
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      cw[r][c] = *reinterpret_cast<const v4u*>(codes + row * KB + c * 1024 + lane * 16);
+      cw[r][c] = load_stream<v4u>(codes + row * KB + c * 1024 + lane * 16);
       sv[r][c] = __half2float(wscale[row * G + 32 * c + (lane >> 1)]);
     }
   }
@@ -595,7 +609,7 @@ __global__ __launch_bounds__(256) void gemv_w4_row_kernel(
     const size_t row = static_cast<size_t>(min(row0 + r, N - 1));
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      cw[r][c] = *reinterpret_cast<const v2u*>(codes + row * KB + c * 512 + lane * 8);
+      cw[r][c] = load_stream<v2u>(codes + row * KB + c * 512 + lane * 8);
       const int g = 8 * c + (lane >> 3);
       const uint16_t sb = wscale[row * G + g];
       sv[r][c] = BF ? bf16_to_f32(sb) : __half2float(__builtin_bit_cast(__half, sb));
