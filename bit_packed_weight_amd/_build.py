@@ -23,7 +23,12 @@ SOURCES = ["api.cpp", "prepare.cpp", "quant.hip", "gemv.hip", "gemm_i8.hip", "ge
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-variable", "-Wno-unused-function",
           "-Wno-pass-failed", "-I", os.path.join(ROOT, "include")]
 # Packed fp32 instructions stay off: the compiler must not form v_pk_*_f32.
-DEVICE = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Kernel arguments are preloaded into SGPRs (up to 16 dwords), so a kernel
+# starts without waiting on argument loads; that wait is a visible part of a
+# few-microsecond GEMV. The code object keeps the ordinary loads for firmware
+# without preloading.
+DEVICE = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-kernarg-preload-count=16"]
 # The int8 GEMM folds every MFMA result with VALU instructions, which cannot
 # read AGPRs: its MFMA results must be allocated in VGPRs.
 EXTRA = {"gemm_i8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}

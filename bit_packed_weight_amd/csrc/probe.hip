@@ -21,7 +21,7 @@ __global__ __launch_bounds__(kThreads) void probe_read_kernel(const v4u* __restr
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
     const size_t idx = base + static_cast<size_t>(i) * kThreads + threadIdx.x;
-    v[i] = idx < n16 ? src[idx] : v4u{0, 0, 0, 0};
+    v[i] = idx < n16 ? __builtin_nontemporal_load(src + idx) : v4u{0, 0, 0, 0};   // streaming, as the GEMVs
   }
   uint32_t x = 0;
 #pragma unroll
