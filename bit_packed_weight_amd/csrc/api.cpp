@@ -65,7 +65,8 @@ int check_weights(const bpw_weights* w) {
     return fail(BPW_EUNSUPPORTED, "ternary weights carry fp16 scales only");
   if (!w->codes || !w->scales) return fail(BPW_EINVAL, "codes / scales plane is NULL");
   if (!aligned(w->codes, 16)) return fail(BPW_EALIGN, "codes plane must be 16-byte aligned");
-  if (!aligned(w->scales, 2)) return fail(BPW_EALIGN, "scales plane must be 2-byte aligned");
+  if (!aligned(w->scales, 16)) return fail(BPW_EALIGN, "scales plane must be 16-byte aligned");
+  if (w->zeros && !aligned(w->zeros, 16)) return fail(BPW_EALIGN, "zero-point plane must be 16-byte aligned");
   if ((w->fmt == BPW_INT4_ZP) != (w->zeros != nullptr))
     return fail(BPW_EINVAL, w->fmt == BPW_INT4_ZP ? "INT4_ZP needs a zero-point plane" : "zero-point plane given for a format without zero points");
   if (w->perm && w->fmt == BPW_TERNARY2)

@@ -326,14 +326,20 @@ __global__ __launch_bounds__(NW * 64) void gemv_t2_skinny_kernel(
   // Loads in the order they are consumed (the hardware counts them in issue
   // order): activations, group scales and row scales first (small, mostly L2
   // hits), then the code stream, tile by tile, group by group.
+  // (token rows n >= M are zero in A: their outputs are never stored)
   v4u ain[GPW][4];
-  const int mA = min(n, M - 1);
 #pragma unroll
-  for (int u = 0; u < GPW; ++u) {
-    const int g = min(gb + u, G - 1);
-    const v4u* src = reinterpret_cast<const v4u*>(q + static_cast<size_t>(mA) * K + g * 128 + 64 * h);
+  for (int u = 0; u < GPW; ++u)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ain[u][i] = src[i];
+    for (int i = 0; i < 4; ++i) ain[u][i] = v4u{0, 0, 0, 0};
+  if (n < M) {
+#pragma unroll
+    for (int u = 0; u < GPW; ++u) {
+      const int g = min(gb + u, G - 1);
+      const v4u* src = reinterpret_cast<const v4u*>(q + static_cast<size_t>(n) * K + g * 128 + 64 * h);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ain[u][i] = src[i];
+    }
   }
   __half sc[MAXT][GPW];                                    // converted at use, not at load
   const uint8_t* crow[MAXT];
@@ -581,6 +587,162 @@ __global__ __launch_bounds__(NW * 64) void gemv_w4_kernel(
       const int mm = d_row(r, h);
       if (mm < M && nn < N) store_out(y + static_cast<size_t>(mm) * N + nn, v);
     }
+  }
+}
+
+// ---------------------------------------------------------------- 4-bit, 2 <= M <= 16
+// Streaming form for the decode shapes: one workgroup per CU takes rpw weight
+// rows (16-row tiles) over the whole K; its NW waves split the groups, GPW
+// each. Every load is issued before the first MFMA: scales and zeros, the
+// code stream tile by tile, then the activations. MFMA f32_16x16x32 (f16/bf16):
+// lane (n, j) = (l % 16, l / 16) holds token row n for A and weight row n of
+// the tile for B, columns 32j..32j+31 of each 128-group (16 code bytes, one
+// 8-column chunk per MFMA; the activations are permuted inside each chunk to
+// the dequantiser's order). The group result is folded with its scale in
+// fp32; the waves' sums meet in LDS in a fixed order.
+template <int GPW, int MAXT, bool BF, bool ZP, typename TOut>
+__global__ __launch_bounds__(512) void gemv_w4_skinny_kernel(
+    const uint8_t* __restrict__ codes, const uint16_t* __restrict__ wscale,
+    const uint8_t* __restrict__ zeros, const uint16_t* __restrict__ x, int M, int N, int K, int rpw,
+    TOut* __restrict__ y) {
+  extern __shared__ float red4[];                          // [tile of a pair][wave][reg][lane]
+  const int NW = blockDim.x >> 6;
+  const int G = K >> 7, KB = K >> 1, ZB = (G + 1) >> 1;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, j = lane >> 4;
+  const int r0 = blockIdx.x * rpw;
+  const int r1 = min(r0 + rpw, N);
+  const int gb = wave * GPW;
+
+  // Scales and zero bytes of this wave's groups for the workgroup's rows: a
+  // (rows x GPW) block per wave, element e = local row e / GPW, group
+  // gb + e % GPW, loaded with coalesced small loads (SPL per lane), put in the
+  // wave's own LDS slice once the code loads are out and read back in MFMA
+  // layout. Only the wave itself touches its slice: no workgroup barrier.
+  constexpr int BLK = MAXT * 16 * GPW, SPL = (BLK + 63) / 64;
+  uint16_t* ssc = reinterpret_cast<uint16_t*>(red4 + 2 * NW * 4 * 64) + wave * BLK;
+  uint8_t* szr = reinterpret_cast<uint8_t*>(reinterpret_cast<uint16_t*>(red4 + 2 * NW * 4 * 64) + NW * BLK) + wave * BLK;
+  const int nel = (r1 - r0) * GPW;
+  uint16_t sst[SPL];
+  uint8_t zst[SPL];
+#pragma unroll
+  for (int c = 0; c < SPL; ++c) {
+    const int e = lane + 64 * c, rr = e / GPW, gc = min(gb + e - rr * GPW, G - 1);
+    const size_t row = static_cast<size_t>(r0 + rr);
+    sst[c] = e < nel ? wscale[row * G + gc] : 0;
+    zst[c] = ZP && e < nel ? zeros[row * ZB + (gc >> 1)] : 0;
+  }
+  const uint8_t* crow[MAXT];
+  int lrow[MAXT];                                          // row within the workgroup's share
+#pragma unroll
+  for (int t = 0; t < MAXT; ++t) {
+    // rows past this workgroup's share read its last row again (same address
+    // across the wave) and are never stored
+    lrow[t] = min(16 * t + n, r1 - r0 - 1);
+    crow[t] = codes + static_cast<size_t>(r0 + lrow[t]) * KB + 16 * j;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  v4u cw[MAXT][GPW];
+#pragma unroll
+  for (int t = 0; t < MAXT; ++t)
+#pragma unroll
+    for (int u = 0; u < GPW; ++u) {
+      cw[t][u] = *reinterpret_cast<const v4u*>(crow[t] + min(gb + u, G - 1) * 64);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  // Activations of token row n only where n < M (the other A rows are zero:
+  // their outputs are never stored). Issued after the code stream: measured
+  // a little faster than ahead of it.
+  v4u ain[GPW][4];
+#pragma unroll
+  for (int u = 0; u < GPW; ++u)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ain[u][i] = v4u{0, 0, 0, 0};
+  if (n < M) {
+#pragma unroll
+    for (int u = 0; u < GPW; ++u) {
+      const int g = min(gb + u, G - 1);
+      const v4u* src = reinterpret_cast<const v4u*>(x + static_cast<size_t>(n) * K + g * 128 + 32 * j);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ain[u][i] = src[i];
+    }
+  }
+  // A operands: each 8-column chunk in the order [0, 4, 1, 5, 2, 6, 3, 7].
+  v4u a[GPW][4];
+#pragma unroll
+  for (int u = 0; u < GPW; ++u)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const v4u v = ain[u][i];
+      a[u][i] = v4u{perm_b32(v.z, v.x, 0x05040100u), perm_b32(v.z, v.x, 0x07060302u),
+                    perm_b32(v.w, v.y, 0x05040100u), perm_b32(v.w, v.y, 0x07060302u)};
+    }
+#pragma unroll
+  for (int c = 0; c < SPL; ++c) {
+    const int e = lane + 64 * c;
+    if (e < nel) {
+      ssc[e] = sst[c];
+      if (ZP) szr[e] = zst[c];
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // This lane's scales and zero points, read back in one batch.
+  uint16_t sreg[MAXT][GPW];
+  int zreg[MAXT][GPW];
+#pragma unroll
+  for (int t = 0; t < MAXT; ++t)
+#pragma unroll
+    for (int u = 0; u < GPW; ++u) {
+      const int gc = min(gb + u, G - 1);
+      sreg[t][u] = ssc[lrow[t] * GPW + u];
+      zreg[t][u] = ZP ? (szr[lrow[t] * GPW + u] >> (4 * (gc & 1))) & 15 : 8;
+    }
+  // Tiles in pairs: compute both, then one fixed-order reduction through LDS.
+  // Every tile is computed (no branch, so the loads above stay hoisted).
+#pragma unroll
+  for (int t0 = 0; t0 < MAXT; t0 += 2) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int t = t0 + tt;
+      float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int u = 0; u < GPW; ++u) {
+        const int g = gb + u;
+        const int z = zreg[t][u];
+        const uint32_t wv[4] = {cw[t][u].x, cw[t][u].y, cw[t][u].z, cw[t][u].w};
+        v4f d = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if (BF) {
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[u][c]),
+                                                        dequant_w4_bf16(wv[c], static_cast<float>(z)), d, 0, 0, 0);
+          } else {
+            const uint32_t mz = 0xE400u | static_cast<uint32_t>(z);   // fp16 -(1024 + z)
+            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a[u][c]),
+                                                       dequant_w4_f16(wv[c], mz | (mz << 16)), d, 0, 0, 0);
+          }
+        }
+        // groups past the end (ragged K over the waves) count for nothing
+        const uint16_t sb = sreg[t][u];
+        const float sg = g < G ? (BF ? bf16_to_f32(sb) : __half2float(__builtin_bit_cast(__half, sb))) : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = fmaf(d[i], sg, acc[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red4[((tt * NW + wave) * 4 + i) * 64 + lane] = acc[i];
+    }
+    __syncthreads();
+    // 2 tiles x 4 registers x 64 lanes = 512 outputs (16 tokens x 16 rows each)
+    for (int o = tid; o < 512; o += NW * 64) {
+      const int tt = o >> 8, i = (o >> 6) & 3, l = o & 63;
+      float v = 0.0f;
+      for (int w = 0; w < NW; ++w) v += red4[((tt * NW + w) * 4 + i) * 64 + l];
+      const int mm = 4 * (l >> 4) + i, nn = r0 + 16 * (t0 + tt) + (l & 15);
+      if (mm < M && nn < r1) store_out(y + static_cast<size_t>(mm) * N + nn, v);
+    }
+    __syncthreads();
   }
 }
 
@@ -849,6 +1011,41 @@ hipError_t w4_go(const bpw_weights& w, const uint16_t* x, int m, TOut* y, hipStr
   return hipGetLastError();
 }
 
+bool w4_skinny_ok(int64_t m, int64_t k) { return m >= 2 && m <= 16 && k / 128 >= 16 && k / 128 <= 48; }
+
+template <int GPW, int MAXT, bool BF, bool ZP, typename TOut>
+void w4_skinny_go(const bpw_weights& w, const uint16_t* x, int m, int rpw, int nw, TOut* y, hipStream_t s) {
+  const int n = static_cast<int>(w.n), k = static_cast<int>(w.k);
+  auto kern = gemv_w4_skinny_kernel<GPW, MAXT, BF, ZP, TOut>;
+  const size_t lds = 2ull * nw * 4 * 64 * 4 + 3ull * nw * (MAXT * 16 * GPW);
+  allow_lds(kern, lds);
+  kern<<<(n + rpw - 1) / rpw, nw * 64, lds, s>>>(static_cast<const uint8_t*>(w.codes),
+                                                 static_cast<const uint16_t*>(w.scales),
+                                                 static_cast<const uint8_t*>(w.zeros), x, m, n, k, rpw, y);
+}
+
+template <bool BF, bool ZP, typename TOut>
+hipError_t w4_skinny(const bpw_weights& w, const uint16_t* x, int m, TOut* y, hipStream_t s) {
+  const int n = static_cast<int>(w.n), g = static_cast<int>(w.k / 128);
+  // rows split evenly over the CUs (multiple of 8, 16..64: at most four tiles)
+  const int cus = cu_count();
+  int rpw = (n + cus - 1) / cus;
+  rpw = min(64, max(16, (rpw + 7) & ~7));
+  // up to 8 waves of 4..6 groups (16 <= groups <= 48)
+  const int nw = min(8, (g + 3) / 4);
+  const int gpw = (g + nw - 1) / nw;
+  const bool two = rpw <= 32;
+#define BPW_W4S(GPW_)                                                                    \
+  if (gpw == GPW_) {                                                                    \
+    if (two) w4_skinny_go<GPW_, 2, BF, ZP>(w, x, m, rpw, nw, y, s);                     \
+    else w4_skinny_go<GPW_, 4, BF, ZP>(w, x, m, rpw, nw, y, s);                         \
+    return hipGetLastError();                                                           \
+  }
+  BPW_W4S(4) BPW_W4S(5) BPW_W4S(6)
+#undef BPW_W4S
+  return hipErrorInvalidValue;
+}
+
 template <int CH, bool BF, bool ZP, typename TOut>
 void w4_row_go(const bpw_weights& w, const uint16_t* x, TOut* y, hipStream_t s) {
   const int n = static_cast<int>(w.n), k = static_cast<int>(w.k);
@@ -872,6 +1069,7 @@ hipError_t w4_dispatch_f(const bpw_weights& w, const uint16_t* x, int m, TOut* y
     }
     return hipGetLastError();
   }
+  if (w4_skinny_ok(m, w.k)) return w4_skinny<BF, ZP>(w, x, m, y, s);
   const int nw = waves_for(w.k / 128);
   const int fold = fold_for(m);
 #define BPW_W4(NW_, F_) \
@@ -898,7 +1096,7 @@ bool gemv_t2_fits(int64_t m, int64_t k) {
 }
 
 bool gemv_w4_fits(int64_t m, int64_t k) {
-  return m >= 1 && m <= 32 && (w4_row_ok(m, k) || static_cast<size_t>(m) * k * 2 <= kLdsBudget);
+  return m >= 1 && m <= 32 && (w4_row_ok(m, k) || w4_skinny_ok(m, k) || static_cast<size_t>(m) * k * 2 <= kLdsBudget);
 }
 
 hipError_t launch_gemv_t2(const bpw_weights& w, const int8_t* q, const float* x_scale, int64_t m,

@@ -166,7 +166,9 @@ def w4_reference(w: synth.Workload, rounded: bool):
                                                    ("int4_sym", "bf16", False), ("int4_sym", "f16", False),
                                                    ("int4_zp", "bf16", True)])
 @pytest.mark.parametrize("m,k,n", [(1, 640, 333), (1, 2048, 301), (1, 8192, 66), (3, 128, 64), (8, 5120, 200),
-                                   (16, 1024, 97), (32, 256, 130)])
+                                   (16, 1024, 97), (32, 256, 130),
+                                   # streaming skinny kernel: 16..48 groups, 4..6 per wave, ragged waves and tiles
+                                   (2, 2048, 1000), (16, 6144, 777), (5, 4224, 3000), (12, 2560, 9000)])
 def test_gemv_w4_parity(fmt, x_dtype, act_order, m, k, n):
     w = w4_case(fmt, m, k, n, 300 + m + k + n, act_order, x_dtype)
     pw = prepare(w)
