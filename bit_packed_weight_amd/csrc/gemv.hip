@@ -297,7 +297,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_t2_kernel(
   }
 }
 
-// ---------------------------------------------------------------- ternary, 2 <= M <= 32, K <= 4096
+// ---------------------------------------------------------------- ternary, 2 <= M <= 32, K <= 8192
 // Skinny products stream the weights like the M = 1 kernel but feed int8 MFMA.
 // One workgroup per CU owns a contiguous slice of weight rows (processed as
 // tiles of 32 rows); its NW waves split K, GPW groups each. A wave keeps the
