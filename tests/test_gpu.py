@@ -85,7 +85,9 @@ def run_ternary(w: synth.Workload, entry: str):
 
 
 @pytest.mark.parametrize("m,k,n", [(1, 512, 256), (1, 4096, 1000), (2, 640, 333), (4, 128, 64),
-                                   (7, 1024, 520), (16, 4096, 300), (32, 256, 97), (1, 8192, 130)])
+                                   (7, 1024, 520), (16, 4096, 300), (32, 256, 97), (1, 8192, 130),
+                                   # skinny kernel: 3 and 4 groups per wave, four-tile shares, ragged tiles
+                                   (32, 8192, 3000), (9, 3072, 20000), (24, 6144, 9000)])
 @pytest.mark.parametrize("out", ["f32", "f16", "bf16"])
 def test_gemv_ternary_parity(m, k, n, out):
     w = ternary_case(m, k, n, 100 + m + k + n, out)
@@ -103,7 +105,8 @@ def test_gemm_ternary_parity(m, k, n):
 @pytest.mark.parametrize("path", [bpw.PATH_GEMV, bpw.PATH_GEMM])
 @pytest.mark.parametrize("m,k,n,win", [(3, 256, 70, (0, 3, 0, 70)), (32, 512, 200, (5, 29, 33, 170)),
                                        (1, 128, 40, (0, 1, 7, 9)), (1, 4096, 77, (0, 1, 3, 70)),
-                                       (1, 8192, 9, (0, 1, 0, 9))])
+                                       (1, 8192, 9, (0, 1, 0, 9)), (16, 8192, 600, (3, 14, 100, 580)),
+                                       (12, 3072, 20000, (0, 12, 9000, 9777))])
 def test_partials_bit_exact(path, m, k, n, win):
     # stress inputs: full int8 range and every 2-bit code including 3
     rng = np.random.default_rng(m + k + n)
@@ -175,6 +178,17 @@ def test_gemv_w4_parity(fmt, x_dtype, act_order, m, k, n):
     y = bpw.gemv_packed(pw, to_dev(w.x, x_dtype))
     torch.cuda.synchronize()
     assert_close(host(y), w4_reference(w, rounded=False), x_dtype, f"gemv {fmt} {x_dtype} m={m} k={k} n={n}")
+
+
+@pytest.mark.parametrize("x_dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("m,k,n", [(1, 5120, 700), (8, 5120, 700), (3, 2048, 5000)])
+def test_gemv_w4_f32_out(x_dtype, m, k, n):
+    w = w4_case("int4_zp", m, k, n, 500 + m + k + n, True, x_dtype)
+    pw = prepare(w)
+    y = bpw.gemv_packed(pw, to_dev(w.x, x_dtype), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert y.dtype == torch.float32
+    assert_close(host(y), w4_reference(w, rounded=False), "f32", f"gemv int4_zp {x_dtype} f32 out m={m} k={k} n={n}")
 
 
 @pytest.mark.parametrize("fmt,x_dtype,act_order", [("int4_sym", "bf16", False), ("int4_zp", "f16", True),
