@@ -22,8 +22,8 @@ LIB_PATH = os.path.join(_HERE, "libbpw.so")
 OK, EINVAL, ESHAPE, EALIGN, EGIDX, EUNSUPPORTED, EHIP = range(7)
 # weight formats
 TERNARY2, INT4_SYM, INT4_ZP = 1, 2, 3
-# element types
-F32, F16, BF16, I8, I32 = 0, 1, 2, 3, 4
+# element types (I8G: int8 activations with one scale per (row, 128-group))
+F32, F16, BF16, I8, I32, I8G = 0, 1, 2, 3, 4, 5
 # prepare sources
 SRC_PQ2_BLOCKS, SRC_PLANES, SRC_CODES_U8 = 1, 2, 3
 # partial-sum cores / workspace entries
@@ -68,6 +68,8 @@ EXPORTS = {
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "bpw_quantize_rows": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "bpw_quantize_groups": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "bpw_workspace_size": (ctypes.c_int, [ctypes.POINTER(BpwWeights), ctypes.c_int64, ctypes.c_int,
                                           ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]),
     "bpw_gemv_packed": (ctypes.c_int, [ctypes.POINTER(BpwWeights), ctypes.c_void_p, ctypes.c_int,
@@ -257,6 +259,20 @@ def quantize_rows(x, q=None, x_scale=None):
     return q, x_scale
 
 
+def quantize_groups(x, q=None, x_scale=None):
+    """int8 group quantiser on the GPU: returns (q [M,K] int8, x_scale [M,K/128] fp32)."""
+    torch = _torch()
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [M, K] tensor")
+    m, k = x.shape
+    q = torch.empty((m, k), dtype=torch.int8, device=x.device) if q is None else q
+    if x_scale is None:
+        x_scale = torch.empty((m, k // 128), dtype=torch.float32, device=x.device)
+    _check(lib().bpw_quantize_groups(_ptr(x), dtype_code(x.dtype), m, k, _ptr(q), _ptr(x_scale),
+                                     _stream(x.device)))
+    return q, x_scale
+
+
 def workspace_size(w: PackedWeights, m: int, x_dtype: int, entry: int) -> int:
     out = ctypes.c_size_t()
     st = w.struct()
@@ -280,8 +296,10 @@ def _product(entry: int, w: PackedWeights, x, x_scale=None, out_dtype=None, out=
         raise ValueError("x must be a contiguous [M, K] tensor")
     m = x.shape[0]
     xd = dtype_code(x.dtype)
+    if xd == I8 and x_scale is not None and x_scale.dim() == 2:
+        xd = I8G                                   # one scale per (row, 128-group)
     if out is None:
-        out_dtype = out_dtype if out_dtype is not None else (torch.float16 if xd == I8 else x.dtype)
+        out_dtype = out_dtype if out_dtype is not None else (torch.float16 if xd in (I8, I8G) else x.dtype)
         out = torch.empty((m, w.n), dtype=out_dtype, device=x.device)
     ws, ws_bytes = _workspace(w, m, xd, entry, x.device, workspace)
     st = w.struct()

@@ -82,9 +82,11 @@ int check_product(const bpw_weights* w, const void* x, int x_dtype, const float*
   if (!x || !y) return fail(BPW_EINVAL, "x / y is NULL");
   if (!is_out_dtype(y_dtype)) return fail(BPW_EUNSUPPORTED, "output dtype %d unsupported (F32, F16, BF16)", y_dtype);
   if (w->fmt == BPW_TERNARY2) {
-    if (x_dtype != BPW_I8)
+    if (x_dtype != BPW_I8 && x_dtype != BPW_I8G)
       return fail(BPW_EUNSUPPORTED, "ternary weights take int8 activations (x_dtype %d given)", x_dtype);
-    if (!x_scale) return fail(BPW_EINVAL, "int8 activations need x_scale [M]");
+    if (!x_scale) return fail(BPW_EINVAL, x_dtype == BPW_I8 ? "int8 activations need x_scale [M]"
+                                                            : "int8 activations need x_scale [M][K/128]");
+    if (!aligned(x_scale, 4)) return fail(BPW_EALIGN, "x_scale must be 4-byte aligned");
   } else {
     if (x_dtype != BPW_F16 && x_dtype != BPW_BF16)
       return fail(BPW_EUNSUPPORTED, "4-bit weights take fp16 or bf16 activations (x_dtype %d given)", x_dtype);
@@ -97,18 +99,19 @@ int check_product(const bpw_weights* w, const void* x, int x_dtype, const float*
   return BPW_OK;
 }
 
-// Workspace bytes for (weights, M, entry).
-size_t workspace_need(const bpw_weights* w, int64_t m, int entry) {
+// Workspace bytes for (weights, M, activation type, entry).
+size_t workspace_need(const bpw_weights* w, int64_t m, int x_dtype, int entry) {
   const size_t mk = static_cast<size_t>(m) * static_cast<size_t>(w->k);
   if (w->fmt == BPW_TERNARY2) {
+    if (x_dtype == BPW_I8G) return 0;                // decode kernels only, no staging
     if (entry == BPW_PATH_GEMV && gemv_t2_fits(m, w->k)) return 0;
     return round_up(mk);                       // plane-ordered int8 activations
   }
   return w->perm ? round_up(mk * 2) : 0;       // gathered 16-bit activations
 }
 
-int check_workspace(const bpw_weights* w, int64_t m, int entry, void* ws, size_t ws_bytes) {
-  const size_t need = workspace_need(w, m, entry);
+int check_workspace(const bpw_weights* w, int64_t m, int x_dtype, int entry, void* ws, size_t ws_bytes) {
+  const size_t need = workspace_need(w, m, x_dtype, entry);
   if (need == 0) return BPW_OK;
   if (!ws) return fail(BPW_EINVAL, "this call needs a %zu-byte device workspace", need);
   if (!aligned(ws, kWsAlign)) return fail(BPW_EALIGN, "workspace must be 256-byte aligned");
@@ -120,12 +123,23 @@ int run_product(bool gemv, const bpw_weights* w, const void* x, int x_dtype, con
                 int64_t m, void* y, int y_dtype, void* ws, size_t ws_bytes, void* stream) {
   const int entry = gemv ? BPW_PATH_GEMV : BPW_PATH_GEMM;
   if (int st = check_product(w, x, x_dtype, x_scale, m, y, y_dtype)) return st;
-  if (int st = check_workspace(w, m, entry, ws, ws_bytes)) return st;
+  if (x_dtype == BPW_I8G) {
+    // "Kernel experiments", Test 6: one activation scale per 128-group, folded
+    // with the weight scale of the same group. Decode kernels only.
+    if (!gemv)
+      return fail(BPW_EUNSUPPORTED, "per-group activation scales (BPW_I8G) are supported by bpw_gemv_packed only");
+    if (!gemv_t2_group_fits(m, w->k))
+      return fail(BPW_EUNSUPPORTED, "per-group activation scales need M <= 32 and K <= 8192, or M = 1 and "
+                                    "K a multiple of 4096 up to 16384 (M=%lld, K=%lld)", (long long)m, (long long)w->k);
+  }
+  if (int st = check_workspace(w, m, x_dtype, entry, ws, ws_bytes)) return st;
   if (int st = check_device()) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (w->fmt == BPW_TERNARY2) {
     const int8_t* q = static_cast<const int8_t*>(x);
-    if (gemv && gemv_t2_fits(m, w->k)) return hip_status(launch_gemv_t2(*w, q, x_scale, m, y, y_dtype, s), "ternary GEMV launch");
+    if (x_dtype == BPW_I8G)
+      return hip_status(launch_gemv_t2(*w, q, x_scale, m, y, y_dtype, true, s), "ternary GEMV launch");
+    if (gemv && gemv_t2_fits(m, w->k)) return hip_status(launch_gemv_t2(*w, q, x_scale, m, y, y_dtype, false, s), "ternary GEMV launch");
     int8_t* qp = static_cast<int8_t*>(ws);
     if (int st = hip_status(launch_int8_planes(q, m, w->k, qp, s), "int8 plane reorder launch")) return st;
     return hip_status(launch_gemm_t2(*w, qp, x_scale, m, y, y_dtype, s), "ternary GEMM launch");
@@ -180,14 +194,28 @@ extern "C" int bpw_quantize_rows(const void* x, int x_dtype, int64_t m, int64_t 
                     "quantiser launch");
 }
 
+extern "C" int bpw_quantize_groups(const void* x, int x_dtype, int64_t m, int64_t k, int8_t* q,
+                                   float* x_scale, void* stream) {
+  if (!x || !q || !x_scale) return fail(BPW_EINVAL, "x / q / x_scale is NULL");
+  if (x_dtype != BPW_F32 && x_dtype != BPW_F16 && x_dtype != BPW_BF16)
+    return fail(BPW_EUNSUPPORTED, "quantiser input dtype %d unsupported (F32, F16, BF16)", x_dtype);
+  if (m < 1 || m > (int64_t(1) << 30) || k < 128 || k > (int64_t(1) << 30) || k % 128 != 0)
+    return fail(BPW_ESHAPE, "M=%lld must be in 1..2^30 and K=%lld a multiple of 128 up to 2^30", (long long)m,
+                (long long)k);
+  if (!aligned(x, x_dtype == BPW_F32 ? 4 : 2) || !aligned(q, 16) || !aligned(x_scale, 4))
+    return fail(BPW_EALIGN, "x / q / x_scale misaligned (q must be 16-byte aligned)");
+  if (int st = check_device()) return st;
+  return hip_status(launch_quantize_groups(x, x_dtype, m, k, q, x_scale, static_cast<hipStream_t>(stream)),
+                    "group quantiser launch");
+}
+
 extern "C" int bpw_workspace_size(const bpw_weights* w, int64_t m, int x_dtype, int entry,
                                   size_t* bytes) {
   if (int st = check_weights(w)) return st;
   if (!bytes) return fail(BPW_EINVAL, "bytes is NULL");
   if (entry != BPW_PATH_GEMV && entry != BPW_PATH_GEMM) return fail(BPW_EINVAL, "unknown entry %d", entry);
   if (m < 1 || m > (int64_t(1) << 30)) return fail(BPW_ESHAPE, "M=%lld outside 1..2^30", (long long)m);
-  (void)x_dtype;
-  *bytes = workspace_need(w, m, entry);
+  *bytes = workspace_need(w, m, x_dtype, entry);
   return ok();
 }
 
@@ -219,7 +247,7 @@ extern "C" int bpw_partials(const bpw_weights* w, const int8_t* q, int64_t m, in
   if (path == BPW_PATH_GEMV && !gemv_t2_fits(m, w->k))
     return fail(BPW_ESHAPE, "the GEMV core takes M <= 32 with M*K within its LDS budget");
   if (path == BPW_PATH_GEMM) {
-    if (int st = check_workspace(w, m, BPW_PATH_GEMM, workspace, workspace_bytes)) return st;
+    if (int st = check_workspace(w, m, BPW_I8, BPW_PATH_GEMM, workspace, workspace_bytes)) return st;
   }
   if (int st = check_device()) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);

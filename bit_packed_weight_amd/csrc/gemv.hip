@@ -65,8 +65,9 @@ __device__ __forceinline__ T load_stream(const uint8_t* p) {
 // activation bytes sit in registers in plane order; each code plane of a packed
 // word is one v_dot4 against the matching activation word; the code - 1 offset
 // is minus the half-group sum of q; the half-group partial is folded with its
-// fp32 scale and the row total is a wave reduction.
-template <int R, int CH, typename TOut, bool PARTIALS>
+// fp32 scale and the row total is a wave reduction. GS: x_scale holds one
+// scale per 128-group ([K/128]) and joins the weight scale in the fold.
+template <int R, int CH, typename TOut, bool PARTIALS, bool GS>
 __global__ __launch_bounds__(256) void gemv_t2_row_kernel(
     const uint8_t* __restrict__ codes, const __half* __restrict__ wscale,
     const int8_t* __restrict__ q, const float* __restrict__ x_scale, int N, int K,
@@ -77,6 +78,9 @@ __global__ __launch_bounds__(256) void gemv_t2_row_kernel(
   const int KB = K >> 2, G = K >> 7;
   v4u cw[R][CH];
   float sv[R][CH];
+  float xg[CH];                                 // GS: this lane's activation group scale per chunk
+#pragma unroll
+  for (int c = 0; c < CH; ++c) xg[c] = GS ? x_scale[32 * c + (lane >> 1)] : 1.0f;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const size_t row = static_cast<size_t>(min(row0 + r, N - 1));
@@ -127,12 +131,12 @@ __global__ __launch_bounds__(256) void gemv_t2_row_kernel(
         if ((lane & 1) == 0 && row < N && row >= pn0 && row < pn1)
           pout[static_cast<size_t>(row - pn0) * G + 32 * c + (lane >> 1)] = pg;
       } else {
-        acc[r] = fmaf(static_cast<float>(p), sv[r][c], acc[r]);
+        acc[r] = fmaf(static_cast<float>(p), GS ? sv[r][c] * xg[c] : sv[r][c], acc[r]);
       }
     }
   }
   if (PARTIALS) return;
-  const float xs = x_scale[0];
+  const float xs = GS ? 1.0f : x_scale[0];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const float v = wave_sum(acc[r]);
@@ -308,13 +312,14 @@ __global__ __launch_bounds__(NW * 64) void gemv_t2_kernel(
 // whole 128-byte lines. Codes are decoded signed (the {0xff, 0x00, 0x01, 0x02}
 // byte table), so each chain of four MFMAs is the exact partial P[m,n,g]. The
 // per-wave fp32 results of a tile are summed in a fixed order through LDS.
-template <int NW, int GPW, int MAXT, int FR, typename TOut, bool PARTIALS>
+template <int NW, int GPW, int MAXT, int FR, typename TOut, bool PARTIALS, bool GS>
 __global__ __launch_bounds__(NW * 64) void gemv_t2_skinny_kernel(
     const uint8_t* __restrict__ codes, const __half* __restrict__ wscale,
     const int8_t* __restrict__ q, const float* __restrict__ x_scale, int M, int N, int K, int rpw,
     TOut* __restrict__ y, int32_t* __restrict__ pout, int pm0, int pm1, int pn0, int pn1, int wg0) {
   // FR: accumulator registers that can hold a token row < M (registers 0..7
-  // hold rows 0..15, so 8 when M <= 16, else 16).
+  // hold rows 0..15, so 8 when M <= 16, else 16). GS: x_scale holds one scale
+  // per (row, 128-group), [M][K/128], and joins the weight scale in the fold.
   extern __shared__ float red[];                           // [tile of a pair][wave][reg][lane]
   const int G = K >> 7, KB = K >> 2;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -352,10 +357,23 @@ __global__ __launch_bounds__(NW * 64) void gemv_t2_skinny_kernel(
 #pragma unroll
     for (int u = 0; u < GPW; ++u) sc[t][u] = wscale[row * G + min(gb + u, G - 1)];
   }
+  // GS: the activation group scales of this wave's groups for 32 token rows,
+  // [u][m] in the wave's own LDS slice after the reduction area (loaded here,
+  // stored once the code loads are out).
+  constexpr int XPL = (GPW * 32 + 63) / 64;
+  float* xsl = red + 2 * NW * FR * 64 + wave * (GPW * 32);
+  float xst[XPL];
+  if (GS) {
+#pragma unroll
+    for (int c = 0; c < XPL; ++c) {
+      const int e = min(lane + 64 * c, GPW * 32 - 1), u = e >> 5, m = e & 31;
+      xst[c] = x_scale[min(m, M - 1) * G + min(gb + u, G - 1)];
+    }
+  }
   // Row scales of the outputs this thread stores (the same rows for every tile).
   constexpr int OPT = (2 * FR + NW - 1) / NW;               // outputs per thread per tile pair
   float xsv[OPT];
-  if (!PARTIALS) {
+  if (!PARTIALS && !GS) {
 #pragma unroll
     for (int k = 0; k < OPT; ++k) {
       const int rl = (tid + k * NW * 64) % (FR * 64);
@@ -371,6 +389,14 @@ __global__ __launch_bounds__(NW * 64) void gemv_t2_skinny_kernel(
       cw[t][u] = *reinterpret_cast<const v4u*>(crow[t] + min(gb + u, G - 1) * 32);
       __builtin_amdgcn_sched_barrier(0);
     }
+  if (GS) {
+#pragma unroll
+    for (int c = 0; c < XPL; ++c)
+      if (lane + 64 * c < GPW * 32) xsl[lane + 64 * c] = xst[c];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
   // Keep the transposes below the code loads (an empty asm on their inputs).
 #pragma unroll
   for (int u = 0; u < GPW; ++u)
@@ -421,7 +447,8 @@ __global__ __launch_bounds__(NW * 64) void gemv_t2_skinny_kernel(
           } else {
             const float sg = g < G ? __half2float(sc[t][u]) : 0.0f;
 #pragma unroll
-            for (int r = 0; r < FR; ++r) acc[r] = fmaf(static_cast<float>(d[r]), sg, acc[r]);
+            for (int r = 0; r < FR; ++r)
+              acc[r] = fmaf(static_cast<float>(d[r]), GS ? sg * xsl[u * 32 + d_row(r, h)] : sg, acc[r]);
           }
         }
       }
@@ -441,7 +468,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_t2_skinny_kernel(
       float v = 0.0f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) v += red[((tt * NW + w) * FR + r) * 64 + l];
-      v *= xsv[k];
+      if (!GS) v *= xsv[k];
       const int mm = d_row(r, l >> 5), nn = r0 + 32 * (t0 + tt) + (l & 31);
       if (o0 == o && mm < M && nn < r1) store_out(y + static_cast<size_t>(mm) * N + nn, v);
     }
@@ -882,23 +909,23 @@ unsigned row_blocks(int n, int rows_per_wave) {
   return static_cast<unsigned>(((n + rows_per_wave - 1) / rows_per_wave + 3) / 4);
 }
 
-template <int CH, typename TOut, bool PARTIALS>
+template <int CH, typename TOut, bool PARTIALS, bool GS>
 void t2_row_go(const bpw_weights& w, const int8_t* q, const float* xs, TOut* y, int32_t* pout,
                int pn0, int pn1, hipStream_t s) {
   const int n = static_cast<int>(w.n), k = static_cast<int>(w.k);
-  gemv_t2_row_kernel<kRowT2, CH, TOut, PARTIALS><<<row_blocks(n, kRowT2), 256, 0, s>>>(
+  gemv_t2_row_kernel<kRowT2, CH, TOut, PARTIALS, GS><<<row_blocks(n, kRowT2), 256, 0, s>>>(
       static_cast<const uint8_t*>(w.codes), static_cast<const __half*>(w.scales), q, xs, n, k, y,
       pout, pn0, pn1);
 }
 
-template <typename TOut, bool PARTIALS>
+template <typename TOut, bool PARTIALS, bool GS = false>
 hipError_t t2_row(const bpw_weights& w, const int8_t* q, const float* xs, TOut* y, int32_t* pout,
                   int pn0, int pn1, hipStream_t s) {
   switch (w.k / 4096) {
-    case 1: t2_row_go<1, TOut, PARTIALS>(w, q, xs, y, pout, pn0, pn1, s); break;
-    case 2: t2_row_go<2, TOut, PARTIALS>(w, q, xs, y, pout, pn0, pn1, s); break;
-    case 3: t2_row_go<3, TOut, PARTIALS>(w, q, xs, y, pout, pn0, pn1, s); break;
-    default: t2_row_go<4, TOut, PARTIALS>(w, q, xs, y, pout, pn0, pn1, s); break;
+    case 1: t2_row_go<1, TOut, PARTIALS, GS>(w, q, xs, y, pout, pn0, pn1, s); break;
+    case 2: t2_row_go<2, TOut, PARTIALS, GS>(w, q, xs, y, pout, pn0, pn1, s); break;
+    case 3: t2_row_go<3, TOut, PARTIALS, GS>(w, q, xs, y, pout, pn0, pn1, s); break;
+    default: t2_row_go<4, TOut, PARTIALS, GS>(w, q, xs, y, pout, pn0, pn1, s); break;
   }
   return hipGetLastError();
 }
@@ -940,26 +967,27 @@ int skinny_rpw(int n) {
   return min(rpw, 128);
 }
 
-template <int NW, int GPW, int MAXT, typename TOut, bool PARTIALS>
+template <int NW, int GPW, int MAXT, typename TOut, bool PARTIALS, bool GS>
 void t2_skinny_go(const bpw_weights& w, const int8_t* q, const float* xs, int m, int rpw, TOut* y,
                   int32_t* pout, int pm0, int pm1, int pn0, int pn1, int wg0, int nwg, hipStream_t s) {
   const uint8_t* codes = static_cast<const uint8_t*>(w.codes);
   const __half* sc = static_cast<const __half*>(w.scales);
   const int n = static_cast<int>(w.n), k = static_cast<int>(w.k);
+  const size_t gs_lds = GS ? 4ull * NW * GPW * 32 : 0;     // activation group scales, per wave
   if (m <= 16) {
-    auto kern = gemv_t2_skinny_kernel<NW, GPW, MAXT, 8, TOut, PARTIALS>;
-    const size_t lds = 2ull * NW * 8 * 64 * 4;
+    auto kern = gemv_t2_skinny_kernel<NW, GPW, MAXT, 8, TOut, PARTIALS, GS>;
+    const size_t lds = 2ull * NW * 8 * 64 * 4 + gs_lds;
     allow_lds(kern, lds);
     kern<<<nwg, NW * 64, lds, s>>>(codes, sc, q, xs, m, n, k, rpw, y, pout, pm0, pm1, pn0, pn1, wg0);
   } else {
-    auto kern = gemv_t2_skinny_kernel<NW, GPW, MAXT, 16, TOut, PARTIALS>;
-    const size_t lds = 2ull * NW * 16 * 64 * 4;
+    auto kern = gemv_t2_skinny_kernel<NW, GPW, MAXT, 16, TOut, PARTIALS, GS>;
+    const size_t lds = 2ull * NW * 16 * 64 * 4 + gs_lds;
     allow_lds(kern, lds);
     kern<<<nwg, NW * 64, lds, s>>>(codes, sc, q, xs, m, n, k, rpw, y, pout, pm0, pm1, pn0, pn1, wg0);
   }
 }
 
-template <typename TOut, bool PARTIALS>
+template <typename TOut, bool PARTIALS, bool GS = false>
 hipError_t t2_skinny(const bpw_weights& w, const int8_t* q, const float* xs, int m, TOut* y,
                      int32_t* pout, int pm0, int pm1, int pn0, int pn1, hipStream_t s) {
   const int n = static_cast<int>(w.n), g = static_cast<int>(w.k / 128);
@@ -973,8 +1001,8 @@ hipError_t t2_skinny(const bpw_weights& w, const int8_t* q, const float* xs, int
   const bool two = rpw <= 64;
 #define BPW_SK(NW_, GPW_)                                                                          \
   if (nw == NW_ && gpw == GPW_) {                                                                 \
-    if (two) t2_skinny_go<NW_, GPW_, 2, TOut, PARTIALS>(w, q, xs, m, rpw, y, pout, pm0, pm1, pn0, pn1, wg0, nwg, s); \
-    else t2_skinny_go<NW_, GPW_, 4, TOut, PARTIALS>(w, q, xs, m, rpw, y, pout, pm0, pm1, pn0, pn1, wg0, nwg, s);     \
+    if (two) t2_skinny_go<NW_, GPW_, 2, TOut, PARTIALS, GS>(w, q, xs, m, rpw, y, pout, pm0, pm1, pn0, pn1, wg0, nwg, s); \
+    else t2_skinny_go<NW_, GPW_, 4, TOut, PARTIALS, GS>(w, q, xs, m, rpw, y, pout, pm0, pm1, pn0, pn1, wg0, nwg, s);     \
     return hipGetLastError();                                                                     \
   }
   BPW_SK(8, 1) BPW_SK(8, 2) BPW_SK(16, 1) BPW_SK(16, 2) BPW_SK(16, 3) BPW_SK(16, 4)
@@ -982,9 +1010,18 @@ hipError_t t2_skinny(const bpw_weights& w, const int8_t* q, const float* xs, int
   return hipErrorInvalidValue;
 }
 
+// Activation scales per (row, group): the M = 1 row kernel or the skinny kernel
+// (which also takes M = 1 here).
+bool t2_group_ok(int64_t m, int64_t k) { return t2_row_ok(m, k) || (m >= 1 && m <= 32 && k <= 128 * 16 * 4); }
+
 template <typename TOut>
 hipError_t t2_dispatch(const bpw_weights& w, const int8_t* q, const float* xs, int m, TOut* y,
-                       hipStream_t s) {
+                       bool gs, hipStream_t s) {
+  if (gs) {
+    if (t2_row_ok(m, w.k)) return t2_row<TOut, false, true>(w, q, xs, y, nullptr, 0, 0, s);
+    if (t2_group_ok(m, w.k)) return t2_skinny<TOut, false, true>(w, q, xs, m, y, nullptr, 0, 0, 0, 0, s);
+    return hipErrorInvalidValue;
+  }
   if (t2_row_ok(m, w.k)) return t2_row<TOut, false>(w, q, xs, y, nullptr, 0, 0, s);
   if (t2_skinny_ok(m, w.k)) return t2_skinny<TOut, false>(w, q, xs, m, y, nullptr, 0, 0, 0, 0, s);
   const int nw = waves_for(w.k / 128);
@@ -1099,13 +1136,15 @@ bool gemv_w4_fits(int64_t m, int64_t k) {
   return m >= 1 && m <= 32 && (w4_row_ok(m, k) || w4_skinny_ok(m, k) || static_cast<size_t>(m) * k * 2 <= kLdsBudget);
 }
 
+bool gemv_t2_group_fits(int64_t m, int64_t k) { return t2_group_ok(m, k); }
+
 hipError_t launch_gemv_t2(const bpw_weights& w, const int8_t* q, const float* x_scale, int64_t m,
-                          void* y, int y_dtype, hipStream_t s) {
+                          void* y, int y_dtype, bool group_scales, hipStream_t s) {
   const int mi = static_cast<int>(m);
   switch (y_dtype) {
-    case BPW_F32: return t2_dispatch(w, q, x_scale, mi, static_cast<float*>(y), s);
-    case BPW_F16: return t2_dispatch(w, q, x_scale, mi, static_cast<__half*>(y), s);
-    default: return t2_dispatch(w, q, x_scale, mi, static_cast<uint16_t*>(y), s);
+    case BPW_F32: return t2_dispatch(w, q, x_scale, mi, static_cast<float*>(y), group_scales, s);
+    case BPW_F16: return t2_dispatch(w, q, x_scale, mi, static_cast<__half*>(y), group_scales, s);
+    default: return t2_dispatch(w, q, x_scale, mi, static_cast<uint16_t*>(y), group_scales, s);
   }
 }
 

@@ -13,6 +13,9 @@ namespace bpw {
 // Activation operand preparation (quant.hip).
 hipError_t launch_quantize_rows(const void* x, int x_dtype, int64_t m, int64_t k, int8_t* q,
                                 float* x_scale, hipStream_t s);
+// One scale per (row, 128-group): x_scale [M][K/128]. K % 128 == 0.
+hipError_t launch_quantize_groups(const void* x, int x_dtype, int64_t m, int64_t k, int8_t* q,
+                                  float* x_scale, hipStream_t s);
 // q [M][K] natural order -> plane order inside each 128-group (element 4u+t of a
 // 64-element half-group goes to position 32t + 16*half + u).
 hipError_t launch_int8_planes(const int8_t* q, int64_t m, int64_t k, int8_t* q_planes,
@@ -24,8 +27,11 @@ hipError_t launch_gather_cols(const uint16_t* x, const int32_t* perm, int64_t m,
 // Decode GEMVs (gemv.hip). Return hipErrorInvalidValue when the staged
 // activations do not fit the kernel's LDS budget (caller then routes to GEMM).
 bool gemv_t2_fits(int64_t m, int64_t k);
+// group_scales: x_scale is [M][K/128] (one scale per row and group) instead of
+// [M]; only the shapes gemv_t2_group_fits accepts.
+bool gemv_t2_group_fits(int64_t m, int64_t k);
 hipError_t launch_gemv_t2(const bpw_weights& w, const int8_t* q, const float* x_scale, int64_t m,
-                          void* y, int y_dtype, hipStream_t s);
+                          void* y, int y_dtype, bool group_scales, hipStream_t s);
 hipError_t launch_gemv_t2_partials(const bpw_weights& w, const int8_t* q, int64_t m, int64_t m0,
                                    int64_t m1, int64_t n0, int64_t n1, int32_t* out,
                                    hipStream_t s);

@@ -1,5 +1,5 @@
-// Activation operand kernels: int8 row quantiser, int8 plane reorder, act-order
-// column gather.
+// Activation operand kernels: int8 row and group quantisers, int8 plane
+// reorder, act-order column gather.
 //
 // Quantiser rule: "Kernel experiments: recorded evidence", Test 6 (group-128
 // quantiser: absmax / 127, IEEE division, round half to even, clamp to
@@ -68,6 +68,31 @@ __global__ __launch_bounds__(kQThreads) void quantize_rows_kernel(const T* __res
   if (threadIdx.x == 0) x_scale[row] = scale;
 }
 
+// One wave per (row, 128-group) unit, the same rule with the group's own max:
+// unit u covers x[128u, 128u + 128) because rows are K = 128 G long, and its
+// scale goes to x_scale[u] ([M][G] row-major). Two values per lane.
+template <typename T>
+__global__ __launch_bounds__(256) void quantize_groups_kernel(const T* __restrict__ x, int64_t units,
+                                                              int8_t* __restrict__ q,
+                                                              float* __restrict__ x_scale) {
+  const int lane = threadIdx.x & 63;
+  for (int64_t u = blockIdx.x * 4ll + (threadIdx.x >> 6); u < units; u += gridDim.x * 4ll) {   // whole waves
+    const int64_t i = u * 128 + 2 * lane;
+    const float v0 = ld(x + i), v1 = ld(x + i + 1);
+    float amax = fmaxf(fabsf(v0), fabsf(v1));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    const float scale = amax * (1.0f / 127.0f);    // fp32 reciprocal constant, one rounding
+    const float div = scale > 0.0f ? scale : 1.0f;
+    const float r0 = fminf(fmaxf(rintf(v0 / div), -127.0f), 127.0f);   // IEEE division, ties to even
+    const float r1 = fminf(fmaxf(rintf(v1 / div), -127.0f), 127.0f);
+    const uint32_t pair = (static_cast<uint32_t>(static_cast<int>(r0)) & 0xFFu) |
+                          ((static_cast<uint32_t>(static_cast<int>(r1)) & 0xFFu) << 8);
+    *reinterpret_cast<uint16_t*>(q + i) = static_cast<uint16_t>(pair);
+    if (lane == 0) x_scale[u] = scale;
+  }
+}
+
 // One thread per (row, group, half): 64 natural bytes -> four 16-byte plane chunks.
 __global__ __launch_bounds__(256) void int8_planes_kernel(const int8_t* __restrict__ q,
                                                           int64_t m, int64_t k,
@@ -123,6 +148,22 @@ hipError_t launch_quantize_rows(const void* x, int x_dtype, int64_t m, int64_t k
     case BPW_F32: quantize_go<float>(x, m, k, q, x_scale, s); break;
     case BPW_F16: quantize_go<__half>(x, m, k, q, x_scale, s); break;
     default: quantize_go<uint16_t>(x, m, k, q, x_scale, s); break;
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+void quantize_groups_go(const void* x, int64_t m, int64_t k, int8_t* q, float* x_scale, hipStream_t s) {
+  const int64_t units = m * (k / 128);
+  quantize_groups_kernel<T><<<grid_for(units, 4), 256, 0, s>>>(static_cast<const T*>(x), units, q, x_scale);
+}
+
+hipError_t launch_quantize_groups(const void* x, int x_dtype, int64_t m, int64_t k, int8_t* q,
+                                  float* x_scale, hipStream_t s) {
+  switch (x_dtype) {
+    case BPW_F32: quantize_groups_go<float>(x, m, k, q, x_scale, s); break;
+    case BPW_F16: quantize_groups_go<__half>(x, m, k, q, x_scale, s); break;
+    default: quantize_groups_go<uint16_t>(x, m, k, q, x_scale, s); break;
   }
   return hipGetLastError();
 }

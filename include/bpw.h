@@ -5,7 +5,7 @@
  * 2-bit ternary codes or 4-bit codes, one fp16/bf16 scale (and optionally one
  * 4-bit zero point) per group of 128 along K, with an optional act-order
  * permutation of K. Activations are fp16/bf16, or int8 with one fp32 scale per
- * row. Sources: "Kernel experiments: recorded evidence" (ternary PQ2 format,
+ * row (or, for the decode GEMV, per row and 128-group). Sources: "Kernel experiments: recorded evidence" (ternary PQ2 format,
  * section A and Tests 1, 2, 6-8, 21) and "mate: Marlin-class W4A16 GEMM for
  * mp_31 (SQMMA int4 x fp16) - #6" (4-bit codes, zero points, act order).
  *
@@ -52,6 +52,10 @@ extern "C" {
 #define BPW_BF16 2
 #define BPW_I8 3
 #define BPW_I32 4
+/* int8 activations with one fp32 scale per (row, 128-group): x_scale [M][K/128].
+ * Accepted by bpw_gemv_packed for ternary weights ("Kernel experiments",
+ * Test 6: the quantiser's scale is per group of 128 activations). */
+#define BPW_I8G 5
 
 /* ---- source layouts accepted by bpw_prepare_packed ------------------- */
 #define BPW_SRC_PQ2_BLOCKS 1 /* ternary only: [N][G][34] = fp16 scale (little-endian) + 32 code bytes */
@@ -150,6 +154,17 @@ int bpw_quantize_rows(const void* x, int x_dtype, int64_t m, int64_t k, int8_t* 
                       void* stream);
 
 /*
+ * int8 activation quantiser, one scale per (row, 128-group), the same rule
+ * with the group's own max ("Kernel experiments", Test 6, group-128 form):
+ *   scale[m,g] = fl32(max_{k in g} |x[m,k]| * fl32(1/127)),
+ *   q[m,k]     = clamp(round_half_even(x[m,k] / (scale[m,g] > 0 ? scale[m,g] : 1)), -127, 127).
+ * x: device [M][K] of x_dtype (F32/F16/BF16); K a multiple of 128.
+ * q: device int8 [M][K], 16-byte aligned; x_scale: device fp32 [M][K/128].
+ */
+int bpw_quantize_groups(const void* x, int x_dtype, int64_t m, int64_t k, int8_t* q, float* x_scale,
+                        void* stream);
+
+/*
  * Device workspace (bytes, 256-byte aligned start) that bpw_gemv_packed /
  * bpw_gemm_packed need for this weight, M and activation type; 0 if none.
  * entry: BPW_PATH_GEMV or BPW_PATH_GEMM. Host only.
@@ -159,11 +174,15 @@ int bpw_workspace_size(const bpw_weights* w, int64_t m, int x_dtype, int entry, 
 /*
  * y = x @ W^T, decode-shaped (tuned for M <= 16; any M >= 1 accepted).
  * Supported (fmt, x_dtype): TERNARY2 x I8 (x_scale device fp32 [M] required),
- * INT4_SYM / INT4_ZP x F16 or BF16 (scale_dtype == x_dtype, x_scale NULL).
+ * TERNARY2 x I8G (x_scale device fp32 [M][K/128]; M <= 32 and K <= 8192, or
+ * M = 1 and K a multiple of 4096 up to 16384; other shapes and the GEMM entry
+ * return BPW_EUNSUPPORTED), INT4_SYM / INT4_ZP x F16 or BF16 (scale_dtype ==
+ * x_dtype, x_scale NULL).
  * Anything else returns BPW_EUNSUPPORTED. y: device [M][N] of y_dtype
  * (F32, F16 or BF16; round-to-nearest-even from fp32).
  * Numerics: int8 -> exact int32 group partials, fp32 fold
- * y = x_scale[m] * sum_g scale[n,g] * P[m,n,g]. 4-bit -> the group partial
+ * y = x_scale[m] * sum_g scale[n,g] * P[m,n,g] (I8G: y = sum_g x_scale[m,g] *
+ * scale[n,g] * P[m,n,g], the two scales multiplied in fp32 first). 4-bit -> the group partial
  * sum_k x * (code - zero) is accumulated in fp32 from exact products and the
  * group scale is applied to it (the weight is never rounded).
  * workspace: device, at least bpw_workspace_size(..., BPW_PATH_GEMV) bytes, or
@@ -176,7 +195,7 @@ int bpw_gemv_packed(const bpw_weights* w, const void* x, int x_dtype, const floa
 
 /*
  * y = x @ W^T, prefill-shaped (large M). Same arguments and combinations as
- * bpw_gemv_packed. Numerics: int8 -> as above (int8 MFMA, exact int32 group
+ * bpw_gemv_packed, except I8G (BPW_EUNSUPPORTED). Numerics: int8 -> as above (int8 MFMA, exact int32 group
  * partials). 4-bit -> each weight is dequantised to the activation dtype,
  * round-to-nearest-even of (code - zero) * scale, then multiplied on MFMA with
  * fp32 accumulation (the float path of the mate PR: unpack int4 to the

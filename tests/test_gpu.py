@@ -66,6 +66,32 @@ def test_quantize_rows_bit_exact(dtype, m, k):
     np.testing.assert_array_equal(host(q), q_ref)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("m,k", [(1, 128), (1, 4096), (3, 1152), (16, 8192)])
+def test_quantize_groups_bit_exact(dtype, m, k):
+    rng = np.random.default_rng(m * 11 + k)
+    g = k // 128
+    # a different magnitude per (row, group), ties in group 0 of row 0, a zero group
+    x = (rng.standard_normal((m, k)) * np.repeat(rng.uniform(0.01, 50, size=(m, g)), 128, axis=1)).astype(np.float32)
+    x[0, :8] = [127.0, 2.5, 3.5, -2.5, -0.5, 126.5, 0.5, 1.5]
+    if g > 1:
+        x[m - 1, 128:256] = 0.0
+    if dtype == "f16":
+        xs = x.astype(np.float16)
+        xf = xs.astype(np.float32)
+    elif dtype == "bf16":
+        xs = synth.f32_to_bf16_bits(x)
+        xf = synth.bf16_bits_to_f32(xs)
+    else:
+        xs = xf = x
+    q, s = bpw.quantize_groups(to_dev(xs, dtype))
+    torch.cuda.synchronize()
+    q_ref, s_ref = quant.quantize_groups(xf)
+    assert s.shape == (m, g)
+    np.testing.assert_array_equal(host(s).astype(np.float32), s_ref)
+    np.testing.assert_array_equal(host(q), q_ref)
+
+
 # ------------------------------------------------------------------ ternary x int8
 def ternary_case(m, k, n, seed, out="f16"):
     return synth.ternary_int8(f"t{m}x{k}x{n}", seed, m, k, n, 0.005, 0.05, out)
@@ -93,6 +119,30 @@ def test_gemv_ternary_parity(m, k, n, out):
     w = ternary_case(m, k, n, 100 + m + k + n, out)
     _, _, _, y, y_ref = run_ternary(w, "gemv")
     assert_close(host(y), y_ref, out, f"gemv ternary m={m} k={k} n={n}")
+
+
+@pytest.mark.parametrize("m,k,n", [(1, 4096, 1000), (1, 16384, 77), (1, 512, 256), (2, 640, 333),
+                                   (16, 4096, 14336), (32, 8192, 3000), (9, 3072, 20000)])
+@pytest.mark.parametrize("out", ["f32", "f16"])
+def test_gemv_ternary_group_scales(m, k, n, out):
+    # one activation scale per (row, 128-group): y = sum_g xs[m,g] * ws[n,g] * P[m,n,g]
+    w = ternary_case(m, k, n, 600 + m + k + n, out)
+    pw = prepare(w)
+    q, xs = bpw.quantize_groups(to_dev(w.x, "f32"))
+    y = bpw.gemv_packed(pw, q, xs, out_dtype=TORCH[out])
+    torch.cuda.synchronize()
+    q_ref, xs_ref = quant.quantize_groups(w.x)
+    np.testing.assert_array_equal(host(q), q_ref)
+    _, y_ref = reference.ternary_int8_product_group_scales(q_ref, xs_ref, w.codes, w.scales)
+    assert_close(host(y), y_ref, out, f"gemv ternary group scales m={m} k={k} n={n}")
+
+
+def test_group_scales_refused_where_unsupported():
+    w = ternary_case(4, 256, 64, 9)
+    pw = prepare(w)
+    q, xs = bpw.quantize_groups(to_dev(w.x, "f32"))
+    with pytest.raises(bpw.BpwError, match="bpw_gemv_packed only"):
+        bpw.gemm_packed(pw, q, xs)
 
 
 @pytest.mark.parametrize("m,k,n", [(1, 256, 300), (130, 1024, 520), (300, 640, 257), (64, 128, 256)])

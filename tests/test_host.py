@@ -184,6 +184,27 @@ def test_product_validation_statuses():
     assert _gemv(wp, x_dtype=bpw.F16, xs=None, m=4, ws=(1 << 20) + 16, ws_bytes=1 << 20) == bpw.EALIGN
 
 
+def test_group_scale_validation():
+    lib = bpw.lib()
+    w = _weights(k=4096, n=300)
+    st = lib.bpw_gemm_packed(ctypes.byref(w), 65536, bpw.I8G, 1024, 4, 131072, bpw.F16, None, 0, None)
+    assert st == bpw.EUNSUPPORTED and "bpw_gemv_packed only" in bpw.last_error()
+    assert _gemv(_weights(k=16384), x_dtype=bpw.I8G, m=2) == bpw.EUNSUPPORTED     # K > 8192 beyond M = 1
+    assert _gemv(_weights(k=256), x_dtype=bpw.I8G, m=33) == bpw.EUNSUPPORTED
+    assert _gemv(_weights(k=256), x_dtype=bpw.I8G, xs=None) == bpw.EINVAL
+    assert _gemv(_weights(k=256), x_dtype=bpw.I8G, xs=1026) == bpw.EALIGN
+    assert _gemv(_weights(bpw.INT4_SYM), x_dtype=bpw.I8G) == bpw.EUNSUPPORTED
+    need = ctypes.c_size_t(7)
+    assert lib.bpw_workspace_size(ctypes.byref(_weights(k=8192, n=100)), 32, bpw.I8G, bpw.PATH_GEMV,
+                                  ctypes.byref(need)) == 0
+    assert need.value == 0
+    quant = lib.bpw_quantize_groups
+    assert quant(65536, bpw.F32, 2, 200, 131072, 1024, None) == bpw.ESHAPE      # K % 128
+    assert quant(65536, bpw.I8, 2, 256, 131072, 1024, None) == bpw.EUNSUPPORTED
+    assert quant(65536, bpw.F32, 2, 256, 131080, 1024, None) == bpw.EALIGN      # q 16-byte aligned
+    assert quant(None, bpw.F32, 2, 256, 131072, 1024, None) == bpw.EINVAL
+
+
 def test_workspace_sizes():
     need = ctypes.c_size_t()
     lib = bpw.lib()
