@@ -156,6 +156,25 @@ def bench_ternary_decode_m(bpw, synth, torch, np, steps, warmup, m=16):
             "copies": len(copies)}
 
 
+def bench_ternary_decode_groups(bpw, synth, torch, np, steps, warmup, m=1):
+    """Ternary decode with one activation scale per (row, 128-group): the GEMV alone and,
+    for the complete call, the GPU group quantiser in front of it."""
+    w = synth.ternary_decode(m)
+    planes = bpw.prepare_packed_host(bpw.TERNARY2, w.codes, w.scales)
+    copies = rotated_copies(bpw, planes, 1 << 30)
+    x = to_dev(w.x, "f32", torch, np)
+    q, xs = bpw.quantize_groups(x)
+    y = torch.empty((m, w.n), dtype=torch.float16, device="cuda")
+    nbytes = copies[0].logical_bytes
+    ms = time_graph(torch, lambda i: bpw.gemv_packed(copies[i % len(copies)], q, xs, out=y), steps, warmup)
+    ms_full = time_graph(torch, lambda i: (bpw.quantize_groups(x, q, xs),
+                                           bpw.gemv_packed(copies[i % len(copies)], q, xs, out=y)),
+                         max(steps // 4, 1), max(warmup // 4, 1))
+    return {"workload": "ternary_decode_gemv_group_scales", "M": m, "K": w.k, "N": w.n, "weight_bytes": nbytes,
+            "us_per_call": ms * 1e3, "GB_s": nbytes / (ms * 1e6), "frac_hbm_peak": nbytes / (ms * 1e6) / HBM_PEAK_GBS,
+            "complete_call_us": ms_full * 1e3, "copies": len(copies)}
+
+
 def bench_w4_decode(bpw, synth, torch, np, steps, warmup, m=1):
     w = synth.w4a16_decode(m)
     planes = bpw.prepare_packed_host(bpw.INT4_ZP, w.codes, w.scales, w.zeros, w.g_idx)
@@ -252,7 +271,8 @@ def main():
         extra.append(probe)
         torch.cuda.empty_cache()
     if not args.no_extra:
-        runs = ((bench_ternary_decode_m, 900, 300, {"m": 16}), (bench_w4_decode, 900, 300, {"m": 1}),
+        runs = ((bench_ternary_decode_m, 900, 300, {"m": 16}), (bench_ternary_decode_groups, 900, 300, {"m": 1}),
+                (bench_ternary_decode_groups, 900, 300, {"m": 16}), (bench_w4_decode, 900, 300, {"m": 1}),
                 (bench_w4_decode, 900, 300, {"m": 8}), (bench_w4_prefill, 30, 6, {}), (bench_ternary_prefill, 12, 3, {}))
         for fn, steps, warm, kw in runs:
             r = fn(bpw, synth, torch, np, steps, warm, **kw)
