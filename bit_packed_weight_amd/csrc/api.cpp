@@ -129,8 +129,7 @@ int run_product(bool gemv, const bpw_weights* w, const void* x, int x_dtype, con
     if (!gemv)
       return fail(BPW_EUNSUPPORTED, "per-group activation scales (BPW_I8G) are supported by bpw_gemv_packed only");
     if (!gemv_t2_group_fits(m, w->k))
-      return fail(BPW_EUNSUPPORTED, "per-group activation scales need M <= 32 and K <= 8192, or M = 1 and "
-                                    "K a multiple of 4096 up to 16384 (M=%lld, K=%lld)", (long long)m, (long long)w->k);
+      return fail(BPW_EUNSUPPORTED, "per-group activation scales need M <= 32 (M=%lld)", (long long)m);
   }
   if (int st = check_workspace(w, m, x_dtype, entry, ws, ws_bytes)) return st;
   if (int st = check_device()) return st;
@@ -245,7 +244,7 @@ extern "C" int bpw_partials(const bpw_weights* w, const int8_t* q, int64_t m, in
                 (long long)m1, (long long)n0, (long long)n1, (long long)m, (long long)w->n);
   if (path != BPW_PATH_GEMV && path != BPW_PATH_GEMM) return fail(BPW_EINVAL, "unknown path %d", path);
   if (path == BPW_PATH_GEMV && !gemv_t2_fits(m, w->k))
-    return fail(BPW_ESHAPE, "the GEMV core takes M <= 32 with M*K within its LDS budget");
+    return fail(BPW_ESHAPE, "the GEMV core takes M <= 32");
   if (path == BPW_PATH_GEMM) {
     if (int st = check_workspace(w, m, BPW_I8, BPW_PATH_GEMM, workspace, workspace_bytes)) return st;
   }

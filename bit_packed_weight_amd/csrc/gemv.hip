@@ -59,9 +59,11 @@ __device__ __forceinline__ T load_stream(const uint8_t* p) {
 }
 
 // ---------------------------------------------------------------- ternary, M = 1
-// K a multiple of 4096. Each wave streams R whole rows with one 1 KB load
+// K up to CH * 4096. Each wave streams R whole rows with one 1 KB load
 // instruction per 4096 columns: lane l holds the 64 codes of columns
-// 64l..64l+63 of each 4096-column chunk (half a 128-group). The lane's 64
+// 64l..64l+63 of each 4096-column chunk (half a 128-group); in a last, partial
+// chunk the lanes past K read clamped (in-bounds) addresses and zero their
+// activations, so they count nothing (no branch around any load). The lane's 64
 // activation bytes sit in registers in plane order; each code plane of a packed
 // word is one v_dot4 against the matching activation word; the code - 1 offset
 // is minus the half-group sum of q; the half-group partial is folded with its
@@ -76,26 +78,39 @@ __global__ __launch_bounds__(256) void gemv_t2_row_kernel(
   const int row0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * R;
   if (row0 >= N) return;                        // whole wave; this kernel has no barriers
   const int KB = K >> 2, G = K >> 7;
+  bool ok[CH];                                  // this lane's columns of chunk c lie below K
+#pragma unroll
+  for (int c = 0; c < CH; ++c) ok[c] = c * 4096 + lane * 64 < K;
+  // activations first (small, L2-resident), then the code rows
+  v4u qin[CH][4];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const v4u* src = reinterpret_cast<const v4u*>(q + min(c * 4096 + lane * 64, K - 64));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qin[c][i] = src[i];
+  }
+  __builtin_amdgcn_sched_barrier(0);
   v4u cw[R][CH];
   float sv[R][CH];
   float xg[CH];                                 // GS: this lane's activation group scale per chunk
 #pragma unroll
-  for (int c = 0; c < CH; ++c) xg[c] = GS ? x_scale[32 * c + (lane >> 1)] : 1.0f;
+  for (int c = 0; c < CH; ++c) xg[c] = GS ? x_scale[min(32 * c + (lane >> 1), G - 1)] : 1.0f;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const size_t row = static_cast<size_t>(min(row0 + r, N - 1));
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      cw[r][c] = load_stream<v4u>(codes + row * KB + c * 1024 + lane * 16);
-      sv[r][c] = __half2float(wscale[row * G + 32 * c + (lane >> 1)]);
+      cw[r][c] = load_stream<v4u>(codes + row * KB + min(c * 1024 + lane * 16, KB - 16));
+      sv[r][c] = __half2float(wscale[row * G + min(32 * c + (lane >> 1), G - 1)]);
     }
   }
   v4u qp[CH][4];
   int th[CH];
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
-    const v4u* src = reinterpret_cast<const v4u*>(q + c * 4096 + lane * 64);
-    v4u in[4] = {src[0], src[1], src[2], src[3]};
+    v4u in[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) in[i] = ok[c] ? qin[c][i] : v4u{0, 0, 0, 0};
     to_plane_order(in, qp[c]);
     int sum = 0;
 #pragma unroll
@@ -128,7 +143,7 @@ __global__ __launch_bounds__(256) void gemv_t2_row_kernel(
       if (PARTIALS) {
         const int pg = p + __shfl_xor(p, 1);
         const int row = row0 + r;
-        if ((lane & 1) == 0 && row < N && row >= pn0 && row < pn1)
+        if ((lane & 1) == 0 && ok[c] && row < N && row >= pn0 && row < pn1)
           pout[static_cast<size_t>(row - pn0) * G + 32 * c + (lane >> 1)] = pg;
       } else {
         acc[r] = fmaf(static_cast<float>(p), GS ? sv[r][c] * xg[c] : sv[r][c], acc[r]);
@@ -144,164 +159,7 @@ __global__ __launch_bounds__(256) void gemv_t2_row_kernel(
   }
 }
 
-// ---------------------------------------------------------------- ternary, M <= 32
-// int8 MFMA (i32_32x32x32_i8). Workgroup = 32 weight rows. The rows are first
-// copied whole into LDS with coalesced 16-byte loads along each row; then each
-// wave reads its K-slice in MFMA layout: lane (n, h) takes 16 bytes of row n
-// (half a 32-byte group), whose four code planes are the B operands of four
-// MFMAs; the A operands are the plane-ordered activations, staged once.
-template <int NW, int FOLD, typename TOut, bool PARTIALS>
-__global__ __launch_bounds__(NW * 64) void gemv_t2_kernel(
-    const uint8_t* __restrict__ codes, const __half* __restrict__ wscale,
-    const int8_t* __restrict__ q, const float* __restrict__ x_scale, int M, int N, int K,
-    TOut* __restrict__ y, int32_t* __restrict__ pout, int pm0, int pm1, int pn0, int pn1,
-    int tile0) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  const int G = K >> 7;
-  const int KB = K >> 2;
-  const int CS = KB + 16;                                        // conflict-free row stride
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n0 = (blockIdx.x + tile0) * kRows;
-  uint8_t* cs = smem;                                            // [32][CS] code rows
-  uint8_t* qs = smem + kRows * CS;                               // [M][K] plane order
-  int* ts = reinterpret_cast<int*>(qs + static_cast<size_t>(M) * K);   // [M][G] group sums
-
-  const int gpw = (G + NW - 1) / NW;
-  const int gb = min(G, wave * gpw);
-  const int ge = min(G, gb + gpw);
-  const int n = lane & 31, h = lane >> 5;
-  const int row = min(n0 + n, N - 1);
-  const __half* srow = wscale + static_cast<size_t>(row) * G;
-
-  // Copy the tile's code rows into LDS: flat 16-byte chunks, consecutive threads
-  // on consecutive chunks of a row. The first batch is issued before staging q.
-  constexpr int MAXL = 8;
-  const int cpr = KB >> 4, total = kRows * cpr;
-  v4u cv[MAXL];
-  auto load_batch = [&](int base) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < MAXL; ++i) {
-      const int c = base + tid + NW * 64 * i;
-      if (c < total) {
-        const int r = c / cpr, col = c - r * cpr;
-        cv[i] = *reinterpret_cast<const v4u*>(codes + static_cast<size_t>(min(n0 + r, N - 1)) * KB + col * 16);
-      }
-    }
-  };
-  auto store_batch = [&](int base) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < MAXL; ++i) {
-      const int c = base + tid + NW * 64 * i;
-      if (c < total) {
-        const int r = c / cpr, col = c - r * cpr;
-        *reinterpret_cast<v4u*>(cs + r * CS + col * 16) = cv[i];
-      }
-    }
-  };
-  load_batch(0);
-  float sc[kMaxG];
-#pragma unroll
-  for (int u = 0; u < kMaxG; ++u)
-    if (gb + u < ge) sc[u] = __half2float(srow[gb + u]);
-
-  // Stage q into plane order and compute exact group sums.
-  const int units = M * G * 2;
-  for (int u = tid; u < units; u += NW * 64) {
-    const int hh = u & 1, mg = u >> 1;
-    const int m = mg / G, g = mg - m * G;
-    const v4u* src = reinterpret_cast<const v4u*>(q + static_cast<size_t>(m) * K + g * 128 + hh * 64);
-    v4u in[4] = {src[0], src[1], src[2], src[3]};
-    v4u o[4];
-    to_plane_order(in, o);
-    uint8_t* dst = qs + static_cast<size_t>(m) * K + g * 128 + hh * 16;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) *reinterpret_cast<v4u*>(dst + 32 * t) = o[t];
-    int sum = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sum = sum_i8x4(in[i].x, sum);
-      sum = sum_i8x4(in[i].y, sum);
-      sum = sum_i8x4(in[i].z, sum);
-      sum = sum_i8x4(in[i].w, sum);
-    }
-    sum += __shfl_xor(sum, 1);
-    if (hh == 0) ts[m * G + g] = sum;
-  }
-  store_batch(0);
-  for (int base = NW * 64 * MAXL; base < total; base += NW * 64 * MAXL) {
-    load_batch(base);
-    store_batch(base);
-  }
-  __syncthreads();
-
-  const int mA = min(n, M - 1);
-  const uint8_t* qa = qs + static_cast<size_t>(mA) * K + h * 16;
-  const uint8_t* cb = cs + n * CS + h * 16;
-  float acc[FOLD];
-#pragma unroll
-  for (int r = 0; r < FOLD; ++r) acc[r] = 0.0f;
-
-  for (int g0 = gb; g0 < ge; g0 += kMaxG) {
-    if (g0 != gb) {
-#pragma unroll
-      for (int u = 0; u < kMaxG; ++u)
-        if (g0 + u < ge) sc[u] = __half2float(srow[g0 + u]);
-    }
-#pragma unroll
-    for (int u = 0; u < kMaxG; ++u) {
-      const int g = g0 + u;
-      if (g < ge) {
-        const v4u cw = *reinterpret_cast<const v4u*>(cb + g * 32);
-        v16i d = {};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const v4i b = {static_cast<int>(code_plane(cw.x, t)), static_cast<int>(code_plane(cw.y, t)),
-                         static_cast<int>(code_plane(cw.z, t)), static_cast<int>(code_plane(cw.w, t))};
-          const v4i a = *reinterpret_cast<const v4i*>(qa + g * 128 + 32 * t);
-          d = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, d, 0, 0, 0);
-        }
-        if (PARTIALS) {
-          const int nn = n0 + n;
-#pragma unroll
-          for (int r = 0; r < FOLD; ++r) {
-            const int mm = d_row(r, h);
-            if (mm >= pm0 && mm < pm1 && nn >= pn0 && nn < pn1) {
-              const int p = d[r] - ts[mm * G + g];
-              pout[(static_cast<size_t>(mm - pm0) * (pn1 - pn0) + (nn - pn0)) * G + g] = p;
-            }
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < FOLD; ++r) {
-            const int mm = min(d_row(r, h), M - 1);
-            const int p = d[r] - ts[mm * G + g];
-            acc[r] += static_cast<float>(p) * sc[u];
-          }
-        }
-      }
-    }
-  }
-  if (PARTIALS) return;
-
-  __syncthreads();
-  float* red = reinterpret_cast<float*>(smem);
-#pragma unroll
-  for (int r = 0; r < FOLD; ++r) red[(wave * FOLD + r) * 64 + lane] = acc[r];
-  __syncthreads();
-  if (wave == 0) {
-    const int nn = n0 + n;
-#pragma unroll
-    for (int r = 0; r < FOLD; ++r) {
-      float v = 0.0f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) v += red[(w * FOLD + r) * 64 + lane];
-      const int mm = d_row(r, h);
-      if (mm < M && nn < N) store_out(y + static_cast<size_t>(mm) * N + nn, v * x_scale[mm]);
-    }
-  }
-}
-
-// ---------------------------------------------------------------- ternary, 2 <= M <= 32, K <= 8192
+// ---------------------------------------------------------------- ternary, M <= 32, K <= 4096
 // Skinny products stream the weights like the M = 1 kernel but feed int8 MFMA.
 // One workgroup per CU owns a contiguous slice of weight rows (processed as
 // tiles of 32 rows); its NW waves split K, GPW groups each. A wave keeps the
@@ -473,6 +331,144 @@ __global__ __launch_bounds__(NW * 64) void gemv_t2_skinny_kernel(
       if (o0 == o && mm < M && nn < r1) store_out(y + static_cast<size_t>(mm) * N + nn, v);
     }
     __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- ternary, M <= 32, long K
+// The skinny kernel's scheme for K beyond what one wave's registers hold: the
+// waves step through K in phases of NW * 2 groups (2 per wave), loading a
+// phase's activations, scales and codes together and accumulating two 32-row
+// tiles (rpw <= 64) in fp32 across the phases; one fixed-order reduction
+// through LDS at the end.
+template <int NW, int FR, typename TOut, bool PARTIALS, bool GS>
+__global__ __launch_bounds__(NW * 64) void gemv_t2_long_kernel(
+    const uint8_t* __restrict__ codes, const __half* __restrict__ wscale,
+    const int8_t* __restrict__ q, const float* __restrict__ x_scale, int M, int N, int K, int rpw,
+    TOut* __restrict__ y, int32_t* __restrict__ pout, int pm0, int pm1, int pn0, int pn1, int wg0) {
+  constexpr int GPW = 2;
+  extern __shared__ float red[];                           // [tile][wave][reg][lane], then GS scales
+  const int G = K >> 7, KB = K >> 2;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 31, h = lane >> 5;
+  const int r0 = (blockIdx.x + wg0) * rpw;
+  const int r1 = min(r0 + rpw, N);
+  const int nph = (G + NW * GPW - 1) / (NW * GPW);
+  const uint8_t* crow[2];
+  const __half* srow[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const size_t row = static_cast<size_t>(min(r0 + 32 * t + n, r1 - 1));
+    crow[t] = codes + row * KB + 16 * h;
+    srow[t] = wscale + row * G;
+  }
+  constexpr int OPT = (2 * FR + NW - 1) / NW;
+  float xsv[OPT];
+  if (!PARTIALS && !GS) {
+#pragma unroll
+    for (int k = 0; k < OPT; ++k) {
+      const int rl = (tid + k * NW * 64) % (FR * 64);
+      xsv[k] = x_scale[min(d_row(rl >> 6, (rl & 63) >> 5), M - 1)];
+    }
+  }
+  float* xsl = red + 2 * NW * FR * 64 + wave * (GPW * 32);
+  float acc[2][FR];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int r = 0; r < FR; ++r) acc[t][r] = 0.0f;
+  for (int ph = 0; ph < nph; ++ph) {
+    const int gb = (ph * NW + wave) * GPW;
+    v4u ain[GPW][4];
+#pragma unroll
+    for (int u = 0; u < GPW; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ain[u][i] = v4u{0, 0, 0, 0};
+    if (n < M) {
+#pragma unroll
+      for (int u = 0; u < GPW; ++u) {
+        const v4u* src = reinterpret_cast<const v4u*>(q + static_cast<size_t>(n) * K + min(gb + u, G - 1) * 128 + 64 * h);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ain[u][i] = src[i];
+      }
+    }
+    __half sc[2][GPW];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int u = 0; u < GPW; ++u) sc[t][u] = srow[t][min(gb + u, G - 1)];
+    float xst = 0.0f;                                      // GS: element lane of this wave's [u][m] block
+    if (GS) xst = x_scale[min(lane & 31, M - 1) * G + min(gb + (lane >> 5), G - 1)];
+    __builtin_amdgcn_sched_barrier(0);
+    v4u cw[2][GPW];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int u = 0; u < GPW; ++u) {
+        cw[t][u] = *reinterpret_cast<const v4u*>(crow[t] + min(gb + u, G - 1) * 32);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    if (GS) {
+      // the previous phase's reads of the slice are done (their values were used)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      xsl[lane] = xst;                                     // 64 = GPW * 32 elements
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    v4i a[GPW][4];
+#pragma unroll
+    for (int u = 0; u < GPW; ++u) {
+      v4u o[4];
+      to_plane_order(ain[u], o);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) a[u][t] = __builtin_bit_cast(v4i, o[t]);
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int u = 0; u < GPW; ++u) {
+        const int g = gb + u;                              // past the end: clamped data, zero weight
+        const v4u c = cw[t][u];
+        v16i d = {};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const v4i b = {static_cast<int>(code_plane_signed(c.x, p)), static_cast<int>(code_plane_signed(c.y, p)),
+                         static_cast<int>(code_plane_signed(c.z, p)), static_cast<int>(code_plane_signed(c.w, p))};
+          d = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[u][p], b, d, 0, 0, 0);
+        }
+        if (PARTIALS) {
+          const int nn = r0 + 32 * t + n;
+#pragma unroll
+          for (int r = 0; r < FR; ++r) {
+            const int mm = d_row(r, h);
+            if (g < G && mm < M && mm >= pm0 && mm < pm1 && nn < r1 && nn >= pn0 && nn < pn1)
+              pout[(static_cast<size_t>(mm - pm0) * (pn1 - pn0) + (nn - pn0)) * G + g] = d[r];
+          }
+        } else {
+          const float sg = g < G ? __half2float(sc[t][u]) : 0.0f;
+#pragma unroll
+          for (int r = 0; r < FR; ++r)
+            acc[t][r] = fmaf(static_cast<float>(d[r]), GS ? sg * xsl[u * 32 + d_row(r, h)] : sg, acc[t][r]);
+        }
+      }
+  }
+  if (PARTIALS) return;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int r = 0; r < FR; ++r) red[((t * NW + wave) * FR + r) * 64 + lane] = acc[t][r];
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < OPT; ++k) {
+    const int o0 = tid + k * NW * 64, o = min(o0, 2 * FR * 64 - 1);
+    const int tt = o / (FR * 64), rl = o - tt * FR * 64, r = rl >> 6, l = rl & 63;
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) v += red[((tt * NW + w) * FR + r) * 64 + l];
+    if (!GS) v *= xsv[k];
+    const int mm = d_row(r, l >> 5), nn = r0 + 32 * tt + (l & 31);
+    if (o0 == o && mm < M && nn < r1) store_out(y + static_cast<size_t>(mm) * N + nn, v);
   }
 }
 
@@ -896,14 +892,8 @@ int waves_for(int64_t groups) { return groups >= 16 ? 8 : 4; }
 constexpr int kRowT2 = 2;
 constexpr int kRowW4 = 2;
 
-bool t2_row_ok(int64_t m, int64_t k) { return m == 1 && k % 4096 == 0 && k / 4096 <= 4; }
+bool t2_row_ok(int64_t m, int64_t k) { return m == 1 && k <= 4 * 4096; }
 bool w4_row_ok(int64_t m, int64_t k) { return m == 1 && k % 1024 == 0 && k / 1024 <= 8; }
-
-size_t t2_lds(int64_t m, int64_t k) {
-  const size_t stage = static_cast<size_t>(kRows) * (k / 4 + 16) + static_cast<size_t>(m) * k + 4ull * m * (k / 128);
-  const size_t red = 8ull * 16 * 64 * 4;
-  return stage > red ? stage : red;
-}
 
 unsigned row_blocks(int n, int rows_per_wave) {
   return static_cast<unsigned>(((n + rows_per_wave - 1) / rows_per_wave + 3) / 4);
@@ -921,24 +911,12 @@ void t2_row_go(const bpw_weights& w, const int8_t* q, const float* xs, TOut* y, 
 template <typename TOut, bool PARTIALS, bool GS = false>
 hipError_t t2_row(const bpw_weights& w, const int8_t* q, const float* xs, TOut* y, int32_t* pout,
                   int pn0, int pn1, hipStream_t s) {
-  switch (w.k / 4096) {
+  switch ((w.k + 4095) / 4096) {
     case 1: t2_row_go<1, TOut, PARTIALS, GS>(w, q, xs, y, pout, pn0, pn1, s); break;
     case 2: t2_row_go<2, TOut, PARTIALS, GS>(w, q, xs, y, pout, pn0, pn1, s); break;
     case 3: t2_row_go<3, TOut, PARTIALS, GS>(w, q, xs, y, pout, pn0, pn1, s); break;
     default: t2_row_go<4, TOut, PARTIALS, GS>(w, q, xs, y, pout, pn0, pn1, s); break;
   }
-  return hipGetLastError();
-}
-
-template <int NW, int FOLD, typename TOut>
-hipError_t t2_go(const bpw_weights& w, const int8_t* q, const float* xs, int m, TOut* y,
-                 hipStream_t s) {
-  const int n = static_cast<int>(w.n), k = static_cast<int>(w.k);
-  dim3 grid((n + kRows - 1) / kRows), block(NW * 64);
-  allow_lds(gemv_t2_kernel<NW, FOLD, TOut, false>, t2_lds(m, k));
-  gemv_t2_kernel<NW, FOLD, TOut, false><<<grid, block, t2_lds(m, k), s>>>(
-      static_cast<const uint8_t*>(w.codes), static_cast<const __half*>(w.scales), q, xs, m, n, k,
-      y, nullptr, 0, 0, 0, 0, 0);
   return hipGetLastError();
 }
 
@@ -956,7 +934,10 @@ int cu_count() {
   return cached[dev];
 }
 
-bool t2_skinny_ok(int64_t m, int64_t k) { return m >= 2 && m <= 32 && k <= 128 * 16 * 4; }
+// The skinny kernel holds a wave's whole K slice in registers: up to 32
+// groups (16 waves of 2) without spilling. Longer K goes to the long kernel.
+bool t2_skinny_ok(int64_t m, int64_t k) { return m >= 2 && m <= 32 && k <= 128 * 32; }
+bool t2_long_ok(int64_t m, int64_t k) { return m >= 1 && m <= 32; }
 
 // Rows per workgroup: the rows split evenly over the CUs, at least 16, at most
 // four 32-row tiles.
@@ -980,8 +961,11 @@ void t2_skinny_go(const bpw_weights& w, const int8_t* q, const float* xs, int m,
     allow_lds(kern, lds);
     kern<<<nwg, NW * 64, lds, s>>>(codes, sc, q, xs, m, n, k, rpw, y, pout, pm0, pm1, pn0, pn1, wg0);
   } else {
-    auto kern = gemv_t2_skinny_kernel<NW, GPW, MAXT, 16, TOut, PARTIALS, GS>;
-    const size_t lds = 2ull * NW * 16 * 64 * 4 + gs_lds;
+    // (the dispatcher sends scaled-by-group products above 16 rows to the long
+    // kernel: that form is not built, it would spill)
+    constexpr int FR = GS ? 8 : 16;
+    auto kern = gemv_t2_skinny_kernel<NW, GPW, MAXT, FR, TOut, PARTIALS, GS>;
+    const size_t lds = 2ull * NW * FR * 64 * 4 + gs_lds;
     allow_lds(kern, lds);
     kern<<<nwg, NW * 64, lds, s>>>(codes, sc, q, xs, m, n, k, rpw, y, pout, pm0, pm1, pn0, pn1, wg0);
   }
@@ -992,7 +976,7 @@ hipError_t t2_skinny(const bpw_weights& w, const int8_t* q, const float* xs, int
                      int32_t* pout, int pm0, int pm1, int pn0, int pn1, hipStream_t s) {
   const int n = static_cast<int>(w.n), g = static_cast<int>(w.k / 128);
   const int rpw = skinny_rpw(n);
-  // waves split K: 16 waves of up to 4 groups from 64 groups down, 8 below 16 groups
+  // waves split K: 16 waves of up to 2 groups from 16 groups up, 8 below
   const int nw = g >= 16 ? 16 : 8;
   const int gpw = (g + nw - 1) / nw;
   // workgroups covering weight rows [pn0, pn1) (the whole matrix for a product)
@@ -1005,32 +989,52 @@ hipError_t t2_skinny(const bpw_weights& w, const int8_t* q, const float* xs, int
     else t2_skinny_go<NW_, GPW_, 4, TOut, PARTIALS, GS>(w, q, xs, m, rpw, y, pout, pm0, pm1, pn0, pn1, wg0, nwg, s);     \
     return hipGetLastError();                                                                     \
   }
-  BPW_SK(8, 1) BPW_SK(8, 2) BPW_SK(16, 1) BPW_SK(16, 2) BPW_SK(16, 3) BPW_SK(16, 4)
+  BPW_SK(8, 1) BPW_SK(8, 2) BPW_SK(16, 1) BPW_SK(16, 2)
 #undef BPW_SK
   return hipErrorInvalidValue;
 }
 
-// Activation scales per (row, group): the M = 1 row kernel or the skinny kernel
-// (which also takes M = 1 here).
-bool t2_group_ok(int64_t m, int64_t k) { return t2_row_ok(m, k) || (m >= 1 && m <= 32 && k <= 128 * 16 * 4); }
+template <int NW, int FR, typename TOut, bool PARTIALS, bool GS>
+void t2_long_go(const bpw_weights& w, const int8_t* q, const float* xs, int m, int rpw, TOut* y,
+                int32_t* pout, int pm0, int pm1, int pn0, int pn1, int wg0, int nwg, hipStream_t s) {
+  auto kern = gemv_t2_long_kernel<NW, FR, TOut, PARTIALS, GS>;
+  const size_t lds = 2ull * NW * FR * 64 * 4 + (GS ? 4ull * NW * 64 : 0);
+  allow_lds(kern, lds);
+  kern<<<nwg, NW * 64, lds, s>>>(static_cast<const uint8_t*>(w.codes), static_cast<const __half*>(w.scales), q,
+                                 xs, m, static_cast<int>(w.n), static_cast<int>(w.k), rpw, y, pout, pm0, pm1,
+                                 pn0, pn1, wg0);
+}
 
+template <typename TOut, bool PARTIALS, bool GS = false>
+hipError_t t2_long(const bpw_weights& w, const int8_t* q, const float* xs, int m, TOut* y,
+                   int32_t* pout, int pm0, int pm1, int pn0, int pn1, hipStream_t s) {
+  const int n = static_cast<int>(w.n);
+  const int rpw = min(skinny_rpw(n), 64);                  // two 32-row tiles
+  const int wg0 = PARTIALS ? pn0 / rpw : 0;
+  const int nwg = PARTIALS ? (pn1 - 1) / rpw - wg0 + 1 : (n + rpw - 1) / rpw;
+  // 16 waves (128 VGPRs each) while the accumulators hold 8 registers, 8
+  // waves for 16 (more would spill)
+  if (m <= 16) t2_long_go<16, 8, TOut, PARTIALS, GS>(w, q, xs, m, rpw, y, pout, pm0, pm1, pn0, pn1, wg0, nwg, s);
+  else t2_long_go<8, 16, TOut, PARTIALS, GS>(w, q, xs, m, rpw, y, pout, pm0, pm1, pn0, pn1, wg0, nwg, s);
+  return hipGetLastError();
+}
+
+// M = 1 up to K = 16384: the row kernel; M = 2..32 up to 32 groups: the
+// skinny kernel; any other M <= 32: the long-K kernel. The same routing with
+// per-(row, group) activation scales.
 template <typename TOut>
 hipError_t t2_dispatch(const bpw_weights& w, const int8_t* q, const float* xs, int m, TOut* y,
                        bool gs, hipStream_t s) {
   if (gs) {
     if (t2_row_ok(m, w.k)) return t2_row<TOut, false, true>(w, q, xs, y, nullptr, 0, 0, s);
-    if (t2_group_ok(m, w.k)) return t2_skinny<TOut, false, true>(w, q, xs, m, y, nullptr, 0, 0, 0, 0, s);
+    // (above 16 rows the skinny kernel's four-tile form would spill with the scales)
+    if (m <= 16 && t2_skinny_ok(m, w.k)) return t2_skinny<TOut, false, true>(w, q, xs, m, y, nullptr, 0, 0, 0, 0, s);
+    if (t2_long_ok(m, w.k)) return t2_long<TOut, false, true>(w, q, xs, m, y, nullptr, 0, 0, 0, 0, s);
     return hipErrorInvalidValue;
   }
   if (t2_row_ok(m, w.k)) return t2_row<TOut, false>(w, q, xs, y, nullptr, 0, 0, s);
   if (t2_skinny_ok(m, w.k)) return t2_skinny<TOut, false>(w, q, xs, m, y, nullptr, 0, 0, 0, 0, s);
-  const int nw = waves_for(w.k / 128);
-  const int fold = fold_for(m);
-#define BPW_T2(NW_, F_) \
-  if (nw == NW_ && fold == F_) return t2_go<NW_, F_, TOut>(w, q, xs, m, y, s);
-  BPW_T2(8, 1) BPW_T2(8, 4) BPW_T2(8, 8) BPW_T2(8, 16)
-  BPW_T2(4, 1) BPW_T2(4, 4) BPW_T2(4, 8) BPW_T2(4, 16)
-#undef BPW_T2
+  if (t2_long_ok(m, w.k)) return t2_long<TOut, false>(w, q, xs, m, y, nullptr, 0, 0, 0, 0, s);
   return hipErrorInvalidValue;
 }
 
@@ -1048,6 +1052,9 @@ hipError_t w4_go(const bpw_weights& w, const uint16_t* x, int m, TOut* y, hipStr
   return hipGetLastError();
 }
 
+// 16..48 groups: 4..6 per wave (6 spills a few registers with zero points,
+// still far ahead of the LDS-tiled kernel, whose staging does not fit M * K
+// at these sizes)
 bool w4_skinny_ok(int64_t m, int64_t k) { return m >= 2 && m <= 16 && k / 128 >= 16 && k / 128 <= 48; }
 
 template <int GPW, int MAXT, bool BF, bool ZP, typename TOut>
@@ -1127,16 +1134,13 @@ hipError_t w4_dispatch(const bpw_weights& w, const uint16_t* x, bool bf, int m, 
 
 }  // namespace
 
-bool gemv_t2_fits(int64_t m, int64_t k) {
-  if (m < 1 || m > 32) return false;
-  return t2_row_ok(m, k) || t2_skinny_ok(m, k) || t2_lds(m, k) <= kLdsBudget;
-}
+bool gemv_t2_fits(int64_t m, int64_t k) { return m >= 1 && m <= 32; }
 
 bool gemv_w4_fits(int64_t m, int64_t k) {
   return m >= 1 && m <= 32 && (w4_row_ok(m, k) || w4_skinny_ok(m, k) || static_cast<size_t>(m) * k * 2 <= kLdsBudget);
 }
 
-bool gemv_t2_group_fits(int64_t m, int64_t k) { return t2_group_ok(m, k); }
+bool gemv_t2_group_fits(int64_t m, int64_t k) { return m >= 1 && m <= 32; }
 
 hipError_t launch_gemv_t2(const bpw_weights& w, const int8_t* q, const float* x_scale, int64_t m,
                           void* y, int y_dtype, bool group_scales, hipStream_t s) {
@@ -1151,30 +1155,17 @@ hipError_t launch_gemv_t2(const bpw_weights& w, const int8_t* q, const float* x_
 hipError_t launch_gemv_t2_partials(const bpw_weights& w, const int8_t* q, int64_t m, int64_t m0,
                                    int64_t m1, int64_t n0, int64_t n1, int32_t* out,
                                    hipStream_t s) {
-  const int n = static_cast<int>(w.n), k = static_cast<int>(w.k);
+  const int k = static_cast<int>(w.k);
   const int mi = static_cast<int>(m);
   if (t2_row_ok(m, k))   // the product for M = 1 runs the row kernel: verify that core
     return t2_row<float, true>(w, q, nullptr, nullptr, out, static_cast<int>(n0), static_cast<int>(n1), s);
-  if (t2_skinny_ok(m, k))   // and the skinny kernel for 2 <= M <= 32, K <= 8192
+  if (t2_skinny_ok(m, k))   // the skinny kernel for 2 <= M <= 32 up to 32 groups
     return t2_skinny<float, true>(w, q, nullptr, mi, static_cast<float*>(nullptr), out, static_cast<int>(m0),
                                   static_cast<int>(m1), static_cast<int>(n0), static_cast<int>(n1), s);
-  if (t2_lds(m, k) > kLdsBudget) return hipErrorInvalidValue;
-  const int t0 = static_cast<int>(n0 / kRows), t1 = static_cast<int>((n1 - 1) / kRows);
-  dim3 grid(t1 - t0 + 1);
-  if (waves_for(k / 128) == 8) {
-    allow_lds(gemv_t2_kernel<8, 16, float, true>, t2_lds(m, k));
-    gemv_t2_kernel<8, 16, float, true><<<grid, 512, t2_lds(m, k), s>>>(
-        static_cast<const uint8_t*>(w.codes), static_cast<const __half*>(w.scales), q, nullptr,
-        mi, n, k, nullptr, out, static_cast<int>(m0), static_cast<int>(m1), static_cast<int>(n0),
-        static_cast<int>(n1), t0);
-  } else {
-    allow_lds(gemv_t2_kernel<4, 16, float, true>, t2_lds(m, k));
-    gemv_t2_kernel<4, 16, float, true><<<grid, 256, t2_lds(m, k), s>>>(
-        static_cast<const uint8_t*>(w.codes), static_cast<const __half*>(w.scales), q, nullptr,
-        mi, n, k, nullptr, out, static_cast<int>(m0), static_cast<int>(m1), static_cast<int>(n0),
-        static_cast<int>(n1), t0);
-  }
-  return hipGetLastError();
+  if (t2_long_ok(m, k))     // and the long-K kernel for the rest
+    return t2_long<float, true>(w, q, nullptr, mi, static_cast<float*>(nullptr), out, static_cast<int>(m0),
+                                static_cast<int>(m1), static_cast<int>(n0), static_cast<int>(n1), s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemv_w4(const bpw_weights& w, const void* x_sorted, int x_dtype, int64_t m,

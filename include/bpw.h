@@ -174,10 +174,9 @@ int bpw_workspace_size(const bpw_weights* w, int64_t m, int x_dtype, int entry, 
 /*
  * y = x @ W^T, decode-shaped (tuned for M <= 16; any M >= 1 accepted).
  * Supported (fmt, x_dtype): TERNARY2 x I8 (x_scale device fp32 [M] required),
- * TERNARY2 x I8G (x_scale device fp32 [M][K/128]; M <= 32 and K <= 8192, or
- * M = 1 and K a multiple of 4096 up to 16384; other shapes and the GEMM entry
- * return BPW_EUNSUPPORTED), INT4_SYM / INT4_ZP x F16 or BF16 (scale_dtype ==
- * x_dtype, x_scale NULL).
+ * TERNARY2 x I8G (x_scale device fp32 [M][K/128]; M <= 32, larger M and the
+ * GEMM entry return BPW_EUNSUPPORTED), INT4_SYM / INT4_ZP x F16 or BF16
+ * (scale_dtype == x_dtype, x_scale NULL).
  * Anything else returns BPW_EUNSUPPORTED. y: device [M][N] of y_dtype
  * (F32, F16 or BF16; round-to-nearest-even from fp32).
  * Numerics: int8 -> exact int32 group partials, fp32 fold

@@ -112,8 +112,10 @@ def run_ternary(w: synth.Workload, entry: str):
 
 @pytest.mark.parametrize("m,k,n", [(1, 512, 256), (1, 4096, 1000), (2, 640, 333), (4, 128, 64),
                                    (7, 1024, 520), (16, 4096, 300), (32, 256, 97), (1, 8192, 130),
-                                   # skinny kernel: 3 and 4 groups per wave, four-tile shares, ragged tiles
-                                   (32, 8192, 3000), (9, 3072, 20000), (24, 6144, 9000)])
+                                   # skinny kernel: four-tile shares, ragged tiles; long-K kernel: 2..4 phases,
+                                   # ragged last phase; M = 1 past the row kernel's K; row kernel partial chunk
+                                   (32, 8192, 3000), (9, 3072, 20000), (24, 6144, 9000), (16, 14336, 4096),
+                                   (4, 11008, 700), (1, 20480, 500), (1, 14336, 1000), (1, 1152, 333)])
 @pytest.mark.parametrize("out", ["f32", "f16", "bf16"])
 def test_gemv_ternary_parity(m, k, n, out):
     w = ternary_case(m, k, n, 100 + m + k + n, out)
@@ -122,7 +124,8 @@ def test_gemv_ternary_parity(m, k, n, out):
 
 
 @pytest.mark.parametrize("m,k,n", [(1, 4096, 1000), (1, 16384, 77), (1, 512, 256), (2, 640, 333),
-                                   (16, 4096, 14336), (32, 8192, 3000), (9, 3072, 20000)])
+                                   (16, 4096, 14336), (32, 8192, 3000), (9, 3072, 20000), (20, 4096, 700),
+                                   (1, 20480, 300), (8, 14336, 1000)])
 @pytest.mark.parametrize("out", ["f32", "f16"])
 def test_gemv_ternary_group_scales(m, k, n, out):
     # one activation scale per (row, 128-group): y = sum_g xs[m,g] * ws[n,g] * P[m,n,g]
@@ -156,7 +159,8 @@ def test_gemm_ternary_parity(m, k, n):
 @pytest.mark.parametrize("m,k,n,win", [(3, 256, 70, (0, 3, 0, 70)), (32, 512, 200, (5, 29, 33, 170)),
                                        (1, 128, 40, (0, 1, 7, 9)), (1, 4096, 77, (0, 1, 3, 70)),
                                        (1, 8192, 9, (0, 1, 0, 9)), (16, 8192, 600, (3, 14, 100, 580)),
-                                       (12, 3072, 20000, (0, 12, 9000, 9777))])
+                                       (12, 3072, 20000, (0, 12, 9000, 9777)), (3, 12288, 500, (0, 3, 17, 463)),
+                                       (1, 5248, 300, (0, 1, 0, 300))])
 def test_partials_bit_exact(path, m, k, n, win):
     # stress inputs: full int8 range and every 2-bit code including 3
     rng = np.random.default_rng(m + k + n)

@@ -189,8 +189,7 @@ def test_group_scale_validation():
     w = _weights(k=4096, n=300)
     st = lib.bpw_gemm_packed(ctypes.byref(w), 65536, bpw.I8G, 1024, 4, 131072, bpw.F16, None, 0, None)
     assert st == bpw.EUNSUPPORTED and "bpw_gemv_packed only" in bpw.last_error()
-    assert _gemv(_weights(k=16384), x_dtype=bpw.I8G, m=2) == bpw.EUNSUPPORTED     # K > 8192 beyond M = 1
-    assert _gemv(_weights(k=256), x_dtype=bpw.I8G, m=33) == bpw.EUNSUPPORTED
+    assert _gemv(_weights(k=256), x_dtype=bpw.I8G, m=33) == bpw.EUNSUPPORTED     # decode shapes only
     assert _gemv(_weights(k=256), x_dtype=bpw.I8G, xs=None) == bpw.EINVAL
     assert _gemv(_weights(k=256), x_dtype=bpw.I8G, xs=1026) == bpw.EALIGN
     assert _gemv(_weights(bpw.INT4_SYM), x_dtype=bpw.I8G) == bpw.EUNSUPPORTED
