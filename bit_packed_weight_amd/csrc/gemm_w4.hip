@@ -152,23 +152,26 @@ __global__ __launch_bounds__(NT, 1) void gemm_w4_kernel(
 
   // One 64-column half (u) of group g in LDS buffer g & 1: four MFMA steps with
   // weights `cur`, each interleaved with the next step's A reads and a quarter
-  // of the next stage's dequant (`prep` -> `nxt`).
+  // of the next stage's dequant (`prep` -> `nxt`). The A operands of a step
+  // are read one step ahead into aop[step & 1]; the first half's last step
+  // already reads the second half's first step (same buffer), so only the
+  // first step of a group, right after the barrier that publishes its
+  // buffer, waits for its reads.
   const int nsw = n & 15;
+  v4u aop[2][8];
+  auto a_read_step = [&](int buf, int u, int ks, v4u (&dst)[8]) __attribute__((always_inline)) {
+    const uint8_t* base = smem + buf * A_BYTES + n * A_ROW + 16 * ((8 * u + 4 * h + ks) ^ nsw);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dst[i] = *reinterpret_cast<const v4u*>(base + i * 32 * A_ROW);
+  };
   auto half_stage = [&](int buf, int u, v4u (&cur)[2][4], v4u (&nxt)[2][4], const BPrep& prep)
       __attribute__((always_inline)) {
-    const uint8_t* base = smem + buf * A_BYTES + n * A_ROW;
-    auto chunk = [&](int ks) __attribute__((always_inline)) { return 16 * ((8 * u + 4 * h + ks) ^ nsw); };
-    v4u aop[2][8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) aop[0][i] = *reinterpret_cast<const v4u*>(base + i * 32 * A_ROW + chunk(0));
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      if (ks < 3) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          aop[(ks + 1) & 1][i] = *reinterpret_cast<const v4u*>(base + i * 32 * A_ROW + chunk(ks + 1));
-      }
+      if (ks < 3)
+        a_read_step(buf, u, ks + 1, aop[(ks + 1) & 1]);
+      else if (u == 0)
+        a_read_step(buf, 1, 0, aop[0]);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
 #pragma unroll
@@ -210,9 +213,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_w4_kernel(
   __syncthreads();
 
   for (int g = 0; g < G; ++g) {
-    // The next group streams into the other buffer while this one is used;
-    // every register read below was loaded at least one group earlier and
-    // waited for at the previous barrier.
+    // The first step's A reads go out first, so that the loads and dequant
+    // preparation below cover their latency. The next group streams into the
+    // other buffer while this one is used; every register read below was
+    // loaded at least one group earlier and waited for at the previous barrier.
+    a_read_step(g & 1, 0, 0, aop[0]);
+    __builtin_amdgcn_sched_barrier(0);
     graw_load(r2, min(g + 2, G - 1));
     BPrep pa, pb;
     b_prep(r0, 1, pa);                 // second half of this group
