@@ -84,12 +84,16 @@ __global__ __launch_bounds__(NT, 1) void gemm_t2_kernel(
   const int n = lane & 31, h = lane >> 5;
 
   // A: row r of a buffer is 8 chunks of 16 bytes; chunk c sits in slot
-  // c ^ (r & 7), so the 32 rows of one MFMA read hit distinct bank groups.
+  // c ^ ((r >> 1) & 7). Two 128-byte rows share one pass over the 64 LDS banks,
+  // so the 16 rows a 16-lane phase of one MFMA read touches (8 even, 8 odd)
+  // land on 16 distinct bank groups.
   // Direct load t (0..3) of wave w fills LDS bytes [(4w + t) * 1024, +1024):
-  // rows 8 (4w + t) + lane / 8, slot lane % 8.
+  // rows 8 (4w + t) + lane / 8, slot lane % 8; ((row >> 1) & 7) is
+  // (4t + lane / 16) & 7.
   const int a_row0 = 32 * wave + (lane >> 3);
-  const int a_chunk = (lane & 7) ^ (a_row0 & 7);   // (row & 7) is the same for all t
-  const int8_t* a_base = qp + a_chunk * 16;
+  // (4t + lane / 16) & 7 takes two values: t even, t odd.
+  const int8_t* a_base[2] = {qp + 16 * ((lane & 7) ^ ((lane >> 4) & 7)),
+                             qp + 16 * ((lane & 7) ^ ((4 + (lane >> 4)) & 7))};
   int a_row[4];                                      // token rows past the end are clamped
 #pragma unroll
   for (int t = 0; t < 4; ++t) a_row[t] = min(m0 + a_row0 + 8 * t, M - 1);
@@ -97,16 +101,17 @@ __global__ __launch_bounds__(NT, 1) void gemm_t2_kernel(
   auto a_load = [&](int g, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int8_t* src = a_base + static_cast<size_t>(a_row[t]) * K + g * 128;
+      const int8_t* src = a_base[t & 1] + static_cast<size_t>(a_row[t]) * K + g * 128;
       lds_dma16(src, __builtin_amdgcn_readfirstlane(lds0 + buf * A_BYTES + t * 1024));
     }
   };
   // A operand reads (into AGPRs, see ds_read_agpr): plane t of token row
-  // 32 i + n is chunk 2t + h; the buffer and token tile are immediate offsets.
+  // 32 i + n is chunk 2t + h; the buffer and token tile are immediate offsets
+  // (32 i rows shift (row >> 1) by 16 i: the slot does not depend on i).
   uint32_t a_addr[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t)
-    a_addr[t] = static_cast<uint32_t>(reinterpret_cast<size_t>(smem)) + n * A_ROW + 16 * ((2 * t + h) ^ (n & 7));
+    a_addr[t] = static_cast<uint32_t>(reinterpret_cast<size_t>(smem)) + n * A_ROW + 16 * ((2 * t + h) ^ ((n >> 1) & 7));
   auto a_read = [&](auto BUFC, auto IC, v4i (&dst)[4]) __attribute__((always_inline)) {
     constexpr int OFF = decltype(BUFC)::value * A_BYTES + decltype(IC)::value * 32 * A_ROW;
 #pragma unroll
