@@ -156,6 +156,23 @@ def bench_ternary_decode_m(bpw, synth, torch, np, steps, warmup, m=16):
             "copies": len(copies)}
 
 
+def bench_ternary_long_k(bpw, synth, torch, np, steps, warmup, m=16, k=14336, n=4096):
+    """Ternary decode with K beyond 32 groups (a down-projection shape): split-K slices
+    of 32 groups side by side, then the fixed-order reduce, both inside the call."""
+    w = synth.ternary_int8(f"long_k_m{m}", 5, m, k, n, 0.005, 0.05, "f16")
+    planes = bpw.prepare_packed_host(bpw.TERNARY2, w.codes, w.scales)
+    copies = rotated_copies(bpw, planes, 1 << 30)
+    x = to_dev(w.x, "f32", torch, np)
+    q, xs = bpw.quantize_rows(x)
+    y = torch.empty((m, n), dtype=torch.float16, device="cuda")
+    ws = torch.empty(max(bpw.workspace_size(copies[0], m, bpw.I8, bpw.PATH_GEMV), 1), dtype=torch.uint8, device="cuda")
+    nbytes = copies[0].logical_bytes
+    ms = time_graph(torch, lambda i: bpw.gemv_packed(copies[i % len(copies)], q, xs, out=y, workspace=ws), steps, warmup)
+    return {"workload": "ternary_decode_gemv_long_k", "M": m, "K": k, "N": n, "weight_bytes": nbytes,
+            "us_per_call": ms * 1e3, "GB_s": nbytes / (ms * 1e6), "frac_hbm_peak": nbytes / (ms * 1e6) / HBM_PEAK_GBS,
+            "copies": len(copies)}
+
+
 def bench_ternary_decode_groups(bpw, synth, torch, np, steps, warmup, m=1):
     """Ternary decode with one activation scale per (row, 128-group): the GEMV alone and,
     for the complete call, the GPU group quantiser in front of it."""
@@ -271,7 +288,8 @@ def main():
         extra.append(probe)
         torch.cuda.empty_cache()
     if not args.no_extra:
-        runs = ((bench_ternary_decode_m, 900, 300, {"m": 16}), (bench_ternary_decode_groups, 900, 300, {"m": 1}),
+        runs = ((bench_ternary_decode_m, 900, 300, {"m": 16}), (bench_ternary_long_k, 600, 200, {"m": 16}),
+                (bench_ternary_decode_groups, 900, 300, {"m": 1}),
                 (bench_ternary_decode_groups, 900, 300, {"m": 16}), (bench_w4_decode, 900, 300, {"m": 1}),
                 (bench_w4_decode, 900, 300, {"m": 8}), (bench_w4_prefill, 30, 6, {}), (bench_ternary_prefill, 12, 3, {}))
         for fn, steps, warm, kw in runs:

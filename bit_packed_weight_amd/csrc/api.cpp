@@ -104,7 +104,8 @@ size_t workspace_need(const bpw_weights* w, int64_t m, int x_dtype, int entry) {
   const size_t mk = static_cast<size_t>(m) * static_cast<size_t>(w->k);
   if (w->fmt == BPW_TERNARY2) {
     if (x_dtype == BPW_I8G) return 0;                // decode kernels only, no staging
-    if (entry == BPW_PATH_GEMV && gemv_t2_fits(m, w->k)) return 0;
+    if (entry == BPW_PATH_GEMV && gemv_t2_fits(m, w->k))   // fp32 split-K slices for long K
+      return round_up(gemv_t2_split_bytes(m, w->n, w->k, false));
     return round_up(mk);                       // plane-ordered int8 activations
   }
   return w->perm ? round_up(mk * 2) : 0;       // gathered 16-bit activations
@@ -137,8 +138,9 @@ int run_product(bool gemv, const bpw_weights* w, const void* x, int x_dtype, con
   if (w->fmt == BPW_TERNARY2) {
     const int8_t* q = static_cast<const int8_t*>(x);
     if (x_dtype == BPW_I8G)
-      return hip_status(launch_gemv_t2(*w, q, x_scale, m, y, y_dtype, true, s), "ternary GEMV launch");
-    if (gemv && gemv_t2_fits(m, w->k)) return hip_status(launch_gemv_t2(*w, q, x_scale, m, y, y_dtype, false, s), "ternary GEMV launch");
+      return hip_status(launch_gemv_t2(*w, q, x_scale, m, y, y_dtype, true, nullptr, 0, s), "ternary GEMV launch");
+    if (gemv && gemv_t2_fits(m, w->k))
+      return hip_status(launch_gemv_t2(*w, q, x_scale, m, y, y_dtype, false, ws, ws_bytes, s), "ternary GEMV launch");
     int8_t* qp = static_cast<int8_t*>(ws);
     if (int st = hip_status(launch_int8_planes(q, m, w->k, qp, s), "int8 plane reorder launch")) return st;
     return hip_status(launch_gemm_t2(*w, qp, x_scale, m, y, y_dtype, s), "ternary GEMM launch");

@@ -170,11 +170,17 @@ __global__ __launch_bounds__(256) void gemv_t2_row_kernel(
 // whole 128-byte lines. Codes are decoded signed (the {0xff, 0x00, 0x01, 0x02}
 // byte table), so each chain of four MFMAs is the exact partial P[m,n,g]. The
 // per-wave fp32 results of a tile are summed in a fixed order through LDS.
-template <int NW, int GPW, int MAXT, int FR, typename TOut, bool PARTIALS, bool GS>
+//
+// SPLIT (split-K for long K): blockIdx.y selects the K slice of NW * GPW groups
+// starting at group blockIdx.y * NW * GPW; the workgroup's fixed-order sum over
+// its waves goes, unscaled, to part[blockIdx.y][M][N] (fp32), and
+// splitk_reduce_kernel adds the slices in slice order and applies x_scale.
+template <int NW, int GPW, int MAXT, int FR, typename TOut, bool PARTIALS, bool GS, bool SPLIT = false>
 __global__ __launch_bounds__(NW * 64) void gemv_t2_skinny_kernel(
     const uint8_t* __restrict__ codes, const __half* __restrict__ wscale,
     const int8_t* __restrict__ q, const float* __restrict__ x_scale, int M, int N, int K, int rpw,
-    TOut* __restrict__ y, int32_t* __restrict__ pout, int pm0, int pm1, int pn0, int pn1, int wg0) {
+    TOut* __restrict__ y, int32_t* __restrict__ pout, int pm0, int pm1, int pn0, int pn1, int wg0,
+    float* __restrict__ part) {
   // FR: accumulator registers that can hold a token row < M (registers 0..7
   // hold rows 0..15, so 8 when M <= 16, else 16). GS: x_scale holds one scale
   // per (row, 128-group), [M][K/128], and joins the weight scale in the fold.
@@ -184,7 +190,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_t2_skinny_kernel(
   const int n = lane & 31, h = lane >> 5;
   const int r0 = (blockIdx.x + wg0) * rpw;
   const int r1 = min(r0 + rpw, N);
-  const int gb = wave * GPW;
+  const int gb = (SPLIT ? blockIdx.y * NW * GPW : 0) + wave * GPW;
 
   // Loads in the order they are consumed (the hardware counts them in issue
   // order): activations, group scales and row scales first (small, mostly L2
@@ -231,7 +237,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_t2_skinny_kernel(
   // Row scales of the outputs this thread stores (the same rows for every tile).
   constexpr int OPT = (2 * FR + NW - 1) / NW;               // outputs per thread per tile pair
   float xsv[OPT];
-  if (!PARTIALS && !GS) {
+  if (!PARTIALS && !GS && !SPLIT) {
 #pragma unroll
     for (int k = 0; k < OPT; ++k) {
       const int rl = (tid + k * NW * 64) % (FR * 64);
@@ -326,9 +332,13 @@ __global__ __launch_bounds__(NW * 64) void gemv_t2_skinny_kernel(
       float v = 0.0f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) v += red[((tt * NW + w) * FR + r) * 64 + l];
-      if (!GS) v *= xsv[k];
+      if (!GS && !SPLIT) v *= xsv[k];
       const int mm = d_row(r, l >> 5), nn = r0 + 32 * (t0 + tt) + (l & 31);
-      if (o0 == o && mm < M && nn < r1) store_out(y + static_cast<size_t>(mm) * N + nn, v);
+      if (SPLIT) {
+        if (o0 == o && mm < M && nn < r1) part[(static_cast<size_t>(blockIdx.y) * M + mm) * N + nn] = v;
+      } else if (o0 == o && mm < M && nn < r1) {
+        store_out(y + static_cast<size_t>(mm) * N + nn, v);
+      }
     }
     __syncthreads();
   }
@@ -959,7 +969,7 @@ void t2_skinny_go(const bpw_weights& w, const int8_t* q, const float* xs, int m,
     auto kern = gemv_t2_skinny_kernel<NW, GPW, MAXT, 8, TOut, PARTIALS, GS>;
     const size_t lds = 2ull * NW * 8 * 64 * 4 + gs_lds;
     allow_lds(kern, lds);
-    kern<<<nwg, NW * 64, lds, s>>>(codes, sc, q, xs, m, n, k, rpw, y, pout, pm0, pm1, pn0, pn1, wg0);
+    kern<<<nwg, NW * 64, lds, s>>>(codes, sc, q, xs, m, n, k, rpw, y, pout, pm0, pm1, pn0, pn1, wg0, nullptr);
   } else {
     // (the dispatcher sends scaled-by-group products above 16 rows to the long
     // kernel: that form is not built, it would spill)
@@ -967,7 +977,7 @@ void t2_skinny_go(const bpw_weights& w, const int8_t* q, const float* xs, int m,
     auto kern = gemv_t2_skinny_kernel<NW, GPW, MAXT, FR, TOut, PARTIALS, GS>;
     const size_t lds = 2ull * NW * FR * 64 * 4 + gs_lds;
     allow_lds(kern, lds);
-    kern<<<nwg, NW * 64, lds, s>>>(codes, sc, q, xs, m, n, k, rpw, y, pout, pm0, pm1, pn0, pn1, wg0);
+    kern<<<nwg, NW * 64, lds, s>>>(codes, sc, q, xs, m, n, k, rpw, y, pout, pm0, pm1, pn0, pn1, wg0, nullptr);
   }
 }
 
@@ -992,6 +1002,57 @@ hipError_t t2_skinny(const bpw_weights& w, const int8_t* q, const float* xs, int
   BPW_SK(8, 1) BPW_SK(8, 2) BPW_SK(16, 1) BPW_SK(16, 2)
 #undef BPW_SK
   return hipErrorInvalidValue;
+}
+
+// y[m][n] = x_scale[m] * (part[0][m][n] + part[1][m][n] + ...), slices in order.
+template <typename TOut>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int splits, int M,
+                                                            int N, const float* __restrict__ x_scale,
+                                                            TOut* __restrict__ y) {
+  const size_t total = static_cast<size_t>(M) * N;
+  for (size_t i = blockIdx.x * 256ull + threadIdx.x; i < total; i += gridDim.x * 256ull) {
+    float v = part[i];
+    for (int sl = 1; sl < splits; ++sl) v += part[sl * total + i];
+    store_out(y + i, v * x_scale[i / N]);
+  }
+}
+
+// Split-K for 2 <= M <= 32 beyond 32 groups: slices of 32 groups (16 waves of
+// 2) side by side, rows per workgroup chosen so that row blocks x slices fill
+// the CUs about once.
+int t2_splits(int64_t k) { return static_cast<int>((k / 128 + 31) / 32); }
+bool t2_split_ok(int64_t m, int64_t k) { return m >= 2 && m <= 32 && k > 128 * 32; }
+
+template <typename TOut>
+hipError_t t2_split(const bpw_weights& w, const int8_t* q, const float* xs, int m, TOut* y, float* part,
+                    hipStream_t s) {
+  const int n = static_cast<int>(w.n), k = static_cast<int>(w.k);
+  const int splits = t2_splits(k);
+  // the fewest rows per workgroup (a multiple of 8, 16..128) whose row blocks
+  // times slices still fit one workgroup per CU; 128 if none does
+  const int cus = cu_count();
+  int rpw = 16;
+  while (rpw < 128 && static_cast<int64_t>((n + rpw - 1) / rpw) * splits > cus) rpw += 8;
+  const int nwg = (n + rpw - 1) / rpw;
+  const uint8_t* codes = static_cast<const uint8_t*>(w.codes);
+  const __half* sc = static_cast<const __half*>(w.scales);
+  const dim3 grid(nwg, splits);
+  auto go = [&](auto kern, int fr) {
+    const size_t lds = 2ull * 16 * fr * 64 * 4;
+    allow_lds(kern, lds);
+    kern<<<grid, 16 * 64, lds, s>>>(codes, sc, q, xs, m, n, k, rpw, y, nullptr, 0, 0, 0, 0, 0, part);
+  };
+  if (m <= 16) {
+    if (rpw <= 64) go(gemv_t2_skinny_kernel<16, 2, 2, 8, TOut, false, false, true>, 8);
+    else go(gemv_t2_skinny_kernel<16, 2, 4, 8, TOut, false, false, true>, 8);
+  } else {
+    if (rpw <= 64) go(gemv_t2_skinny_kernel<16, 2, 2, 16, TOut, false, false, true>, 16);
+    else go(gemv_t2_skinny_kernel<16, 2, 4, 16, TOut, false, false, true>, 16);
+  }
+  const size_t total = static_cast<size_t>(m) * n;
+  const int rblocks = static_cast<int>(std::min<size_t>((total + 255) / 256, 4096));
+  splitk_reduce_kernel<TOut><<<rblocks, 256, 0, s>>>(part, splits, m, n, xs, y);
+  return hipGetLastError();
 }
 
 template <int NW, int FR, typename TOut, bool PARTIALS, bool GS>
@@ -1024,7 +1085,7 @@ hipError_t t2_long(const bpw_weights& w, const int8_t* q, const float* xs, int m
 // per-(row, group) activation scales.
 template <typename TOut>
 hipError_t t2_dispatch(const bpw_weights& w, const int8_t* q, const float* xs, int m, TOut* y,
-                       bool gs, hipStream_t s) {
+                       bool gs, float* part, hipStream_t s) {
   if (gs) {
     if (t2_row_ok(m, w.k)) return t2_row<TOut, false, true>(w, q, xs, y, nullptr, 0, 0, s);
     // (above 16 rows the skinny kernel's four-tile form would spill with the scales)
@@ -1034,6 +1095,7 @@ hipError_t t2_dispatch(const bpw_weights& w, const int8_t* q, const float* xs, i
   }
   if (t2_row_ok(m, w.k)) return t2_row<TOut, false>(w, q, xs, y, nullptr, 0, 0, s);
   if (t2_skinny_ok(m, w.k)) return t2_skinny<TOut, false>(w, q, xs, m, y, nullptr, 0, 0, 0, 0, s);
+  if (part && t2_split_ok(m, w.k)) return t2_split<TOut>(w, q, xs, m, y, part, s);
   if (t2_long_ok(m, w.k)) return t2_long<TOut, false>(w, q, xs, m, y, nullptr, 0, 0, 0, 0, s);
   return hipErrorInvalidValue;
 }
@@ -1142,13 +1204,20 @@ bool gemv_w4_fits(int64_t m, int64_t k) {
 
 bool gemv_t2_group_fits(int64_t m, int64_t k) { return m >= 1 && m <= 32; }
 
+size_t gemv_t2_split_bytes(int64_t m, int64_t n, int64_t k, bool group_scales) {
+  if (group_scales || !t2_split_ok(m, k)) return 0;
+  return static_cast<size_t>(t2_splits(k)) * static_cast<size_t>(m) * static_cast<size_t>(n) * sizeof(float);
+}
+
 hipError_t launch_gemv_t2(const bpw_weights& w, const int8_t* q, const float* x_scale, int64_t m,
-                          void* y, int y_dtype, bool group_scales, hipStream_t s) {
+                          void* y, int y_dtype, bool group_scales, void* ws, size_t ws_bytes, hipStream_t s) {
   const int mi = static_cast<int>(m);
+  const size_t need = gemv_t2_split_bytes(m, w.n, w.k, group_scales);
+  float* part = need > 0 && ws && ws_bytes >= need ? static_cast<float*>(ws) : nullptr;
   switch (y_dtype) {
-    case BPW_F32: return t2_dispatch(w, q, x_scale, mi, static_cast<float*>(y), group_scales, s);
-    case BPW_F16: return t2_dispatch(w, q, x_scale, mi, static_cast<__half*>(y), group_scales, s);
-    default: return t2_dispatch(w, q, x_scale, mi, static_cast<uint16_t*>(y), group_scales, s);
+    case BPW_F32: return t2_dispatch(w, q, x_scale, mi, static_cast<float*>(y), group_scales, part, s);
+    case BPW_F16: return t2_dispatch(w, q, x_scale, mi, static_cast<__half*>(y), group_scales, part, s);
+    default: return t2_dispatch(w, q, x_scale, mi, static_cast<uint16_t*>(y), group_scales, part, s);
   }
 }
 

@@ -30,8 +30,12 @@ bool gemv_t2_fits(int64_t m, int64_t k);
 // group_scales: x_scale is [M][K/128] (one scale per row and group) instead of
 // [M]; only the shapes gemv_t2_group_fits accepts.
 bool gemv_t2_group_fits(int64_t m, int64_t k);
+// Split-K workspace (fp32 partial slices) the decode GEMV uses for 2 <= M <= 32
+// beyond 32 groups with row scales; 0 for other shapes. With less workspace
+// than this the long-K kernel runs instead.
+size_t gemv_t2_split_bytes(int64_t m, int64_t n, int64_t k, bool group_scales);
 hipError_t launch_gemv_t2(const bpw_weights& w, const int8_t* q, const float* x_scale, int64_t m,
-                          void* y, int y_dtype, bool group_scales, hipStream_t s);
+                          void* y, int y_dtype, bool group_scales, void* ws, size_t ws_bytes, hipStream_t s);
 hipError_t launch_gemv_t2_partials(const bpw_weights& w, const int8_t* q, int64_t m, int64_t m0,
                                    int64_t m1, int64_t n0, int64_t n1, int32_t* out,
                                    hipStream_t s);

@@ -123,6 +123,26 @@ def test_gemv_ternary_parity(m, k, n, out):
     assert_close(host(y), y_ref, out, f"gemv ternary m={m} k={k} n={n}")
 
 
+# Split-K decode (2 <= M <= 32 beyond 32 groups): slices of 32 groups side by
+# side, fp32 partials summed in slice order. Ragged last slices (2 and 1
+# groups), M past 16, and a repeat that must be bit-identical.
+@pytest.mark.parametrize("m,k,n", [(16, 14336, 4096), (5, 4352, 1000), (32, 8320, 777), (2, 16384, 64)])
+def test_gemv_ternary_split_k(m, k, n):
+    w = ternary_case(m, k, n, 900 + m + k + n, "f16")
+    pw = prepare(w)
+    need = bpw.workspace_size(pw, m, bpw.I8, bpw.PATH_GEMV)
+    assert need == -(-(-(-k // (128 * 32)) * m * n * 4) // 256) * 256      # slices x M x N fp32, 256-byte rounded
+    q, xs = bpw.quantize_rows(to_dev(w.x, "f32"))
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device=DEV)
+    y1 = bpw.gemv_packed(pw, q, xs, workspace=ws)
+    y2 = bpw.gemv_packed(pw, q, xs, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2), "split-K result changed between calls"
+    q_ref, xs_ref = quant.quantize_rows(w.x)
+    _, y_ref = reference.ternary_int8_product(q_ref, xs_ref, w.codes, w.scales)
+    assert_close(host(y1), y_ref, "f16", f"gemv ternary split-K m={m} k={k} n={n}")
+
+
 @pytest.mark.parametrize("m,k,n", [(1, 4096, 1000), (1, 16384, 77), (1, 512, 256), (2, 640, 333),
                                    (16, 4096, 14336), (32, 8192, 3000), (9, 3072, 20000), (20, 4096, 700),
                                    (1, 20480, 300), (8, 14336, 1000)])

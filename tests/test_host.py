@@ -212,6 +212,14 @@ def test_workspace_sizes():
     assert need.value == 0
     assert lib.bpw_workspace_size(ctypes.byref(w), 2048, bpw.I8, bpw.PATH_GEMM, ctypes.byref(need)) == 0
     assert need.value == 2048 * 4096
+    # ternary decode beyond 32 groups, 2 <= M <= 32: fp32 split-K slices of 32 groups
+    wl = _weights(k=14336, n=4096)
+    assert lib.bpw_workspace_size(ctypes.byref(wl), 16, bpw.I8, bpw.PATH_GEMV, ctypes.byref(need)) == 0
+    assert need.value == 4 * 16 * 4096 * 4
+    assert lib.bpw_workspace_size(ctypes.byref(wl), 1, bpw.I8, bpw.PATH_GEMV, ctypes.byref(need)) == 0
+    assert need.value == 0                                             # M = 1: the row kernel
+    assert lib.bpw_workspace_size(ctypes.byref(wl), 16, bpw.I8G, bpw.PATH_GEMV, ctypes.byref(need)) == 0
+    assert need.value == 0                                             # group scales: long-K kernel
     wp = _weights(bpw.INT4_ZP, k=5120, zeros=True, perm=True)
     assert lib.bpw_workspace_size(ctypes.byref(wp), 8, bpw.F16, bpw.PATH_GEMV, ctypes.byref(need)) == 0
     assert need.value == 8 * 5120 * 2
