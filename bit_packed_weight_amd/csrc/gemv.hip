@@ -1017,7 +1017,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   }
 }
 
-// Split-K for 2 <= M <= 32 beyond 32 groups: slices of 32 groups (16 waves of
+// Split-K for 2 <= M <= 32 beyond 32 groups ("Kernel experiments: recorded
+// evidence", Tests 21 and 30: more blocks for small-output shapes, partial sums
+// added in a fixed order by a second kernel): slices of 32 groups (16 waves of
 // 2) side by side, rows per workgroup chosen so that row blocks x slices fill
 // the CUs about once.
 int t2_splits(int64_t k) { return static_cast<int>((k / 128 + 31) / 32); }

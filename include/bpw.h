@@ -190,8 +190,9 @@ int bpw_workspace_size(const bpw_weights* w, int64_t m, int x_dtype, int entry, 
  * Split-K (ternary x I8, 2 <= M <= 32, K > 4096): K is cut into slices of 32
  * groups computed side by side; the workspace holds their fp32 sums
  * [slices][M][N], added in slice order by a second launch on the same stream
- * (deterministic; the "Kernel experiments" page's split-K with a fixed-order
- * reduce for long-K decode shapes).
+ * (deterministic). "Kernel experiments: recorded evidence", Test 21: split-K
+ * gives the small-output down projection more blocks, and a second kernel adds
+ * the partial sums in a fixed order; Test 30: split-K for small-output shapes.
  */
 int bpw_gemv_packed(const bpw_weights* w, const void* x, int x_dtype, const float* x_scale,
                     int64_t m, void* y, int y_dtype, void* workspace, size_t workspace_bytes,
