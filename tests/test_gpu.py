@@ -254,6 +254,28 @@ def test_gemv_w4_parity(fmt, x_dtype, act_order, m, k, n):
     assert_close(host(y), w4_reference(w, rounded=False), x_dtype, f"gemv {fmt} {x_dtype} m={m} k={k} n={n}")
 
 
+# Bit-identical repeats, outputs of one token row independent of the other
+# rows, and every output written over a NaN-poisoned buffer: the M = 1 row
+# kernel (act order), the skinny M = 8 kernel, and the prefill GEMM.
+@pytest.mark.parametrize("entry,m,k,n", [("gemv", 1, 5120, 700), ("gemv", 8, 5120, 700), ("gemm", 300, 1024, 520)])
+def test_w4_determinism_row_independence(entry, m, k, n):
+    w = w4_case("int4_zp", m, k, n, 600 + m + k + n, True, "f16")
+    pw = prepare(w)
+    fn = bpw.gemv_packed if entry == "gemv" else bpw.gemm_packed
+    x = to_dev(w.x, "f16")
+    y1 = torch.full((m, n), float("nan"), dtype=torch.float16, device=DEV)
+    fn(pw, x, out=y1)
+    y2 = fn(pw, x)
+    x2 = x.clone()
+    if m > 1:
+        x2[1:] = torch.randn(x2[1:].shape, device=DEV).to(torch.float16)
+    y3 = fn(pw, x2)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y1).all()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(y1[0].view(torch.int16), y3[0].view(torch.int16))
+
+
 @pytest.mark.parametrize("x_dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("m,k,n", [(1, 5120, 700), (8, 5120, 700), (3, 2048, 5000)])
 def test_gemv_w4_f32_out(x_dtype, m, k, n):
