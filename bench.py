@@ -233,6 +233,41 @@ def bench_ternary_prefill(bpw, synth, torch, np, steps, warmup):
             "TOP_s": ops / (ms * 1e9), "frac_int8_mfma_peak": ops / (ms * 1e9) / INT8_PEAK_TOPS}
 
 
+def bench_dense_reference(torch, steps=20, warmup=5):
+    """The platform's dense GEMMs (hipBLASLt through torch) at the two prefill shapes, with
+    no quantisation: context for the MFMA fractions, not part of the library. Event-timed
+    loops (these calls refuse graph capture here)."""
+    def timed(fn, n, w):
+        for i in range(w):
+            fn(i)
+        torch.cuda.synchronize()
+        st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        st.record()
+        for i in range(n):
+            fn(i)
+        en.record()
+        torch.cuda.synchronize()
+        return st.elapsed_time(en) / n
+    out = []
+    m, k, n = 2048, 4096, 14336
+    a = torch.randn(m, k, device="cuda").to(torch.bfloat16)
+    ws = [torch.randn(n, k, device="cuda").to(torch.bfloat16) for _ in range(4)]
+    y = torch.empty(m, n, device="cuda", dtype=torch.bfloat16)
+    ms = timed(lambda i: torch.matmul(a, ws[i % 4].t(), out=y), steps, warmup)
+    out.append({"workload": "reference_dense_bf16_gemm", "M": m, "K": k, "N": n, "us_per_call": ms * 1e3,
+                "TFLOP_s": 2.0 * m * n * k / (ms * 1e9), "frac_bf16_mfma_peak": 2.0 * m * n * k / (ms * 1e9) / BF16_PEAK_TFLOPS,
+                "kind": "platform reference (hipBLASLt, bf16 weights, no dequant)"})
+    del a, ws, y
+    m, k, n = 4096, 8192, 28672
+    qa = torch.randint(-127, 128, (m, k), device="cuda", dtype=torch.int8)
+    qb = [torch.randint(-1, 2, (n, k), device="cuda", dtype=torch.int8).t() for _ in range(2)]   # column-major B
+    ms = timed(lambda i: torch._int_mm(qa, qb[i % 2]), max(steps // 3, 2), 2)
+    out.append({"workload": "reference_dense_int8_gemm", "M": m, "K": k, "N": n, "us_per_call": ms * 1e3,
+                "TOP_s": 2.0 * m * n * k / (ms * 1e9), "frac_int8_mfma_peak": 2.0 * m * n * k / (ms * 1e9) / INT8_PEAK_TOPS,
+                "kind": "platform reference (hipBLASLt, int8 weights, int32 out, no fold)"})
+    return out
+
+
 def cpu_baseline(synth, np, budget_s=12.0):
     """The CPU oracle (unchanged) on the headline workload, repeated for ~budget_s."""
     from oracle import quant, reference  # noqa: PLC0415 (test infrastructure, this leg only)
@@ -297,6 +332,10 @@ def main():
             log(f"[bench] {json.dumps(r)}")
             extra.append(r)
             torch.cuda.empty_cache()
+        for r in bench_dense_reference(torch):
+            log(f"[bench] {json.dumps(r)}")
+            extra.append(r)
+        torch.cuda.empty_cache()
     cpu = None if args.no_cpu else cpu_baseline(synth, np)
     if cpu:
         log(f"[bench] cpu oracle: {cpu['value']:.3f} GB/s on {cpu['cores']} threads")
