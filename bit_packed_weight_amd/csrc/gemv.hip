@@ -17,6 +17,8 @@
 // fp16) - #6": a decode GEMV that reads each weight once; the zero point is
 // subtracted from the code exactly (code - zero is an integer in -15..15) and
 // the group scale is applied to the fp32 group partial.
+#include <atomic>
+
 #include "device.h"
 #include "launch.h"
 
@@ -931,17 +933,18 @@ hipError_t t2_row(const bpw_weights& w, const int8_t* q, const float* xs, TOut* 
 }
 
 // Compute units of the current device (the skinny kernel runs one workgroup per
-// CU); queried once per device.
+// CU); queried once per device. Callers on several host threads may race to
+// fill an entry; they store the same value.
 int cu_count() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int c = 0;
+  int c = cached[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
     if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
-    cached[dev] = c;
+    cached[dev].store(c, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return c;
 }
 
 // The skinny kernel holds a wave's whole K slice in registers: up to 32
