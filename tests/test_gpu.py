@@ -298,6 +298,31 @@ def test_gemm_w4_parity(fmt, x_dtype, act_order, m, k, n):
     assert_close(host(y), w4_reference(w, rounded=True), x_dtype, f"gemm {fmt} {x_dtype} m={m} k={k} n={n}")
 
 
+# Degenerate shapes: one output row, one 128-group, and M on both sides of the
+# decode entry's hand-over to the GEMM kernels (M = 32 decode, M = 33 GEMM).
+@pytest.mark.parametrize("entry,m,k,n", [("gemv", 1, 128, 1), ("gemv", 32, 128, 1), ("gemv", 33, 256, 65),
+                                         ("gemv", 32, 4096, 33), ("gemm", 1, 128, 1), ("gemm", 33, 128, 257)])
+def test_ternary_degenerate_shapes(entry, m, k, n):
+    w = ternary_case(m, k, n, 1100 + m + k + n, "f32")
+    _, q, _, y, y_ref = run_ternary(w, entry)
+    assert y.shape == (m, n)
+    assert_close(host(y), y_ref, "f32", f"{entry} ternary m={m} k={k} n={n}")
+
+
+@pytest.mark.parametrize("fmt,x_dtype,entry,m,k,n", [("int4_zp", "f16", "gemv", 1, 1024, 1), ("int4_sym", "bf16", "gemv", 16, 2048, 1),
+                                                     ("int4_zp", "f16", "gemv", 33, 128, 40), ("int4_sym", "bf16", "gemm", 1, 128, 1)])
+def test_w4_degenerate_shapes(fmt, x_dtype, entry, m, k, n):
+    w = w4_case(fmt, m, k, n, 1200 + m + k + n, fmt == "int4_zp", x_dtype)
+    pw = prepare(w)
+    fn = bpw.gemv_packed if entry == "gemv" else bpw.gemm_packed
+    y = fn(pw, to_dev(w.x, x_dtype))
+    torch.cuda.synchronize()
+    assert y.shape == (m, n)
+    # the GEMM kernels (entry gemm, or M > 32 through the decode entry) round W to the activation dtype
+    rounded = entry == "gemm" or m > 32
+    assert_close(host(y), w4_reference(w, rounded=rounded), x_dtype, f"{entry} {fmt} m={m} k={k} n={n}")
+
+
 # ------------------------------------------------------------------ named workloads, full size
 def test_workload_ternary_tiny_full():
     w = synth.ternary_tiny()
