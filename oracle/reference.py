@@ -16,6 +16,10 @@ is a small integer times an fp16/bf16 scale) and multiplies with BLAS in fp64.
   K rows by group so that ``x[:, perm] @ W[perm] == x @ W``; a ``g_idx``
   whose sorted groups are not contiguous runs of the group size is refused
   with the invariant named.
+* 4-bit weights x int8 activations -- "TensorFold PR #1176" (the int8
+  prompt GEMM): per group an exact integer dot of the int8 activations with
+  the codes, the weight offset entering through the group's activation sum;
+  here the exact partial ``sum q * (code - zero)`` folded like the ternary one.
 * Rounded dequantisation for the large-M float path -- the pages' float
   kernels round the dequantised weight to the activation dtype before the
   product ("Kernel experiments", Test 5's batched GEMV; the mate PR's note
@@ -134,4 +138,46 @@ def ternary_int8_product_group_scales(q, x_scale_groups, codes, scales):
     s = np.asarray(scales, np.float64)
     xs = np.asarray(x_scale_groups, np.float64)
     y = np.einsum("mng,ng,mg->mn", p.astype(np.float64), s, xs)
+    return p, y
+
+
+# ---------------------------------------------------------------- 4-bit x int8
+def int4_partials(q: np.ndarray, codes: np.ndarray, zeros=None, g_idx=None) -> np.ndarray:
+    """Exact int group partials of 4-bit weights against int8 activations.
+
+    "TensorFold PR #1176" (the int8 prompt GEMM, "What changes"): an affine
+    4-bit code is already an exact int8, so each group's dot with int8
+    activations is an exact integer, and the weight's offset enters through
+    the group's activation sum. With the weights of this library written as
+    ``(code - zero) * scale`` the group partial is
+
+        P[m, n, g] = sum over k in group g of q[m, k] * (code[n, k] - zero[n, g])
+
+    with zero = 8 for symmetric codes and group(k) = g_idx[k] under act order,
+    else k // 128. Each group is one fp64 matmul of integers below 2**53 in
+    magnitude (|P| <= 127 * 15 * 128), so the result is exact; returned as int64.
+    """
+    m, k = q.shape
+    n = codes.shape[0]
+    groups = k // GROUP
+    grp = np.arange(k) // GROUP if g_idx is None else np.asarray(g_idx, np.int64)
+    qf = q.astype(np.float64)
+    out = np.empty((m, n, groups), dtype=np.int64)
+    for g in range(groups):
+        cols = np.flatnonzero(grp == g)
+        z = 8.0 if zeros is None else np.asarray(zeros, np.float64)[:, g][:, None]
+        wg = codes[:, cols].astype(np.float64) - z
+        out[:, :, g] = (qf[:, cols] @ wg.T).astype(np.int64)
+    return out
+
+
+def int4_int8_product(q, x_scale, codes, scales, zeros=None, g_idx=None):
+    """y[m,n] = x_scale[m] * sum_g scale[n,g] * P[m,n,g] (fp64), P from ``int4_partials``.
+
+    Returns (P, y). The activation side is int8 with one scale per row, the
+    same activation operand as the ternary int8 path.
+    """
+    p = int4_partials(q, codes, zeros, g_idx)
+    s = np.asarray(scales, np.float64)
+    y = np.einsum("mng,ng->mn", p.astype(np.float64), s) * np.asarray(x_scale, np.float64)[:, None]
     return p, y

@@ -430,3 +430,94 @@ def test_workload_generators_shapes_and_ranges():
     assert perm.shape == (512,)
     w4 = synth.int4_sym("t", 3, 4, 256, 8)
     assert w4.x.dtype == np.uint16 and w4.scales.dtype == np.uint16
+
+
+# ------------------------------------------------------------------ 4-bit x int8
+def _brute_int4_partials(q, codes, zeros, g_idx):
+    m, k = q.shape
+    n = codes.shape[0]
+    out = np.zeros((m, n, k // 128), dtype=np.int64)
+    for mi in range(m):
+        for ni in range(n):
+            for kk in range(k):
+                g = kk // 128 if g_idx is None else int(g_idx[kk])
+                z = 8 if zeros is None else int(zeros[ni, g])
+                out[mi, ni, g] += int(q[mi, kk]) * (int(codes[ni, kk]) - z)
+    return out
+
+
+@pytest.mark.parametrize("m,k,n,zp,act", [(1, 128, 3, False, False), (3, 256, 4, True, False),
+                                          (2, 256, 2, True, True), (2, 384, 3, False, True)])
+def test_int4_partials_brute_force(m, k, n, zp, act):
+    rng = np.random.default_rng(7000 + 10 * m + n + k)
+    q = rng.integers(-127, 128, size=(m, k), dtype=np.int8)
+    codes = rng.integers(0, 16, size=(n, k), dtype=np.uint8)
+    zeros = rng.integers(0, 16, size=(n, k // 128), dtype=np.uint8) if zp else None
+    g_idx = _valid_gidx(rng, k) if act else None
+    np.testing.assert_array_equal(reference.int4_partials(q, codes, zeros, g_idx),
+                                  _brute_int4_partials(q, codes, zeros, g_idx))
+
+
+def test_int4_partials_extremes():
+    # |P| reaches 127 * 15 * 128 with q = -127, code 0, zero 15 (and the opposite sign).
+    k = 256
+    q = np.full((2, k), -127, np.int8)
+    q[1] = 127
+    codes = np.zeros((2, k), np.uint8)
+    codes[1] = 15
+    zeros = np.array([[15, 15], [0, 0]], np.uint8)
+    p = reference.int4_partials(q, codes, zeros)
+    assert p[0, 0, 0] == 127 * 15 * 128 and p[1, 0, 0] == -127 * 15 * 128
+    assert p[0, 1, 1] == -127 * 15 * 128 and p[1, 1, 1] == 127 * 15 * 128
+
+
+def test_int4_int8_product_matches_affine_split_exactly():
+    # The page's form: per group scale * (q . code) plus the offset -scale * zero
+    # times the group's activation sum, in exact rationals; power-of-two scales
+    # keep the oracle's fp64 sums exact.
+    rng = np.random.default_rng(7101)
+    m, k, n = 2, 384, 3
+    q = rng.integers(-127, 128, size=(m, k), dtype=np.int8)
+    codes = rng.integers(0, 16, size=(n, k), dtype=np.uint8)
+    zeros = rng.integers(0, 16, size=(n, 3), dtype=np.uint8)
+    scales = np.ldexp(1.0, rng.integers(-12, -4, size=(n, 3))).astype(np.float16)
+    xs = np.ldexp(1.0, rng.integers(-9, -3, size=m)).astype(np.float32)
+    g_idx = _valid_gidx(rng, k)
+    _, y = reference.int4_int8_product(q, xs, codes, scales, zeros, g_idx)
+    for mi in range(m):
+        for ni in range(n):
+            acc = Fraction(0)
+            for g in range(3):
+                cols = [kk for kk in range(k) if g_idx[kk] == g]
+                dot = sum(int(q[mi, kk]) * int(codes[ni, kk]) for kk in cols)
+                qsum = sum(int(q[mi, kk]) for kk in cols)
+                s = Fraction(float(scales[ni, g]))
+                acc += s * dot + (-s * int(zeros[ni, g])) * qsum
+            assert Fraction(float(y[mi, ni])) == Fraction(float(xs[mi])) * acc
+
+
+def test_int4_int8_product_equals_dequantised_matmul():
+    # Against the (separately pinned) dequantised weights: y = xs * (q @ W^T).
+    wl = synth.int4_zp_actorder("t", 31, 3, 512, 7)
+    rng = np.random.default_rng(7102)
+    q = rng.integers(-127, 128, size=(3, 512), dtype=np.int8)
+    xs = rng.uniform(0.001, 0.05, size=3).astype(np.float32)
+    _, y = reference.int4_int8_product(q, xs, wl.codes, wl.scales, wl.zeros, wl.g_idx)
+    w = reference.weights_int4(wl.codes, wl.scales, wl.zeros, wl.g_idx)
+    want = xs.astype(np.float64)[:, None] * reference.product(q.astype(np.float64), w)
+    np.testing.assert_allclose(y, want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+
+
+def test_int4_partials_act_order_sorted_form_and_negative_control():
+    # The sorted form (activations and codes permuted, group j // 128) gives the
+    # same partials; reading the zero points by k // 128 in the original order does not.
+    rng = np.random.default_rng(7103)
+    m, k, n = 2, 512, 5
+    q = rng.integers(-127, 128, size=(m, k), dtype=np.int8)
+    codes = rng.integers(0, 16, size=(n, k), dtype=np.uint8)
+    zeros = rng.integers(0, 16, size=(n, 4), dtype=np.uint8)
+    g_idx = _valid_gidx(rng, k)
+    perm = reference.act_order_perm(g_idx, k)
+    p = reference.int4_partials(q, codes, zeros, g_idx)
+    np.testing.assert_array_equal(reference.int4_partials(q[:, perm], codes[:, perm], zeros, None), p)
+    assert not np.array_equal(reference.int4_partials(q, codes, zeros, None), p)
