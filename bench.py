@@ -233,6 +233,20 @@ def bench_ternary_prefill(bpw, synth, torch, np, steps, warmup):
             "TOP_s": ops / (ms * 1e9), "frac_int8_mfma_peak": ops / (ms * 1e9) / INT8_PEAK_TOPS}
 
 
+def bench_w4a8_prefill(bpw, synth, torch, np, steps, warmup):
+    """The 4-bit prefill weights against int8 activation rows (the int8 matrix core)."""
+    w = synth.w4a16_prefill()
+    planes = bpw.prepare_packed_host(bpw.INT4_SYM, w.codes, w.scales, scale_dtype=bpw.BF16)
+    copies = rotated_copies(bpw, planes, 512 << 20, max_copies=18)
+    q, xs = bpw.quantize_rows(to_dev(w.x, "bf16", torch, np))
+    y = torch.empty((w.m, w.n), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(bpw.workspace_size(copies[0], w.m, bpw.I8, bpw.PATH_GEMM), dtype=torch.uint8, device="cuda")
+    ms = time_graph(torch, lambda i: bpw.gemm_packed(copies[i % len(copies)], q, xs, out=y, workspace=ws), steps, warmup)
+    ops = 2.0 * w.m * w.n * w.k
+    return {"workload": "w4a8_prefill_gemm", "M": w.m, "K": w.k, "N": w.n, "us_per_call": ms * 1e3,
+            "TOP_s": ops / (ms * 1e9), "frac_int8_mfma_peak": ops / (ms * 1e9) / INT8_PEAK_TOPS}
+
+
 def bench_dense_reference(torch, steps=20, warmup=5):
     """The platform's dense GEMMs (hipBLASLt through torch) at the two prefill shapes, with
     no quantisation: context for the MFMA fractions, not part of the library. Event-timed
@@ -326,7 +340,8 @@ def main():
         runs = ((bench_ternary_decode_m, 900, 300, {"m": 16}), (bench_ternary_long_k, 600, 200, {"m": 16}),
                 (bench_ternary_decode_groups, 900, 300, {"m": 1}),
                 (bench_ternary_decode_groups, 900, 300, {"m": 16}), (bench_w4_decode, 900, 300, {"m": 1}),
-                (bench_w4_decode, 900, 300, {"m": 8}), (bench_w4_prefill, 30, 6, {}), (bench_ternary_prefill, 12, 3, {}))
+                (bench_w4_decode, 900, 300, {"m": 8}), (bench_w4_prefill, 30, 6, {}), (bench_w4a8_prefill, 30, 6, {}),
+                (bench_ternary_prefill, 12, 3, {}))
         for fn, steps, warm, kw in runs:
             r = fn(bpw, synth, torch, np, steps, warm, **kw)
             log(f"[bench] {json.dumps(r)}")

@@ -87,9 +87,14 @@ int check_product(const bpw_weights* w, const void* x, int x_dtype, const float*
     if (!x_scale) return fail(BPW_EINVAL, x_dtype == BPW_I8 ? "int8 activations need x_scale [M]"
                                                             : "int8 activations need x_scale [M][K/128]");
     if (!aligned(x_scale, 4)) return fail(BPW_EALIGN, "x_scale must be 4-byte aligned");
+  } else if (x_dtype == BPW_I8) {
+    // "TensorFold PR #1176": 4-bit weights against int8 activations on the int8 matrix core.
+    if (!x_scale) return fail(BPW_EINVAL, "int8 activations need x_scale [M]");
+    if (!aligned(x_scale, 4)) return fail(BPW_EALIGN, "x_scale must be 4-byte aligned");
   } else {
     if (x_dtype != BPW_F16 && x_dtype != BPW_BF16)
-      return fail(BPW_EUNSUPPORTED, "4-bit weights take fp16 or bf16 activations (x_dtype %d given)", x_dtype);
+      return fail(BPW_EUNSUPPORTED, "4-bit weights take fp16, bf16 or int8 (row scale) activations (x_dtype %d given)",
+                  x_dtype);
     if (x_dtype != w->scale_dtype)
       return fail(BPW_EUNSUPPORTED, "4-bit weights need scale dtype == activation dtype");
     if (x_scale) return fail(BPW_EINVAL, "x_scale must be NULL for fp16/bf16 activations");
@@ -108,6 +113,7 @@ size_t workspace_need(const bpw_weights* w, int64_t m, int x_dtype, int entry) {
       return round_up(gemv_t2_split_bytes(m, w->n, w->k, false));
     return round_up(mk);                       // plane-ordered int8 activations
   }
+  if (x_dtype == BPW_I8) return round_up(mk);  // nibble-ordered int8 activations
   return w->perm ? round_up(mk * 2) : 0;       // gathered 16-bit activations
 }
 
@@ -132,9 +138,18 @@ int run_product(bool gemv, const bpw_weights* w, const void* x, int x_dtype, con
     if (!gemv_t2_group_fits(m, w->k))
       return fail(BPW_EUNSUPPORTED, "per-group activation scales need M <= 32 (M=%lld)", (long long)m);
   }
+  if (is_int4(w->fmt) && x_dtype == BPW_I8 && gemv)
+    return fail(BPW_EUNSUPPORTED, "4-bit weights with int8 activations run through bpw_gemm_packed only");
   if (int st = check_workspace(w, m, x_dtype, entry, ws, ws_bytes)) return st;
   if (int st = check_device()) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (is_int4(w->fmt) && x_dtype == BPW_I8) {
+    int8_t* qn = static_cast<int8_t*>(ws);
+    if (int st = hip_status(launch_int8_nibbles(static_cast<const int8_t*>(x), w->perm, m, w->k, qn, s),
+                            "int8 nibble reorder launch"))
+      return st;
+    return hip_status(launch_gemm_w4a8(*w, qn, x_scale, m, y, y_dtype, s), "4-bit x int8 GEMM launch");
+  }
   if (w->fmt == BPW_TERNARY2) {
     const int8_t* q = static_cast<const int8_t*>(x);
     if (x_dtype == BPW_I8G)
@@ -236,7 +251,6 @@ extern "C" int bpw_partials(const bpw_weights* w, const int8_t* q, int64_t m, in
                             int64_t m0, int64_t m1, int64_t n0, int64_t n1, int32_t* out,
                             void* workspace, size_t workspace_bytes, void* stream) {
   if (int st = check_weights(w)) return st;
-  if (w->fmt != BPW_TERNARY2) return fail(BPW_EUNSUPPORTED, "partials are defined for ternary weights only");
   if (!q || !out) return fail(BPW_EINVAL, "q / out is NULL");
   if (!aligned(q, 16)) return fail(BPW_EALIGN, "q must be 16-byte aligned");
   if (!aligned(out, 4)) return fail(BPW_EALIGN, "out must be 4-byte aligned");
@@ -245,6 +259,8 @@ extern "C" int bpw_partials(const bpw_weights* w, const int8_t* q, int64_t m, in
     return fail(BPW_ESHAPE, "window [%lld,%lld) x [%lld,%lld) outside M=%lld, N=%lld", (long long)m0,
                 (long long)m1, (long long)n0, (long long)n1, (long long)m, (long long)w->n);
   if (path != BPW_PATH_GEMV && path != BPW_PATH_GEMM) return fail(BPW_EINVAL, "unknown path %d", path);
+  if (w->fmt != BPW_TERNARY2 && path != BPW_PATH_GEMM)
+    return fail(BPW_EUNSUPPORTED, "partials of 4-bit weights come from the GEMM core only");
   if (path == BPW_PATH_GEMV && !gemv_t2_fits(m, w->k))
     return fail(BPW_ESHAPE, "the GEMV core takes M <= 32");
   if (path == BPW_PATH_GEMM) {
@@ -255,6 +271,10 @@ extern "C" int bpw_partials(const bpw_weights* w, const int8_t* q, int64_t m, in
   if (path == BPW_PATH_GEMV)
     return hip_status(launch_gemv_t2_partials(*w, q, m, m0, m1, n0, n1, out, s), "GEMV partials launch");
   int8_t* qp = static_cast<int8_t*>(workspace);
+  if (w->fmt != BPW_TERNARY2) {
+    if (int st = hip_status(launch_int8_nibbles(q, w->perm, m, w->k, qp, s), "int8 nibble reorder launch")) return st;
+    return hip_status(launch_gemm_w4a8_partials(*w, qp, m, m0, m1, n0, n1, out, s), "GEMM partials launch");
+  }
   if (int st = hip_status(launch_int8_planes(q, m, w->k, qp, s), "int8 plane reorder launch")) return st;
   return hip_status(launch_gemm_t2_partials(*w, qp, m, m0, m1, n0, n1, out, s), "GEMM partials launch");
 }

@@ -85,6 +85,22 @@ __device__ __forceinline__ uint32_t code_plane_signed(uint32_t w, int t) {
   return perm_b32(0u, 0x020100FFu, code_plane(w, t));
 }
 
+// 4-bit codes of one packed dword (byte b: code 2b in the low nibble, code
+// 2b + 1 in the high one) as signed bytes code - zero, with zadd holding
+// 0x80 - zero in every byte: code + 0x80 - zero stays within 0x71..0x8f (no
+// carry into the next byte), and flipping bit 7 gives the two's complement of
+// code - zero. nib_lo gives codes 0, 2, 4, 6 of the dword, nib_hi codes 1, 3, 5, 7.
+__device__ __forceinline__ uint32_t nib_lo_signed(uint32_t w, uint32_t zadd) {
+  return ((w & 0x0F0F0F0Fu) + zadd) ^ 0x80808080u;
+}
+__device__ __forceinline__ uint32_t nib_hi_signed(uint32_t w, uint32_t zadd) {
+  return (((w >> 4) & 0x0F0F0F0Fu) + zadd) ^ 0x80808080u;
+}
+// The matching activation order: of 8 bytes (a = bytes 0..3, b = bytes 4..7),
+// the even ones, then the odd ones.
+__device__ __forceinline__ uint32_t even_bytes(uint32_t a, uint32_t b) { return perm_b32(b, a, 0x06040200u); }
+__device__ __forceinline__ uint32_t odd_bytes(uint32_t a, uint32_t b) { return perm_b32(b, a, 0x07050301u); }
+
 // Workgroup id remap so that consecutive logical tiles land on the same XCD
 // (hardware dispatches workgroup i to XCD i % 8).
 __device__ __forceinline__ int xcd_swizzle(int bid, int nblocks) {

@@ -20,6 +20,15 @@
 // one 32-row tile ahead. Weights never touch LDS: each lane loads its own 16
 // code bytes per 32-row weight tile and group one group ahead and decodes them
 // straight into B operands.
+//
+// The same kernel takes 4-bit weights ("TensorFold PR #1176", the int8 prompt
+// GEMM: an affine 4-bit code is an exact int8, so the group dot runs on the
+// int8 matrix core). Each lane then loads 32 code bytes per weight tile and
+// group and decodes every nibble to the signed byte code - zero (zero 8 for
+// symmetric codes), so the int32 MFMA result is again the exact partial
+// P[m,n,g] = sum q * (code - zero) and the fold is unchanged. The activations
+// come in nibble order: within each 8 bytes of a row, the even-indexed
+// elements, then the odd ones, in the chunk arrangement of the plane order.
 #include "device.h"
 #include "launch.h"
 #include "store.h"
@@ -66,15 +75,26 @@ __device__ __forceinline__ void tile_coords(int t, int mtiles, int ntiles, int& 
   nt = r / gs;
 }
 
-template <typename TOut, bool PARTIALS>
+// Weight formats of the kernel: ternary codes, 4-bit symmetric (zero 8), 4-bit
+// with a zero point per (row, group).
+enum { WF_T2 = 0, WF_I4 = 1, WF_I4Z = 2 };
+
+template <typename TOut, bool PARTIALS, int WF>
 __global__ __launch_bounds__(NT, 1) void gemm_t2_kernel(
     const int8_t* __restrict__ qp, const float* __restrict__ x_scale,
-    const uint8_t* __restrict__ codes, const __half* __restrict__ wscale, int M, int N, int K,
+    const uint8_t* __restrict__ codes, const uint16_t* __restrict__ wscale,
+    const uint8_t* __restrict__ zeros, int bf_scale, int M, int N, int K,
     TOut* __restrict__ y, int32_t* __restrict__ pout, int pm0, int pm1, int pn0, int pn1,
     int mt0, int mtiles, int nt0, int ntiles) {
   extern __shared__ __align__(16) uint8_t smem[];
+  constexpr bool W4 = WF != WF_T2;
   const int G = K >> 7;
-  const int KB = K >> 2;
+  const int KB = W4 ? (K >> 1) : (K >> 2);
+  const int ZB = (G + 1) >> 1;
+  const bool bfs = W4 && bf_scale;
+  auto scale_f32 = [&](uint16_t bits) __attribute__((always_inline)) {
+    return bfs ? bf16_to_f32(bits) : __half2float(__builtin_bit_cast(__half, bits));
+  };
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int mt, nt;
   tile_coords(xcd_swizzle(blockIdx.x, mtiles * ntiles), mtiles, ntiles, mt, nt);
@@ -118,36 +138,66 @@ __global__ __launch_bounds__(NT, 1) void gemm_t2_kernel(
     for (int t = 0; t < 4; ++t) ds_read_agpr<OFF>(dst[t], a_addr[t]);
   };
 
-  // B: this lane's two weight rows (one per 32-row tile of the wave).
+  // B: this lane's two weight rows (one per 32-row tile of the wave). Lane
+  // half h takes weights [64h, 64h + 64) of each group: 16 ternary or 32
+  // 4-bit code bytes.
   const uint8_t* b_src[2];
-  const __half* s_src[2];
+  const uint16_t* s_src[2];
+  const uint8_t* z_src[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const size_t row = static_cast<size_t>(min(n0 + 64 * wave + 32 * j + n, N - 1));
-    b_src[j] = codes + row * KB + 16 * h;
+    b_src[j] = codes + row * KB + (W4 ? 32 : 16) * h;
     s_src[j] = wscale + row * G;
+    z_src[j] = WF == WF_I4Z ? zeros + row * ZB : nullptr;
   }
   // Raw bytes only (the scale is converted a group later, so that nothing
   // waits on these loads before it has to).
   struct Raw {
-    v4u c[2];
-    __half s[2];
+    v4u c[2][W4 ? 2 : 1];
+    uint16_t s[2];
+    uint32_t z[2];        // zero-point byte of the row (two groups), and the group's nibble shift
+    uint32_t zsh;
   };
   auto raw_load = [&](Raw& r, int g) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      r.c[j] = *reinterpret_cast<const v4u*>(b_src[j] + g * 32);
+      if (W4) {
+        r.c[j][0] = *reinterpret_cast<const v4u*>(b_src[j] + g * 64);
+        r.c[j][W4 ? 1 : 0] = *reinterpret_cast<const v4u*>(b_src[j] + g * 64 + 16);
+      } else {
+        r.c[j][0] = *reinterpret_cast<const v4u*>(b_src[j] + g * 32);
+      }
       r.s[j] = s_src[j][g];
+      r.z[j] = WF == WF_I4Z ? static_cast<uint32_t>(z_src[j][g >> 1]) : 0u;
     }
+    r.zsh = 4u * static_cast<uint32_t>(g & 1);
   };
-  // 16 code bytes -> the four code planes as signed MFMA B operands. Lane half
-  // h, plane t, byte 4q + p holds the weight at 64h + 16q + 4p + t of the
-  // group, matching plane-ordered activations at offset 32t + 16h + 4q + p.
-  auto decode = [&](const v4u& c, v4i (&b)[4]) __attribute__((always_inline)) {
+  // Ternary: 16 code bytes -> the four code planes as signed MFMA B operands.
+  // Lane half h, plane t, byte 4q + p holds the weight at 64h + 16q + 4p + t
+  // of the group, matching plane-ordered activations at offset 32t + 16h + 4q + p.
+  // 4-bit: 32 code bytes (dwords d0..d7) -> MFMA t takes dwords 2t and 2t + 1
+  // as (low nibbles, high nibbles) of each, so byte 4q + p holds the weight at
+  // 64h + 16t + 8(q >> 1) + 2p + (q & 1), matching nibble-ordered activations
+  // at the same offset 32t + 16h + 4q + p.
+  auto decode = [&](const Raw& r, int j, v4i (&b)[4]) __attribute__((always_inline)) {
+    if (W4) {
+      const uint32_t z = WF == WF_I4Z ? ((r.z[j] >> r.zsh) & 15u) : 8u;
+      const uint32_t zadd = (0x80u - z) * 0x01010101u;
+      const uint32_t d[8] = {r.c[j][0].x, r.c[j][0].y, r.c[j][0].z, r.c[j][0].w,
+                             r.c[j][W4 ? 1 : 0].x, r.c[j][W4 ? 1 : 0].y, r.c[j][W4 ? 1 : 0].z, r.c[j][W4 ? 1 : 0].w};
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-      b[t] = v4i{static_cast<int>(code_plane_signed(c.x, t)), static_cast<int>(code_plane_signed(c.y, t)),
-                 static_cast<int>(code_plane_signed(c.z, t)), static_cast<int>(code_plane_signed(c.w, t))};
+      for (int t = 0; t < 4; ++t)
+        b[t] = v4i{static_cast<int>(nib_lo_signed(d[2 * t], zadd)), static_cast<int>(nib_hi_signed(d[2 * t], zadd)),
+                   static_cast<int>(nib_lo_signed(d[2 * t + 1], zadd)),
+                   static_cast<int>(nib_hi_signed(d[2 * t + 1], zadd))};
+    } else {
+      const v4u& c = r.c[j][0];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        b[t] = v4i{static_cast<int>(code_plane_signed(c.x, t)), static_cast<int>(code_plane_signed(c.y, t)),
+                   static_cast<int>(code_plane_signed(c.z, t)), static_cast<int>(code_plane_signed(c.w, t))};
+    }
   };
 
   v16f acc[4][2];
@@ -189,8 +239,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_t2_kernel(
   raw_load(raw, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  decode(raw.c[0], bop[0]);
-  float s0 = __half2float(raw.s[0]), s1 = __half2float(raw.s[1]);
+  decode(raw, 0, bop[0]);
+  float s0 = scale_f32(raw.s[0]), s1 = scale_f32(raw.s[1]);
 
   // One 128-group in LDS buffer BUF. On entry: bop[0] holds this group's first
   // weight tile, raw its raw bytes, dprev/sprev the previous group's last chain
@@ -211,7 +261,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_t2_kernel(
     // chain (0,0); decode this group's second weight tile; read token tile 1.
     {
       const v16i d = chain(aop[0], bop[0]);
-      decode(raw.c[1], bop[1]);
+      decode(raw, 1, bop[1]);
       a_read(IntC<BUF>{}, IntC<1>{}, aop[1]);
       dprev = d;
 #pragma unroll
@@ -235,7 +285,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_t2_kernel(
       fold(dprev, pi, pj, pj ? s1 : s0, g);
       if (j == 0 && i < 3) a_read(IntC<BUF>{}, IntC<i + 1>{}, aop[(i + 1) & 1]);
       // this group's first weight tile is free after chain (3,0): decode the next one
-      if (c == 7) decode(nraw.c[0], bop[0]);
+      if (c == 7) decode(nraw, 0, bop[0]);
       dprev = d;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -256,8 +306,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_t2_kernel(
     slot(IntC<7>{});
     sprev = s1;
     raw = nraw;
-    s0 = __half2float(nraw.s[0]);
-    s1 = __half2float(nraw.s[1]);
+    s0 = scale_f32(nraw.s[0]);
+    s1 = scale_f32(nraw.s[1]);
     __builtin_amdgcn_s_waitcnt(0);     // the direct A loads and raw weights have landed
     __syncthreads();
   };
@@ -313,14 +363,40 @@ __global__ __launch_bounds__(NT, 1) void gemm_t2_kernel(
   }
 }
 
-template <typename TOut>
+template <typename TOut, int WF>
 hipError_t go(const bpw_weights& w, const int8_t* qp, const float* xs, int m, TOut* y,
               hipStream_t s) {
   const int n = static_cast<int>(w.n), k = static_cast<int>(w.k);
   const int mtiles = (m + BM - 1) / BM, ntiles = (n + BN - 1) / BN;
-  gemm_t2_kernel<TOut, false><<<mtiles * ntiles, NT, LDS_BYTES, s>>>(
-      qp, xs, static_cast<const uint8_t*>(w.codes), static_cast<const __half*>(w.scales), m, n, k,
-      y, nullptr, 0, 0, 0, 0, 0, mtiles, 0, ntiles);
+  gemm_t2_kernel<TOut, false, WF><<<mtiles * ntiles, NT, LDS_BYTES, s>>>(
+      qp, xs, static_cast<const uint8_t*>(w.codes), static_cast<const uint16_t*>(w.scales),
+      static_cast<const uint8_t*>(w.zeros), w.scale_dtype == BPW_BF16, m, n, k, y, nullptr, 0, 0, 0, 0,
+      0, mtiles, 0, ntiles);
+  return hipGetLastError();
+}
+
+template <int WF>
+hipError_t go_out(const bpw_weights& w, const int8_t* qp, const float* xs, int m, void* y, int y_dtype,
+                  hipStream_t s) {
+  switch (y_dtype) {
+    case BPW_F32: return go<float, WF>(w, qp, xs, m, static_cast<float*>(y), s);
+    case BPW_F16: return go<__half, WF>(w, qp, xs, m, static_cast<__half*>(y), s);
+    default: return go<uint16_t, WF>(w, qp, xs, m, static_cast<uint16_t*>(y), s);
+  }
+}
+
+template <int WF>
+hipError_t go_partials(const bpw_weights& w, const int8_t* qp, int64_t m, int64_t m0, int64_t m1,
+                       int64_t n0, int64_t n1, int32_t* out, hipStream_t s) {
+  const int n = static_cast<int>(w.n), k = static_cast<int>(w.k);
+  const int mt0 = static_cast<int>(m0 / BM), mt1 = static_cast<int>((m1 - 1) / BM);
+  const int nt0 = static_cast<int>(n0 / BN), nt1 = static_cast<int>((n1 - 1) / BN);
+  const int mtiles = mt1 - mt0 + 1, ntiles = nt1 - nt0 + 1;
+  gemm_t2_kernel<float, true, WF><<<mtiles * ntiles, NT, LDS_BYTES, s>>>(
+      qp, nullptr, static_cast<const uint8_t*>(w.codes), static_cast<const uint16_t*>(w.scales),
+      static_cast<const uint8_t*>(w.zeros), w.scale_dtype == BPW_BF16, static_cast<int>(m), n, k, nullptr,
+      out, static_cast<int>(m0), static_cast<int>(m1), static_cast<int>(n0), static_cast<int>(n1), mt0,
+      mtiles, nt0, ntiles);
   return hipGetLastError();
 }
 
@@ -328,27 +404,27 @@ hipError_t go(const bpw_weights& w, const int8_t* qp, const float* xs, int m, TO
 
 hipError_t launch_gemm_t2(const bpw_weights& w, const int8_t* q_planes, const float* x_scale,
                           int64_t m, void* y, int y_dtype, hipStream_t s) {
-  const int mi = static_cast<int>(m);
-  switch (y_dtype) {
-    case BPW_F32: return go(w, q_planes, x_scale, mi, static_cast<float*>(y), s);
-    case BPW_F16: return go(w, q_planes, x_scale, mi, static_cast<__half*>(y), s);
-    default: return go(w, q_planes, x_scale, mi, static_cast<uint16_t*>(y), s);
-  }
+  return go_out<WF_T2>(w, q_planes, x_scale, static_cast<int>(m), y, y_dtype, s);
 }
 
 hipError_t launch_gemm_t2_partials(const bpw_weights& w, const int8_t* q_planes, int64_t m,
                                    int64_t m0, int64_t m1, int64_t n0, int64_t n1, int32_t* out,
                                    hipStream_t s) {
-  const int n = static_cast<int>(w.n), k = static_cast<int>(w.k);
-  const int mt0 = static_cast<int>(m0 / BM), mt1 = static_cast<int>((m1 - 1) / BM);
-  const int nt0 = static_cast<int>(n0 / BN), nt1 = static_cast<int>((n1 - 1) / BN);
-  const int mtiles = mt1 - mt0 + 1, ntiles = nt1 - nt0 + 1;
-  gemm_t2_kernel<float, true><<<mtiles * ntiles, NT, LDS_BYTES, s>>>(
-      q_planes, nullptr, static_cast<const uint8_t*>(w.codes),
-      static_cast<const __half*>(w.scales), static_cast<int>(m), n, k, nullptr, out,
-      static_cast<int>(m0), static_cast<int>(m1), static_cast<int>(n0), static_cast<int>(n1),
-      mt0, mtiles, nt0, ntiles);
-  return hipGetLastError();
+  return go_partials<WF_T2>(w, q_planes, m, m0, m1, n0, n1, out, s);
+}
+
+hipError_t launch_gemm_w4a8(const bpw_weights& w, const int8_t* q_nibbles, const float* x_scale,
+                            int64_t m, void* y, int y_dtype, hipStream_t s) {
+  const int mi = static_cast<int>(m);
+  return w.fmt == BPW_INT4_ZP ? go_out<WF_I4Z>(w, q_nibbles, x_scale, mi, y, y_dtype, s)
+                              : go_out<WF_I4>(w, q_nibbles, x_scale, mi, y, y_dtype, s);
+}
+
+hipError_t launch_gemm_w4a8_partials(const bpw_weights& w, const int8_t* q_nibbles, int64_t m,
+                                     int64_t m0, int64_t m1, int64_t n0, int64_t n1, int32_t* out,
+                                     hipStream_t s) {
+  return w.fmt == BPW_INT4_ZP ? go_partials<WF_I4Z>(w, q_nibbles, m, m0, m1, n0, n1, out, s)
+                              : go_partials<WF_I4>(w, q_nibbles, m, m0, m1, n0, n1, out, s);
 }
 
 }  // namespace bpw

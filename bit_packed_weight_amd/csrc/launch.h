@@ -20,6 +20,11 @@ hipError_t launch_quantize_groups(const void* x, int x_dtype, int64_t m, int64_t
 // 64-element half-group goes to position 32t + 16*half + u).
 hipError_t launch_int8_planes(const int8_t* q, int64_t m, int64_t k, int8_t* q_planes,
                               hipStream_t s);
+// q [M][K] -> nibble order for the 4-bit x int8 GEMM (gathered through perm
+// when perm is not NULL): inside each 64-element half h of a 128-group, element
+// 16t + 8a + 2p + b goes to position 32t + 16h + 4(2a + b) + p.
+hipError_t launch_int8_nibbles(const int8_t* q, const int32_t* perm, int64_t m, int64_t k,
+                               int8_t* q_nibbles, hipStream_t s);
 // x_perm[m][j] = x[m][perm[j]] for 16-bit elements.
 hipError_t launch_gather_cols(const uint16_t* x, const int32_t* perm, int64_t m, int64_t k,
                               uint16_t* x_perm, hipStream_t s);
@@ -50,6 +55,12 @@ hipError_t launch_gemm_t2(const bpw_weights& w, const int8_t* q_planes, const fl
 hipError_t launch_gemm_t2_partials(const bpw_weights& w, const int8_t* q_planes, int64_t m,
                                    int64_t m0, int64_t m1, int64_t n0, int64_t n1, int32_t* out,
                                    hipStream_t s);
+// 4-bit weights x int8 activations (nibble order), same kernel as the ternary GEMM.
+hipError_t launch_gemm_w4a8(const bpw_weights& w, const int8_t* q_nibbles, const float* x_scale,
+                            int64_t m, void* y, int y_dtype, hipStream_t s);
+hipError_t launch_gemm_w4a8_partials(const bpw_weights& w, const int8_t* q_nibbles, int64_t m,
+                                     int64_t m0, int64_t m1, int64_t n0, int64_t n1, int32_t* out,
+                                     hipStream_t s);
 hipError_t launch_gemm_w4(const bpw_weights& w, const void* x_sorted, int x_dtype, int64_t m,
                           void* y, int y_dtype, hipStream_t s);
 

@@ -112,6 +112,53 @@ __global__ __launch_bounds__(256) void int8_planes_kernel(const int8_t* __restri
   }
 }
 
+// Nibble order for the 4-bit x int8 GEMM, one thread per (row, group, half):
+// 64 activation bytes (gathered through perm under act order) -> four 16-byte
+// chunks; chunk t holds natural bytes 16t .. 16t + 15 of the half as (even
+// bytes of the first 8, odd bytes of the first 8, even and odd of the second 8)
+// and goes where plane t of the plane order goes.
+__global__ __launch_bounds__(256) void int8_nibbles_kernel(const int8_t* __restrict__ q,
+                                                           const int32_t* __restrict__ perm,
+                                                           int64_t m, int64_t k,
+                                                           int8_t* __restrict__ out) {
+  const int64_t per_row = k / 64;
+  const int64_t units = m * per_row;
+  for (int64_t u = blockIdx.x * 256ll + threadIdx.x; u < units; u += gridDim.x * 256ll) {
+    const int64_t base = u * 64;
+    const int hh = static_cast<int>(u & 1);
+    uint32_t d[16];
+    if (perm) {
+      const int64_t row = u / per_row;
+      const int32_t* pj = perm + (u - row * per_row) * 64;
+      const uint8_t* qr = reinterpret_cast<const uint8_t*>(q) + row * k;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) v |= static_cast<uint32_t>(qr[pj[4 * i + b]]) << (8 * b);
+        d[i] = v;
+      }
+    } else {
+      const v4u* src = reinterpret_cast<const v4u*>(q + base);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const v4u v = src[i];
+        d[4 * i] = v.x;
+        d[4 * i + 1] = v.y;
+        d[4 * i + 2] = v.z;
+        d[4 * i + 3] = v.w;
+      }
+    }
+    int8_t* gbase = out + (base - hh * 64);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t* c = d + 4 * t;
+      *reinterpret_cast<v4u*>(gbase + 32 * t + 16 * hh) =
+          v4u{even_bytes(c[0], c[1]), odd_bytes(c[0], c[1]), even_bytes(c[2], c[3]), odd_bytes(c[2], c[3])};
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void gather_cols_kernel(const uint16_t* __restrict__ x,
                                                           const int32_t* __restrict__ perm,
                                                           int64_t m, int64_t k,
@@ -172,6 +219,13 @@ hipError_t launch_int8_planes(const int8_t* q, int64_t m, int64_t k, int8_t* q_p
                               hipStream_t s) {
   const int64_t units = m * (k / 64);
   int8_planes_kernel<<<grid_for(units, 256), 256, 0, s>>>(q, m, k, q_planes);
+  return hipGetLastError();
+}
+
+hipError_t launch_int8_nibbles(const int8_t* q, const int32_t* perm, int64_t m, int64_t k,
+                               int8_t* q_nibbles, hipStream_t s) {
+  const int64_t units = m * (k / 64);
+  int8_nibbles_kernel<<<grid_for(units, 256), 256, 0, s>>>(q, perm, m, k, q_nibbles);
   return hipGetLastError();
 }
 

@@ -391,3 +391,113 @@ def test_workload_ternary_prefill_sampled():
         q_win, _ = quant.quantize_rows(w.x[m0:m1])        # the oracle quantises its own rows
         np.testing.assert_array_equal(host(p), reference.ternary_partials(q_win, w.codes[n0:n1]),
                                       err_msg=f"window {(m0, m1, n0, n1)}")
+
+
+# ------------------------------------------------------------------ 4-bit x int8 (prefill GEMM)
+def w4a8_case(fmt, m, k, n, seed, act_order, scale_dtype):
+    w = w4_case(fmt, m, k, n, seed, act_order, scale_dtype)
+    q_ref, xs_ref = quant.quantize_rows(w.x_f32())
+    return w, q_ref, xs_ref
+
+
+def w4a8_reference(w, q_ref, xs_ref, rows=None, cols=None):
+    rows = slice(None) if rows is None else rows
+    cols = slice(None) if cols is None else cols
+    zeros = w.zeros[cols] if w.fmt == "int4_zp" else None
+    return reference.int4_int8_product(q_ref[rows], xs_ref[rows], w.codes[cols], w.scales_f64()[cols], zeros,
+                                       w.g_idx)
+
+
+@pytest.mark.parametrize("fmt,scale_dtype,act_order", [("int4_sym", "bf16", False), ("int4_zp", "f16", True),
+                                                       ("int4_zp", "f16", False), ("int4_sym", "f16", True)])
+@pytest.mark.parametrize("m,k,n", [(1, 256, 300), (130, 1024, 520), (300, 640, 257), (64, 128, 256),
+                                   (129, 2048, 1000)])
+def test_gemm_w4a8_parity(fmt, scale_dtype, act_order, m, k, n):
+    w, q_ref, xs_ref = w4a8_case(fmt, m, k, n, 400 + m + k + n, act_order, scale_dtype)
+    pw = prepare(w)
+    q, xs = bpw.quantize_rows(to_dev(w.x_f32(), "f32"))
+    y = bpw.gemm_packed(pw, q, xs)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(q), q_ref)
+    _, y_ref = w4a8_reference(w, q_ref, xs_ref)
+    assert_close(host(y), y_ref, "f16", f"gemm w4a8 {fmt} {scale_dtype} act={act_order} m={m} k={k} n={n}")
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_gemm_w4a8_output_dtypes(out):
+    w, q_ref, xs_ref = w4a8_case("int4_zp", 77, 512, 300, 431, True, "bf16")
+    pw = prepare(w)
+    y = bpw.gemm_packed(pw, to_dev(q_ref, "i8"), to_dev(xs_ref, "f32"), out_dtype=TORCH[out])
+    torch.cuda.synchronize()
+    _, y_ref = w4a8_reference(w, q_ref, xs_ref)
+    assert_close(host(y), y_ref, out, f"gemm w4a8 out={out}")
+
+
+@pytest.mark.parametrize("fmt,act_order", [("int4_sym", False), ("int4_zp", True), ("int4_zp", False)])
+@pytest.mark.parametrize("m,k,n,win", [(3, 256, 70, (0, 3, 0, 70)), (300, 640, 520, (5, 290, 33, 510)),
+                                       (130, 1024, 260, (128, 130, 255, 260))])
+def test_partials_w4a8_bit_exact(fmt, act_order, m, k, n, win):
+    # stress inputs: the full int8 range, every code and zero point
+    rng = np.random.default_rng(m + k + n + 5)
+    q = synth.random_int8(m + k + 1, m, k)
+    codes = rng.integers(0, 16, size=(n, k), dtype=np.uint8)
+    scales = rng.uniform(0.001, 0.02, size=(n, k // 128)).astype(np.float16)
+    zeros = rng.integers(0, 16, size=(n, k // 128), dtype=np.uint8) if fmt == "int4_zp" else None
+    g_idx = None
+    if act_order:
+        g_idx = np.empty(k, np.int32)
+        g_idx[rng.permutation(k)] = np.arange(k, dtype=np.int32) // 128
+    pw = bpw.prepare_packed(bpw.FORMAT_NAMES[fmt], codes, scales, zeros, g_idx, device=DEV)
+    m0, m1, n0, n1 = win
+    p = bpw.partials(pw, to_dev(q, "i8"), bpw.PATH_GEMM, m0, m1, n0, n1)
+    torch.cuda.synchronize()
+    z = zeros[n0:n1] if zeros is not None else None
+    p_ref = reference.int4_partials(q[m0:m1], codes[n0:n1], z, g_idx)
+    np.testing.assert_array_equal(host(p), p_ref)
+
+
+def test_w4a8_determinism_row_independence_and_poison():
+    w, q_ref, xs_ref = w4a8_case("int4_zp", 300, 1024, 520, 441, True, "f16")
+    pw = prepare(w)
+    q, xs = to_dev(q_ref, "i8"), to_dev(xs_ref, "f32")
+    y1 = torch.full((300, 520), float("nan"), dtype=torch.float16, device=DEV)
+    bpw.gemm_packed(pw, q, xs, out=y1)
+    y2 = bpw.gemm_packed(pw, q, xs)
+    q2 = q.clone()
+    q2[1:] = torch.randint(-127, 128, q2[1:].shape, device=DEV, dtype=torch.int8)
+    y3 = bpw.gemm_packed(pw, q2, xs)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y1).all()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(y1[0].view(torch.int16), y3[0].view(torch.int16))
+
+
+def test_w4a8_refused_by_gemv_entry():
+    w, q_ref, xs_ref = w4a8_case("int4_sym", 4, 256, 64, 451, False, "bf16")
+    pw = prepare(w)
+    with pytest.raises(bpw.BpwError) as e:
+        bpw.gemv_packed(pw, to_dev(q_ref, "i8"), to_dev(xs_ref, "f32"))
+    assert e.value.status == bpw.EUNSUPPORTED and "bpw_gemm_packed" in str(e.value)
+
+
+def test_workload_w4a8_prefill_sampled():
+    # The 4-bit prefill workload's weights (M=2048, K=4096, N=14336) against
+    # its activations quantised to int8 rows.
+    w = synth.w4a16_prefill()
+    pw = prepare(w)
+    q, xs = bpw.quantize_rows(to_dev(w.x, "bf16"))
+    y = bpw.gemm_packed(pw, q, xs, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(2)
+    rows = np.unique(np.concatenate([[0, w.m - 1], rng.choice(w.m, 30, replace=False)]))
+    cols = np.unique(np.concatenate([np.arange(64), np.arange(w.n - 64, w.n), rng.choice(w.n, 512, replace=False)]))
+    q_ref, xs_ref = quant.quantize_rows(w.x_f32()[rows])
+    np.testing.assert_array_equal(host(q)[rows], q_ref)
+    _, y_ref = reference.int4_int8_product(q_ref, xs_ref, w.codes[cols], w.scales_f64()[cols])
+    assert_close(host(y)[np.ix_(rows, cols)], y_ref, "bf16", "w4a8 prefill sampled")
+    for (m0, m1, n0, n1) in [(0, 64, 0, 256), (w.m - 64, w.m, w.n - 256, w.n)]:
+        p = bpw.partials(pw, q, bpw.PATH_GEMM, m0, m1, n0, n1)
+        torch.cuda.synchronize()
+        q_win, _ = quant.quantize_rows(w.x_f32()[m0:m1])
+        np.testing.assert_array_equal(host(p), reference.int4_partials(q_win, w.codes[n0:n1]),
+                                      err_msg=f"window {(m0, m1, n0, n1)}")

@@ -176,6 +176,7 @@ def test_product_validation_statuses():
     assert _gemv(_weights(bpw.INT4_SYM), x_dtype=bpw.BF16, xs=None) == bpw.EUNSUPPORTED    # scale/act dtype
     assert _gemv(_weights(bpw.INT4_SYM), x_dtype=bpw.F16, xs=1024) == bpw.EINVAL
     assert _gemv(_weights(bpw.INT4_SYM), x_dtype=bpw.I8) == bpw.EUNSUPPORTED
+    assert "bpw_gemm_packed only" in bpw.last_error()                  # 4-bit x int8: GEMM entry
     # act order needs a workspace
     wp = _weights(bpw.INT4_SYM, perm=True)
     assert _gemv(wp, x_dtype=bpw.F16, xs=None, m=4) == bpw.EINVAL
@@ -239,3 +240,25 @@ def test_partials_and_probe_validation():
     assert lib.bpw_probe(bpw.PROBE_READ, 4096, 8192, 1000, None) == bpw.ESHAPE
     assert lib.bpw_quantize_rows(4096, bpw.I8, 1, 16, 8192, 12288, None) == bpw.EUNSUPPORTED
     assert lib.bpw_quantize_rows(None, bpw.F32, 1, 16, 8192, 12288, None) == bpw.EINVAL
+
+
+def test_w4a8_validation_and_workspace():
+    lib = bpw.lib()
+
+    def gemm(w, xs=1024, ws=None, ws_bytes=0, m=4, x_dtype=bpw.I8):
+        return lib.bpw_gemm_packed(ctypes.byref(w), 65536, x_dtype, xs, m, 131072, bpw.F16, ws, ws_bytes, None)
+
+    for w in (_weights(bpw.INT4_SYM), _weights(bpw.INT4_SYM, scale_dtype=bpw.BF16),
+              _weights(bpw.INT4_ZP, zeros=True, perm=True)):
+        assert gemm(w, xs=None) == bpw.EINVAL                       # int8 needs row scales
+        assert gemm(w, xs=1026) == bpw.EALIGN
+        assert gemm(w) == bpw.EINVAL and "workspace" in bpw.last_error()   # nibble-ordered copy of q
+        assert gemm(w, ws=1 << 20, ws_bytes=4 * 256 - 1) == bpw.ESHAPE
+        assert gemm(w, x_dtype=bpw.I8G) == bpw.EUNSUPPORTED
+        need = ctypes.c_size_t()
+        assert lib.bpw_workspace_size(ctypes.byref(w), 2048, bpw.I8, bpw.PATH_GEMM, ctypes.byref(need)) == 0
+        assert need.value == 2048 * 256
+    # partials of 4-bit weights: GEMM core only, with the same workspace
+    w4 = _weights(bpw.INT4_ZP, zeros=True)
+    assert lib.bpw_partials(ctypes.byref(w4), 65536, 4, bpw.PATH_GEMM, 0, 4, 0, 8, 4096, None, 0, None) == bpw.EINVAL
+    assert "workspace" in bpw.last_error()
