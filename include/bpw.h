@@ -6,8 +6,10 @@
  * 4-bit zero point) per group of 128 along K, with an optional act-order
  * permutation of K. Activations are fp16/bf16, or int8 with one fp32 scale per
  * row (or, for the decode GEMV, per row and 128-group). Sources: "Kernel experiments: recorded evidence" (ternary PQ2 format,
- * section A and Tests 1, 2, 6-8, 21) and "mate: Marlin-class W4A16 GEMM for
- * mp_31 (SQMMA int4 x fp16) - #6" (4-bit codes, zero points, act order).
+ * section A and Tests 1, 2, 6-8, 21), "mate: Marlin-class W4A16 GEMM for
+ * mp_31 (SQMMA int4 x fp16) - #6" (4-bit codes, zero points, act order) and
+ * "TensorFold PR #1176" (4-bit weights against int8 activations on the int8
+ * matrix instruction).
  *
  * Conventions for every entry point:
  *  - "host" pointers are ordinary CPU memory; "device" pointers are GPU memory
@@ -176,7 +178,9 @@ int bpw_workspace_size(const bpw_weights* w, int64_t m, int x_dtype, int entry, 
  * Supported (fmt, x_dtype): TERNARY2 x I8 (x_scale device fp32 [M] required),
  * TERNARY2 x I8G (x_scale device fp32 [M][K/128]; M <= 32, larger M and the
  * GEMM entry return BPW_EUNSUPPORTED), INT4_SYM / INT4_ZP x F16 or BF16
- * (scale_dtype == x_dtype, x_scale NULL).
+ * (scale_dtype == x_dtype, x_scale NULL). INT4_SYM / INT4_ZP x I8 (either
+ * scale dtype, x_scale device fp32 [M]) runs through bpw_gemm_packed only
+ * (here BPW_EUNSUPPORTED).
  * Anything else returns BPW_EUNSUPPORTED. y: device [M][N] of y_dtype
  * (F32, F16 or BF16; round-to-nearest-even from fp32).
  * Numerics: int8 -> exact int32 group partials, fp32 fold
@@ -200,11 +204,18 @@ int bpw_gemv_packed(const bpw_weights* w, const void* x, int x_dtype, const floa
 
 /*
  * y = x @ W^T, prefill-shaped (large M). Same arguments and combinations as
- * bpw_gemv_packed, except I8G (BPW_EUNSUPPORTED). Numerics: int8 -> as above (int8 MFMA, exact int32 group
- * partials). 4-bit -> each weight is dequantised to the activation dtype,
+ * bpw_gemv_packed, except I8G (BPW_EUNSUPPORTED), plus 4-bit weights x I8.
+ * Numerics: ternary x int8 -> as above (int8 MFMA, exact int32 group
+ * partials). 4-bit x F16/BF16 -> each weight is dequantised to the activation dtype,
  * round-to-nearest-even of (code - zero) * scale, then multiplied on MFMA with
  * fp32 accumulation (the float path of the mate PR: unpack int4 to the
  * activation type before the matrix instruction).
+ * 4-bit x I8 ("TensorFold PR #1176", the int8 prompt GEMM: a 4-bit code is an
+ * exact int8, so the group dot runs exactly on the int8 matrix instruction):
+ * P[m,n,g] = sum_{k in g} q[m,k] * (code[n,k] - zero[n,g]) in exact int32
+ * (zero 8 for INT4_SYM), then y = x_scale[m] * sum_g scale[n,g] * P[m,n,g] in
+ * fp32. With act order, q is gathered through perm. Needs a workspace of
+ * M * K bytes (a reordered copy of q).
  */
 int bpw_gemm_packed(const bpw_weights* w, const void* x, int x_dtype, const float* x_scale,
                     int64_t m, void* y, int y_dtype, void* workspace, size_t workspace_bytes,
@@ -212,10 +223,11 @@ int bpw_gemm_packed(const bpw_weights* w, const void* x, int x_dtype, const floa
 
 /*
  * Verification only: exact int32 group partials
- *   out[(m-m0)][(n-n0)][g] = sum_{k in group g} q[m,k] * (code[n,k] - 1)
+ *   out[(m-m0)][(n-n0)][g] = sum_{k in group g} q[m,k] * value(n,k)
  * for m0 <= m < m1, n0 <= n < n1, computed by the same kernel core as the
- * product (path BPW_PATH_GEMV: M <= 32 only; BPW_PATH_GEMM: any M).
- * TERNARY2 weights without act order only. q: device int8 [M][K].
+ * product, with value = code - 1 (TERNARY2) or code - zero (INT4_*; group g
+ * in act order, q gathered through perm). Path BPW_PATH_GEMV: TERNARY2 and
+ * M <= 32 only; BPW_PATH_GEMM: any format and M. q: device int8 [M][K].
  * out: device int32 [(m1-m0)][(n1-n0)][G]. workspace as for the product.
  */
 int bpw_partials(const bpw_weights* w, const int8_t* q, int64_t m, int path, int64_t m0,
