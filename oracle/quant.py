@@ -11,6 +11,10 @@ Test 8 (CPU activation-group numerical control):
 
 The workloads here use one scale per row (``quantize_rows``); the pages' own
 granularity is one scale per 128-group (``quantize_groups``).
+
+Non-finite inputs (the pages are silent): a block holding a NaN or an
+infinity gets scale NaN and all-zero codes, so every product output that
+uses it comes out NaN instead of a finite value built from the rest.
 """
 from __future__ import annotations
 
@@ -22,11 +26,16 @@ INV127 = np.float32(1.0) / np.float32(127.0)
 def _quantize_blocks(xb: np.ndarray):
     """xb: [..., L] fp32 -> (q int8 [..., L], scale fp32 [...])."""
     xb = np.asarray(xb, dtype=np.float32)
+    ok = np.isfinite(xb)
+    good = ok.all(axis=-1)
+    xb = np.where(ok, xb, np.float32(0.0))
     amax = np.max(np.abs(xb), axis=-1)
     scale = (amax * INV127).astype(np.float32)
     div = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
     ratio = (xb / div[..., None]).astype(np.float32)      # IEEE fp32 division
     q = np.clip(np.rint(ratio), -127.0, 127.0)            # rint: ties to even
+    q = np.where(good[..., None], q, 0.0)
+    scale = np.where(good, scale, np.float32(np.nan)).astype(np.float32)
     return q.astype(np.int8), scale
 
 

@@ -521,3 +521,32 @@ def test_int4_partials_act_order_sorted_form_and_negative_control():
     p = reference.int4_partials(q, codes, zeros, g_idx)
     np.testing.assert_array_equal(reference.int4_partials(q[:, perm], codes[:, perm], zeros, None), p)
     assert not np.array_equal(reference.int4_partials(q, codes, zeros, None), p)
+
+
+def test_quantizer_non_finite_blocks():
+    # A row (or group) holding NaN or an infinity: scale NaN, codes 0; the
+    # other rows keep the ordinary rule (row 2 worked by hand: amax 3).
+    x = np.array([[1.0, np.nan, 2.0, 0.5],
+                  [np.inf, 0.0, 0.0, 0.0],
+                  [1.0, 2.0, -3.0, 0.0],
+                  [-np.inf, 1.0, 1.0, 1.0]], np.float32)
+    q, s = quant.quantize_rows(x)
+    assert np.isnan(s[[0, 1, 3]]).all() and not np.isnan(s[2])
+    assert (q[[0, 1, 3]] == 0).all()
+    assert s[2] == np.float32(np.float32(3.0) * (np.float32(1.0) / np.float32(127.0)))
+    assert q[2].tolist() == [42, 85, -127, 0]
+    # group granularity: only the group with the NaN is affected
+    xg = np.ones((1, 256), np.float32)
+    xg[0, 200] = np.nan
+    qg, sg = quant.quantize_groups(xg)
+    assert not np.isnan(sg[0, 0]) and np.isnan(sg[0, 1])
+    assert (qg[0, :128] == 127).all() and (qg[0, 128:] == 0).all()
+    # the product of a flagged row is NaN everywhere, the other rows are finite
+    rng = np.random.default_rng(5)
+    codes = rng.integers(0, 3, size=(3, 4 * 128)).astype(np.uint8)
+    scales = rng.uniform(0.01, 0.05, size=(3, 4)).astype(np.float16)
+    xr = rng.standard_normal((3, 512)).astype(np.float32)
+    xr[1, 7] = np.inf
+    qr, sr = quant.quantize_rows(xr)
+    _, y = reference.ternary_int8_product(qr, sr, codes, scales)
+    assert np.isnan(y[1]).all() and np.isfinite(y[[0, 2]]).all()
