@@ -6,6 +6,11 @@
 // +-127) and Test 8 (the division by 127 is a multiply by the fp32 reciprocal).
 // Plane order of int8 activations: same page, Test 21 (masked-plane MMA: each
 // code plane of a packed byte multiplies a contiguous slice of activations).
+// A block (row or group) holding a NaN or an infinity gets scale NaN and
+// all-zero codes, so the products that use it come out NaN (the pages say
+// nothing of such inputs). The kernels find such values with one fma per
+// element, fma(v, 0, acc), which turns NaN exactly when v is NaN or infinite,
+// and then take the block's maximum as +inf.
 #include "device.h"
 #include "launch.h"
 
@@ -32,17 +37,23 @@ __global__ __launch_bounds__(kQThreads) void quantize_rows_kernel(const T* __res
   const T* xr = x + row * k;
   int8_t* qr = q + row * k;
   float v[ONEPASS ? V : 1];
-  float amax = 0.0f;
+  float amax = 0.0f, nonfinite = 0.0f;
   if (ONEPASS) {
 #pragma unroll
     for (int j = 0; j < V; ++j) {
       const int64_t i = threadIdx.x + static_cast<int64_t>(j) * kQThreads;
       v[j] = i < k ? ld(xr + i) : 0.0f;
       amax = fmaxf(amax, fabsf(v[j]));
+      nonfinite = fmaf(v[j], 0.0f, nonfinite);
     }
   } else {
-    for (int64_t i = threadIdx.x; i < k; i += kQThreads) amax = fmaxf(amax, fabsf(ld(xr + i)));
+    for (int64_t i = threadIdx.x; i < k; i += kQThreads) {
+      const float x1 = ld(xr + i);
+      amax = fmaxf(amax, fabsf(x1));
+      nonfinite = fmaf(x1, 0.0f, nonfinite);
+    }
   }
+  if (nonfinite != nonfinite) amax = __builtin_inff();
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
@@ -50,6 +61,11 @@ __global__ __launch_bounds__(kQThreads) void quantize_rows_kernel(const T* __res
   amax = wmax[0];
 #pragma unroll
   for (int w = 1; w < kQThreads / 64; ++w) amax = fmaxf(amax, wmax[w]);
+  if (__builtin_isinf(amax)) {                      // the whole workgroup takes this branch
+    for (int64_t i = threadIdx.x; i < k; i += kQThreads) qr[i] = 0;
+    if (threadIdx.x == 0) x_scale[row] = __builtin_nanf("");
+    return;
+  }
   const float scale = amax * (1.0f / 127.0f);      // fp32 reciprocal constant, one rounding
   const float div = scale > 0.0f ? scale : 1.0f;
   if (ONEPASS) {
@@ -80,12 +96,15 @@ __global__ __launch_bounds__(256) void quantize_groups_kernel(const T* __restric
     const int64_t i = u * 128 + 2 * lane;
     const float v0 = ld(x + i), v1 = ld(x + i + 1);
     float amax = fmaxf(fabsf(v0), fabsf(v1));
+    const float nonfinite = fmaf(v0, 0.0f, v1 * 0.0f);
+    if (nonfinite != nonfinite) amax = __builtin_inff();
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-    const float scale = amax * (1.0f / 127.0f);    // fp32 reciprocal constant, one rounding
+    const bool bad = __builtin_isinf(amax);        // the same in every lane of the wave
+    const float scale = bad ? __builtin_nanf("") : amax * (1.0f / 127.0f);   // fp32 reciprocal, one rounding
     const float div = scale > 0.0f ? scale : 1.0f;
-    const float r0 = fminf(fmaxf(rintf(v0 / div), -127.0f), 127.0f);   // IEEE division, ties to even
-    const float r1 = fminf(fmaxf(rintf(v1 / div), -127.0f), 127.0f);
+    const float r0 = bad ? 0.0f : fminf(fmaxf(rintf(v0 / div), -127.0f), 127.0f);   // IEEE division, ties to even
+    const float r1 = bad ? 0.0f : fminf(fmaxf(rintf(v1 / div), -127.0f), 127.0f);
     const uint32_t pair = (static_cast<uint32_t>(static_cast<int>(r0)) & 0xFFu) |
                           ((static_cast<uint32_t>(static_cast<int>(r1)) & 0xFFu) << 8);
     *reinterpret_cast<uint16_t*>(q + i) = static_cast<uint16_t>(pair);

@@ -501,3 +501,82 @@ def test_workload_w4a8_prefill_sampled():
         q_win, _ = quant.quantize_rows(w.x_f32()[m0:m1])
         np.testing.assert_array_equal(host(p), reference.int4_partials(q_win, w.codes[n0:n1]),
                                       err_msg=f"window {(m0, m1, n0, n1)}")
+
+
+# ------------------------------------------------------------------ non-finite activations
+def _with_non_finite(x):
+    x = x.copy()
+    x[1, 5] = np.nan
+    x[3, 0] = np.inf
+    x[3, 9] = -np.inf
+    return x
+
+
+def _as_dtype(x, dtype):
+    if dtype == "f16":
+        xs = x.astype(np.float16)
+        return xs, xs.astype(np.float32)
+    if dtype == "bf16":
+        xs = synth.f32_to_bf16_bits(x)
+        return xs, synth.bf16_bits_to_f32(xs)
+    return x, x
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("k", [512, 10240])
+def test_quantizers_non_finite_blocks(dtype, k):
+    # rows 1 and 3 hold a NaN / infinities: their scale is NaN and their codes 0
+    rng = np.random.default_rng(k + 3)
+    x = _with_non_finite(rng.standard_normal((5, k)).astype(np.float32) * 3)
+    xs, xf = _as_dtype(x, dtype)
+    q, s = bpw.quantize_rows(to_dev(xs, dtype))
+    qg, sg = bpw.quantize_groups(to_dev(xs, dtype))
+    torch.cuda.synchronize()
+    q_ref, s_ref = quant.quantize_rows(xf)
+    qg_ref, sg_ref = quant.quantize_groups(xf)
+    assert np.isnan(s_ref[[1, 3]]).all() and np.isnan(sg_ref[1, 0]) and np.isnan(sg_ref[3, 0])
+    np.testing.assert_array_equal(host(s).astype(np.float32), s_ref)
+    np.testing.assert_array_equal(host(q), q_ref)
+    np.testing.assert_array_equal(host(sg).astype(np.float32), sg_ref)
+    np.testing.assert_array_equal(host(qg), qg_ref)
+
+
+def _check_flagged_rows(y_bad, y_clean, bad_rows):
+    yb, yc = host(y_bad), host(y_clean)
+    assert np.isnan(yb[bad_rows]).all()
+    keep = [r for r in range(yb.shape[0]) if r not in bad_rows]
+    np.testing.assert_array_equal(yb[keep], yc[keep])
+
+
+@pytest.mark.parametrize("entry,fmt,m,k,n", [("gemv", "ternary", 1, 4096, 1000), ("gemv", "ternary", 5, 2048, 700),
+                                             ("gemv", "ternary", 16, 14336, 300), ("gemm", "ternary", 40, 1024, 520),
+                                             ("gemm", "int4_zp", 40, 1024, 520)])
+def test_products_of_non_finite_rows_are_nan(entry, fmt, m, k, n):
+    # A row with a NaN / infinity quantises to scale NaN, and every output of
+    # that row is NaN; the other rows are bit-identical to a run without them.
+    rng = np.random.default_rng(m + k + n)
+    if fmt == "ternary":
+        w = ternary_case(m, k, n, 600 + m)
+    else:
+        w = w4_case(fmt, m, k, n, 600 + m, True, "f16")
+    pw = prepare(w)
+    clean = rng.standard_normal((m, k)).astype(np.float32)
+    bad_rows = [0] if m == 1 else [1, 3]
+    dirty = clean.copy()
+    for r in bad_rows:
+        dirty[r, (7 * r) % k] = np.nan if r % 2 else np.inf
+    fn = bpw.gemv_packed if entry == "gemv" else bpw.gemm_packed
+    outs = []
+    for xin in (dirty, clean):
+        q, xs = bpw.quantize_rows(to_dev(xin, "f32"))
+        outs.append(fn(pw, q, xs))
+    torch.cuda.synchronize()
+    _check_flagged_rows(outs[0], outs[1], bad_rows)
+    if entry == "gemv" and fmt == "ternary":
+        # per-group scales: only the flagged group is NaN, but it reaches every output of its row
+        outs = []
+        for xin in (dirty, clean):
+            q, xs = bpw.quantize_groups(to_dev(xin, "f32"))
+            outs.append(fn(pw, q, xs))
+        torch.cuda.synchronize()
+        _check_flagged_rows(outs[0], outs[1], bad_rows)
