@@ -149,7 +149,10 @@ int bpw_prepare_packed(int fmt, int src_format, int scale_dtype, int64_t n, int6
  * Test 6 (group-128 quantiser) and Test 8 (the fp32 reciprocal-multiply scale):
  *   scale[m] = fl32(max_k |x[m,k]| * fl32(1/127)),
  *   q[m,k]   = clamp(round_half_even(x[m,k] / (scale[m] > 0 ? scale[m] : 1)), -127, 127)
- * with an IEEE fp32 division. x: device [M][K] of x_dtype (F32/F16/BF16);
+ * with an IEEE fp32 division. A row holding a NaN or an infinity gets
+ * x_scale NaN and all-zero codes, so every product output of that row is NaN
+ * (the pages say nothing of such inputs; this makes them visible).
+ * x: device [M][K] of x_dtype (F32/F16/BF16);
  * q: device int8 [M][K]; x_scale: device fp32 [M]. K >= 1, no multiple needed.
  */
 int bpw_quantize_rows(const void* x, int x_dtype, int64_t m, int64_t k, int8_t* q, float* x_scale,
@@ -160,6 +163,7 @@ int bpw_quantize_rows(const void* x, int x_dtype, int64_t m, int64_t k, int8_t* 
  * with the group's own max ("Kernel experiments", Test 6, group-128 form):
  *   scale[m,g] = fl32(max_{k in g} |x[m,k]| * fl32(1/127)),
  *   q[m,k]     = clamp(round_half_even(x[m,k] / (scale[m,g] > 0 ? scale[m,g] : 1)), -127, 127).
+ * A group holding a NaN or an infinity gets scale NaN and zero codes, as for rows.
  * x: device [M][K] of x_dtype (F32/F16/BF16); K a multiple of 128.
  * q: device int8 [M][K], 16-byte aligned; x_scale: device fp32 [M][K/128].
  */
