@@ -24,9 +24,10 @@
 // The same kernel takes 4-bit weights ("TensorFold PR #1176", the int8 prompt
 // GEMM: an affine 4-bit code is an exact int8, so the group dot runs on the
 // int8 matrix core). Each lane then loads 32 code bytes per weight tile and
-// group and decodes every nibble to the signed byte code - zero (zero 8 for
-// symmetric codes), so the int32 MFMA result is again the exact partial
-// P[m,n,g] = sum q * (code - zero) and the fold is unchanged. The activations
+// group and decodes every nibble to the signed byte code - zero, so the int32
+// MFMA result is again the exact partial P[m,n,g] = sum q * (code - zero) and
+// the fold is unchanged (symmetric codes, zero 8, decode to 16 (code - 8) in
+// fewer instructions; their chains carry 16 P and fold with scale / 16). The activations
 // come in nibble order: within each 8 bytes of a row, the even-indexed
 // elements, then the odd ones, in the chunk arrangement of the plane order.
 #include "device.h"
@@ -92,8 +93,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_t2_kernel(
   const int KB = W4 ? (K >> 1) : (K >> 2);
   const int ZB = (G + 1) >> 1;
   const bool bfs = W4 && bf_scale;
+  // Fold scale of a group; symmetric 4-bit chains carry 16 P (see decode).
   auto scale_f32 = [&](uint16_t bits) __attribute__((always_inline)) {
-    return bfs ? bf16_to_f32(bits) : __half2float(__builtin_bit_cast(__half, bits));
+    const float v = bfs ? bf16_to_f32(bits) : __half2float(__builtin_bit_cast(__half, bits));
+    return WF == WF_I4 ? v * 0.0625f : v;
   };
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int mt, nt;
@@ -181,7 +184,20 @@ __global__ __launch_bounds__(NT, 1) void gemm_t2_kernel(
   // 64h + 16t + 8(q >> 1) + 2p + (q & 1), matching nibble-ordered activations
   // at the same offset 32t + 16h + 4q + p.
   auto decode = [&](const Raw& r, int j, v4i (&b)[4]) __attribute__((always_inline)) {
-    if (W4) {
+    if (WF == WF_I4) {
+      // Symmetric codes: w ^ 0x88888888 holds code - 8 as a 4-bit two's
+      // complement in every nibble; moved to the top of its byte it is the
+      // signed byte 16 (code - 8). The chain result is then exactly 16 P
+      // (|16 P| < 2^22), and the fold takes scale / 16 (exact).
+      const uint32_t d[8] = {r.c[j][0].x, r.c[j][0].y, r.c[j][0].z, r.c[j][0].w,
+                             r.c[j][W4 ? 1 : 0].x, r.c[j][W4 ? 1 : 0].y, r.c[j][W4 ? 1 : 0].z, r.c[j][W4 ? 1 : 0].w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint32_t e0 = d[2 * t] ^ 0x88888888u, e1 = d[2 * t + 1] ^ 0x88888888u;
+        b[t] = v4i{static_cast<int>((e0 << 4) & 0xF0F0F0F0u), static_cast<int>(e0 & 0xF0F0F0F0u),
+                   static_cast<int>((e1 << 4) & 0xF0F0F0F0u), static_cast<int>(e1 & 0xF0F0F0F0u)};
+      }
+    } else if (W4) {
       const uint32_t z = WF == WF_I4Z ? ((r.z[j] >> r.zsh) & 15u) : 8u;
       const uint32_t zadd = (0x80u - z) * 0x01010101u;
       const uint32_t d[8] = {r.c[j][0].x, r.c[j][0].y, r.c[j][0].z, r.c[j][0].w,
@@ -215,7 +231,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_t2_kernel(
       for (int r = 0; r < 16; ++r) {
         const int mm = m0 + 32 * i + d_row(r, h);
         if (mm >= pm0 && mm < pm1 && nn >= pn0 && nn < pn1)
-          pout[(static_cast<size_t>(mm - pm0) * (pn1 - pn0) + (nn - pn0)) * G + g] = d[r];
+          pout[(static_cast<size_t>(mm - pm0) * (pn1 - pn0) + (nn - pn0)) * G + g] = WF == WF_I4 ? (d[r] >> 4) : d[r];
       }
     } else {
 #pragma unroll
