@@ -314,7 +314,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only; --gpus must be 1 "
+        print("bench.py: the benchmark runs on one GPU only; --gpus must be 1 "
               "(the multi-GPU sharding of the path is described, not implemented)", file=sys.stderr)
         sys.exit(2)
 
