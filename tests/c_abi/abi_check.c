@@ -91,6 +91,18 @@ int main(void) {
   check(bpw_workspace_size(&w, 1, BPW_I8, BPW_PATH_GEMV, &need) == BPW_OK && need == 0,
         "the M = 1 ternary GEMV needs no workspace");
 
+  /* 4-bit weights with int8 activations: the GEMM entry, a nibble-ordered copy of q. */
+  w.fmt = BPW_INT4_SYM;
+  w.scale_dtype = BPW_BF16;
+  check(bpw_workspace_size(&w, 64, BPW_I8, BPW_PATH_GEMM, &need) == BPW_OK && need == (size_t)64 * K,
+        "the 4-bit x int8 GEMM needs M * K bytes of workspace");
+  check(bpw_gemv_packed(&w, (const void*)(uintptr_t)65536, BPW_I8, (const float*)(uintptr_t)1024, 1,
+                        (void*)(uintptr_t)131072, BPW_F16, NULL, 0, NULL) == BPW_EUNSUPPORTED,
+        "4-bit x int8 through the GEMV entry is refused by name");
+  check(bpw_gemm_packed(&w, (const void*)(uintptr_t)65536, BPW_I8, (const float*)(uintptr_t)1024, 64,
+                        (void*)(uintptr_t)131072, BPW_F16, NULL, 0, NULL) == BPW_EINVAL,
+        "4-bit x int8 without its workspace is refused");
+
   if (failures) return 1;
   printf("ok\n");
   return 0;

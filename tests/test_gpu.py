@@ -472,6 +472,20 @@ def test_w4a8_determinism_row_independence_and_poison():
     assert torch.equal(y1[0].view(torch.int16), y3[0].view(torch.int16))
 
 
+@pytest.mark.parametrize("fmt,m,k,n", [("int4_sym", 1, 128, 1), ("int4_zp", 33, 256, 65), ("int4_sym", 129, 128, 257),
+                                       ("int4_zp", 128, 384, 256)])
+def test_w4a8_degenerate_shapes(fmt, m, k, n):
+    # one row / one output column / one group, and exact tile multiples
+    w, q_ref, xs_ref = w4a8_case(fmt, m, k, n, 460 + m + n, fmt == "int4_zp", "f16")
+    pw = prepare(w)
+    y = bpw.gemm_packed(pw, to_dev(q_ref, "i8"), to_dev(xs_ref, "f32"))
+    p = bpw.partials(pw, to_dev(q_ref, "i8"), bpw.PATH_GEMM, 0, m, 0, n)
+    torch.cuda.synchronize()
+    p_ref, y_ref = w4a8_reference(w, q_ref, xs_ref)
+    np.testing.assert_array_equal(host(p), p_ref)
+    assert_close(host(y), y_ref, "f16", f"w4a8 degenerate {fmt} m={m} k={k} n={n}")
+
+
 def test_w4a8_refused_by_gemv_entry():
     w, q_ref, xs_ref = w4a8_case("int4_sym", 4, 256, 64, 451, False, "bf16")
     pw = prepare(w)
