@@ -594,3 +594,54 @@ def test_products_of_non_finite_rows_are_nan(entry, fmt, m, k, n):
             outs.append(fn(pw, q, xs))
         torch.cuda.synchronize()
         _check_flagged_rows(outs[0], outs[1], bad_rows)
+
+
+# ------------------------------------------------------------------ graph replay
+def _graph_cases():
+    cases = []
+    # ternary decode: row kernel, skinny, split-K (two launches + workspace), group scales
+    for m, k, n in [(1, 4096, 1000), (5, 2048, 700), (16, 14336, 512)]:
+        w = ternary_case(m, k, n, 700 + m)
+        cases.append(("t2 gemv m=%d k=%d" % (m, k), w, "gemv", "rows"))
+    cases.append(("t2 gemv groups", ternary_case(3, 4096, 300, 710), "gemv", "groups"))
+    cases.append(("t2 gemm", ternary_case(200, 1024, 520, 711), "gemm", "rows"))
+    # 4-bit: act-order gather + GEMV, bf16 GEMM, W4A8 GEMM (nibble reorder + GEMM)
+    cases.append(("w4 gemv act", w4_case("int4_zp", 8, 5120, 700, 712, True, "f16"), "gemv", "float"))
+    cases.append(("w4 gemm", w4_case("int4_sym", 300, 1024, 520, 713, False, "bf16"), "gemm", "float"))
+    cases.append(("w4a8 gemm", w4_case("int4_zp", 200, 1024, 520, 714, True, "f16"), "gemm", "rows"))
+    return cases
+
+
+def test_graph_replay_matches_eager():
+    # Each entry point captured into a HIP graph (the form the benchmark times),
+    # replayed three times with eager calls of the library in between, matches
+    # the eager result bit for bit on every replay.
+    for name, w, entry, act in _graph_cases():
+        pw = prepare(w)
+        fn = bpw.gemv_packed if entry == "gemv" else bpw.gemm_packed
+        if act == "float":
+            args = (to_dev(w.x, w.x_dtype),)
+            xd = bpw.dtype_code(TORCH[w.x_dtype])
+        else:
+            x = to_dev(w.x_f32(), "f32")
+            args = bpw.quantize_rows(x) if act == "rows" else bpw.quantize_groups(x)
+            xd = bpw.I8G if act == "groups" else bpw.I8
+        path = bpw.PATH_GEMV if entry == "gemv" else bpw.PATH_GEMM
+        need = bpw.workspace_size(pw, w.m, xd, path)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=DEV) if need else None
+        eager = fn(pw, *args, workspace=ws)
+        torch.cuda.synchronize()
+        out = torch.full_like(eager, float("nan"))
+        stream = torch.cuda.Stream()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            fn(pw, *args, out=out, workspace=ws)
+        for rep in range(3):
+            out.fill_(float("nan"))
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int16) if out.element_size() == 2 else out.view(torch.int32),
+                               eager.view(torch.int16) if eager.element_size() == 2 else eager.view(torch.int32)), \
+                f"{name}: replay {rep} differs from the eager result"
+            fn(pw, *args, workspace=ws)                     # eager work of the library between replays
+            torch.cuda.synchronize()
