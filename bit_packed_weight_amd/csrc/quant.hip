@@ -178,6 +178,21 @@ __global__ __launch_bounds__(256) void int8_nibbles_kernel(const int8_t* __restr
   }
 }
 
+// The same order without act order, one thread per 16-byte chunk: chunk t of
+// half h of a 128-group (natural bytes 64h + 16t ..) only moves to offset
+// 32t + 16h of the group, with its bytes regrouped as above, so thread j reads
+// bytes [16j, 16j + 16) (consecutive threads, consecutive chunks) and writes
+// within the same 128-byte group.
+__global__ __launch_bounds__(256) void int8_nibbles_chunk_kernel(const int8_t* __restrict__ q, int64_t chunks,
+                                                                 int8_t* __restrict__ out) {
+  for (int64_t j = blockIdx.x * 256ll + threadIdx.x; j < chunks; j += gridDim.x * 256ll) {
+    const v4u c = reinterpret_cast<const v4u*>(q)[j];
+    const int t = static_cast<int>(j & 3), hh = static_cast<int>((j >> 2) & 1);
+    *reinterpret_cast<v4u*>(out + (j >> 3) * 128 + 32 * t + 16 * hh) =
+        v4u{even_bytes(c.x, c.y), odd_bytes(c.x, c.y), even_bytes(c.z, c.w), odd_bytes(c.z, c.w)};
+  }
+}
+
 __global__ __launch_bounds__(256) void gather_cols_kernel(const uint16_t* __restrict__ x,
                                                           const int32_t* __restrict__ perm,
                                                           int64_t m, int64_t k,
@@ -243,6 +258,11 @@ hipError_t launch_int8_planes(const int8_t* q, int64_t m, int64_t k, int8_t* q_p
 
 hipError_t launch_int8_nibbles(const int8_t* q, const int32_t* perm, int64_t m, int64_t k,
                                int8_t* q_nibbles, hipStream_t s) {
+  if (!perm) {
+    const int64_t chunks = m * (k / 16);
+    int8_nibbles_chunk_kernel<<<grid_for(chunks, 256), 256, 0, s>>>(q, chunks, q_nibbles);
+    return hipGetLastError();
+  }
   const int64_t units = m * (k / 64);
   int8_nibbles_kernel<<<grid_for(units, 256), 256, 0, s>>>(q, perm, m, k, q_nibbles);
   return hipGetLastError();
