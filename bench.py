@@ -122,6 +122,21 @@ def bench_ternary_decode(bpw, synth, torch, np, steps, warmup):
     return w, nbytes, ms, ms_full, len(copies)
 
 
+def bench_ternary_decode_large(bpw, synth, torch, np, steps, warmup):
+    """The M = 1 decode GEMV on the ternary prefill weight (K=8192, N=28672, 62 MB), first activation row."""
+    w = synth.leading_rows(synth.ternary_prefill(), 1)
+    planes = bpw.prepare_packed_host(bpw.TERNARY2, w.codes, w.scales)
+    w.codes = None
+    copies = rotated_copies(bpw, planes, 1 << 30)
+    q, xs = bpw.quantize_rows(to_dev(w.x, "f32", torch, np))
+    y = torch.empty((1, w.n), dtype=torch.float16, device="cuda")
+    nbytes = copies[0].logical_bytes
+    ms = time_graph(torch, lambda i: bpw.gemv_packed(copies[i % len(copies)], q, xs, out=y), steps, warmup)
+    return {"workload": "ternary_decode_gemv_large_weight", "M": 1, "K": w.k, "N": w.n, "weight_bytes": nbytes,
+            "us_per_call": ms * 1e3, "GB_s": nbytes / (ms * 1e6), "frac_hbm_peak": nbytes / (ms * 1e6) / HBM_PEAK_GBS,
+            "copies": len(copies)}
+
+
 def bench_probe(bpw, torch, kind, nbytes, steps, warmup):
     """Plain streaming read (or copy) of nbytes per call over rotated buffers (>= 1 GiB).
 
@@ -338,7 +353,7 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_extra:
         runs = ((bench_ternary_decode_m, 900, 300, {"m": 16}), (bench_ternary_long_k, 600, 200, {"m": 16}),
-                (bench_ternary_decode_groups, 900, 300, {"m": 1}),
+                (bench_ternary_decode_large, 600, 200, {}), (bench_ternary_decode_groups, 900, 300, {"m": 1}),
                 (bench_ternary_decode_groups, 900, 300, {"m": 16}), (bench_w4_decode, 900, 300, {"m": 1}),
                 (bench_w4_decode, 900, 300, {"m": 8}), (bench_w4_prefill, 30, 6, {}), (bench_w4a8_prefill, 30, 6, {}),
                 (bench_ternary_prefill, 12, 3, {}))

@@ -344,6 +344,27 @@ def test_workload_ternary_decode_full(m):
     np.testing.assert_array_equal(host(p), reference.ternary_partials(q_ref, w.codes))
 
 
+def test_gemv_ternary_large_weight_sampled():
+    # The M = 1 decode GEMV on the ternary prefill weight (K=8192, N=28672):
+    # sampled outputs against the oracle, and every group partial of a few
+    # column windows bit-exact.
+    w = synth.leading_rows(synth.ternary_prefill(), 1)
+    pw = bpw.prepare_packed(bpw.TERNARY2, w.codes, w.scales, device=DEV)
+    q, xs = bpw.quantize_rows(to_dev(w.x, "f32"))
+    y = bpw.gemv_packed(pw, q, xs)
+    torch.cuda.synchronize()
+    q_ref, xs_ref = quant.quantize_rows(w.x)
+    np.testing.assert_array_equal(host(q), q_ref)
+    rng = np.random.default_rng(4)
+    cols = np.unique(np.concatenate([np.arange(64), np.arange(w.n - 64, w.n), rng.choice(w.n, 1024, replace=False)]))
+    _, y_ref = reference.ternary_int8_product(q_ref, xs_ref, w.codes[cols], w.scales[cols])
+    assert_close(host(y)[:, cols], y_ref, "f16", "ternary GEMV on the prefill weight, sampled")
+    for (n0, n1) in [(0, 256), (w.n - 256, w.n), (13000, 13300)]:
+        p = bpw.partials(pw, q, bpw.PATH_GEMV, 0, 1, n0, n1)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(p), reference.ternary_partials(q_ref, w.codes[n0:n1]))
+
+
 @pytest.mark.parametrize("m", [1, 8])
 def test_workload_w4a16_decode_full(m):
     w = synth.w4a16_decode(m)
