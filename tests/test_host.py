@@ -262,3 +262,14 @@ def test_w4a8_validation_and_workspace():
     w4 = _weights(bpw.INT4_ZP, zeros=True)
     assert lib.bpw_partials(ctypes.byref(w4), 65536, 4, bpw.PATH_GEMM, 0, 4, 0, 8, 4096, None, 0, None) == bpw.EINVAL
     assert "workspace" in bpw.last_error()
+
+
+def test_traffic_profile_matches_gemv_sources():
+    # bench.py reports the decode GEMV's measured HBM traffic only while the
+    # committed counter summary was taken on the current GEMV sources; a change
+    # to them must come with new counter passes.
+    import bench
+    traffic = bench.measured_traffic()
+    assert traffic is not None, "GEMV sources changed since the traffic counters were taken"
+    # every weight byte once, plus the activation row, the output and line granularity
+    assert 15597568 <= traffic <= 1.01 * 15597568
