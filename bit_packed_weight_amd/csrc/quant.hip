@@ -1,5 +1,6 @@
 // Activation operand kernels: int8 row and group quantisers, int8 plane
-// reorder, act-order column gather.
+// reorder (ternary GEMM), int8 nibble reorder (4-bit x int8 GEMM, with the
+// act-order gather), act-order column gather for 16-bit activations.
 //
 // Quantiser rule: "Kernel experiments: recorded evidence", Test 6 (group-128
 // quantiser: absmax / 127, IEEE division, round half to even, clamp to
