@@ -10,9 +10,13 @@ HIP events on the launch stream. value = logical weight bytes (codes + scales)
 per call / time per call.
 
 Also reported (same JSON line): the complete decode call (quantiser + GEMV),
-the other decode/prefill workloads (4-bit decode GEMV, bf16 prefill GEMM at
-M=2048, ternary x int8 prefill GEMM), the roofline of the dominant kernel, and
-the CPU oracle timed on a bounded sample of the headline workload.
+the other decode/prefill workloads (ternary decode at M=16, split-K long K,
+per-group activation scales and on the 62 MB prefill weight; 4-bit decode GEMV
+with act order; bf16 prefill GEMM at M=2048; 4-bit x int8 prefill GEMM at
+M=2048; ternary x int8 prefill GEMM; hipBLASLt dense GEMMs at the prefill
+shapes as a platform reference), HBM read/copy probes, the roofline of the
+dominant kernel, and the CPU oracle timed on a bounded sample of the headline
+workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
 """
