@@ -273,3 +273,29 @@ def test_traffic_profile_matches_gemv_sources():
     assert traffic is not None, "GEMV sources changed since the traffic counters were taken"
     # every weight byte once, plus the activation row, the output and line granularity
     assert 15597568 <= traffic <= 1.01 * 15597568
+
+
+def test_last_error_is_per_thread():
+    # Each thread sees the message of its own last failure, however the calls
+    # of several threads interleave.
+    import threading
+    lib = bpw.lib()
+    errors = []
+
+    def worker(kind):
+        for _ in range(300):
+            if kind == 0:
+                st = _gemv(_weights(k=200))
+                want = "multiple of 128"
+            else:
+                st = _gemv(_weights(), x=None)
+                want = "x / y is NULL"
+            msg = bpw.last_error()
+            if want not in msg:
+                errors.append((kind, st, msg))
+    threads = [threading.Thread(target=worker, args=(i % 2,)) for i in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:3]
