@@ -666,3 +666,32 @@ def test_graph_replay_matches_eager():
                 f"{name}: replay {rep} differs from the eager result"
             fn(pw, *args, workspace=ws)                     # eager work of the library between replays
             torch.cuda.synchronize()
+
+
+def test_two_streams_with_their_own_workspaces():
+    # The library keeps no state between calls: the same entry points running
+    # on two streams at once, each with its own workspace, give the
+    # single-stream results bit for bit.
+    cases = []
+    for m, k, n, seed in [(16, 14336, 512, 801), (200, 1024, 520, 802)]:
+        w = ternary_case(m, k, n, seed)
+        pw = prepare(w)
+        q, xs = bpw.quantize_rows(to_dev(w.x_f32(), "f32"))
+        fn = bpw.gemv_packed if m <= 32 else bpw.gemm_packed
+        path = bpw.PATH_GEMV if m <= 32 else bpw.PATH_GEMM
+        need = bpw.workspace_size(pw, m, bpw.I8, path)
+        ref = fn(pw, q, xs)
+        cases.append((fn, pw, q, xs, need, ref))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[], []]
+    wss = [[torch.empty(max(c[4], 1), dtype=torch.uint8, device=DEV) for c in cases] for _ in streams]
+    for it in range(20):
+        for si, st in enumerate(streams):
+            with torch.cuda.stream(st):
+                for ci, (fn, pw, q, xs, need, ref) in enumerate(cases):
+                    outs[si].append((ci, fn(pw, q, xs, workspace=wss[si][ci] if need else None)))
+    torch.cuda.synchronize()
+    for si in range(2):
+        for ci, y in outs[si]:
+            assert torch.equal(y.view(torch.int16), cases[ci][5].view(torch.int16)), f"stream {si} case {ci}"
