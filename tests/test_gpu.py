@@ -115,7 +115,9 @@ def run_ternary(w: synth.Workload, entry: str):
                                    # skinny kernel: four-tile shares, ragged tiles; long-K kernel: 2..4 phases,
                                    # ragged last phase; M = 1 past the row kernel's K; row kernel partial chunk
                                    (32, 8192, 3000), (9, 3072, 20000), (24, 6144, 9000), (16, 14336, 4096),
-                                   (4, 11008, 700), (1, 20480, 500), (1, 14336, 1000), (1, 1152, 333)])
+                                   (4, 11008, 700), (1, 20480, 500), (1, 14336, 1000), (1, 1152, 333),
+                                   # M = 1, N >= 16384: four rows per wave, ragged last wave, one and four chunks
+                                   (1, 4096, 16387), (1, 16384, 16390)])
 @pytest.mark.parametrize("out", ["f32", "f16", "bf16"])
 def test_gemv_ternary_parity(m, k, n, out):
     w = ternary_case(m, k, n, 100 + m + k + n, out)
@@ -145,7 +147,9 @@ def test_gemv_ternary_split_k(m, k, n):
 
 @pytest.mark.parametrize("m,k,n", [(1, 4096, 1000), (1, 16384, 77), (1, 512, 256), (2, 640, 333),
                                    (16, 4096, 14336), (32, 8192, 3000), (9, 3072, 20000), (20, 4096, 700),
-                                   (1, 20480, 300), (8, 14336, 1000)])
+                                   (1, 20480, 300), (8, 14336, 1000),
+                                   # M = 1, N >= 16384: four rows per wave, ragged last wave
+                                   (1, 1024, 16389), (1, 12288, 20001)])
 @pytest.mark.parametrize("out", ["f32", "f16"])
 def test_gemv_ternary_group_scales(m, k, n, out):
     # one activation scale per (row, 128-group): y = sum_g xs[m,g] * ws[n,g] * P[m,n,g]
@@ -180,7 +184,7 @@ def test_gemm_ternary_parity(m, k, n):
                                        (1, 128, 40, (0, 1, 7, 9)), (1, 4096, 77, (0, 1, 3, 70)),
                                        (1, 8192, 9, (0, 1, 0, 9)), (16, 8192, 600, (3, 14, 100, 580)),
                                        (12, 3072, 20000, (0, 12, 9000, 9777)), (3, 12288, 500, (0, 3, 17, 463)),
-                                       (1, 5248, 300, (0, 1, 0, 300))])
+                                       (1, 5248, 300, (0, 1, 0, 300)), (1, 2048, 16400, (0, 1, 15990, 16400))])
 def test_partials_bit_exact(path, m, k, n, win):
     # stress inputs: full int8 range and every 2-bit code including 3
     rng = np.random.default_rng(m + k + n)
