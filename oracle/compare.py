@@ -18,10 +18,16 @@ MIN_EXP = {"f32": -126, "f16": -14, "bf16": -126}
 
 
 def ulp(v: np.ndarray, dtype: str) -> np.ndarray:
-    """Spacing of ``dtype`` values at |v| (normal range, with the subnormal floor)."""
+    """Spacing of ``dtype`` values at |v|.
+
+    A normal |v| in [2**e, 2**(e+1)) has spacing 2**(e - (p - 1)) for a p-bit
+    significand. Zero and the subnormals all have the subnormal quantum
+    2**(MIN_EXP - (p - 1)): the binade exponent is clamped to MIN_EXP, and zero
+    (for which frexp reports exponent 0) is given MIN_EXP explicitly.
+    """
     v = np.abs(np.asarray(v, np.float64))
-    _, e = np.frexp(v)                       # v = m * 2**e, 0.5 <= m < 1
-    e = np.maximum(e - 1, MIN_EXP[dtype])
+    _, e = np.frexp(v)                       # v = m * 2**e, 0.5 <= m < 1 (e = 0 for v = 0)
+    e = np.where(v == 0.0, MIN_EXP[dtype], np.maximum(e - 1, MIN_EXP[dtype]))
     return np.ldexp(1.0, e - (SIG_BITS[dtype] - 1))
 
 

@@ -250,6 +250,52 @@ def test_int8_product_group_scale_variant_reduces_to_row_scales():
     np.testing.assert_array_equal(y1, y2)
 
 
+def _fraction_group_scale_product(q, xs, codes, ws):
+    """y[m][n] = sum over k of q[m,k] * (code[n,k] - 1) * xs[m, k // 128] * ws[n, k // 128],
+    weight by weight in exact rationals ("Kernel experiments", Test 6: one activation
+    scale per group of 128, folded with the weight scale of the same group)."""
+    m, k = q.shape
+    n = codes.shape[0]
+    out = [[Fraction(0)] * n for _ in range(m)]
+    for i in range(m):
+        for j in range(n):
+            acc = Fraction(0)
+            for kk in range(k):
+                g = kk // 128
+                acc += (Fraction(int(q[i, kk])) * (int(codes[j, kk]) - 1) * Fraction(float(xs[i, g]))
+                        * Fraction(float(ws[j, g])))
+            out[i][j] = acc
+    return out
+
+
+def test_int8_product_group_scales_fraction_brute_force():
+    """Distinct scales in every (row, group) and (weight row, group): a paired-up group
+    index (reversed, shifted, or the row scale of group 0 for all) must fail."""
+    rng = np.random.default_rng(9)
+    m, k, n = 3, 384, 4
+    q = rng.integers(-127, 128, size=(m, k), dtype=np.int8)
+    codes = rng.integers(0, 4, size=(n, k), dtype=np.uint8)       # code 3 (+2) included
+    ws = rng.uniform(0.01, 0.05, size=(n, 3)).astype(np.float16)
+    xs = rng.uniform(0.001, 0.1, size=(m, 3)).astype(np.float32)
+    assert len(np.unique(xs)) == xs.size and len(np.unique(ws)) == ws.size
+    exact = _fraction_group_scale_product(q, xs, codes, ws)
+    p, y = reference.ternary_int8_product_group_scales(q, xs, codes, ws)
+    for i in range(m):
+        for j in range(n):
+            assert abs(Fraction(float(y[i, j])) - exact[i][j]) <= abs(exact[i][j]) * Fraction(1, 10 ** 12)
+    # partials by brute force too
+    np.testing.assert_array_equal(p, _brute_partials(q, formats.pack_ternary(codes), k))
+
+    def far(yy):
+        return max(abs(Fraction(float(yy[i, j])) - exact[i][j]) / abs(exact[i][j])
+                   for i in range(m) for j in range(n)) > Fraction(1, 1000)
+    for bad in (xs[:, ::-1], np.roll(xs, 1, axis=1), np.repeat(xs[:, :1], 3, axis=1)):
+        _, yb = reference.ternary_int8_product_group_scales(q, np.ascontiguousarray(bad), codes, ws)
+        assert far(yb)
+    _, yb = reference.ternary_int8_product_group_scales(q, xs, codes, np.ascontiguousarray(ws[:, ::-1]))
+    assert far(yb)
+
+
 # ------------------------------------------------------------------ act order / zero points
 def _valid_gidx(rng, k):
     pi = rng.permutation(k)
