@@ -149,6 +149,28 @@ def _stream(device=None) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _check_tensor(name: str, t, shape: tuple, dtypes: tuple, device=None) -> None:
+    """Refuse, before any library call, a tensor whose shape, dtype, layout or
+    device the kernels would not read within bounds: the C ABI receives bare
+    pointers and cannot check sizes itself."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {[str(d) for d in dtypes]}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _check_gpu(name: str, t) -> None:
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (it is on {t.device})")
+
+
 @dataclasses.dataclass
 class PackedWeights:
     """Prepared planes on the device plus their metadata (see ``bpw_weights``)."""
@@ -165,6 +187,23 @@ class PackedWeights:
     def struct(self) -> BpwWeights:
         return BpwWeights(self.fmt, self.scale_dtype, 128, 0, self.n, self.k, _ptr(self.codes),
                           _ptr(self.scales), _ptr(self.zeros), _ptr(self.perm))
+
+    def validate(self, device) -> None:
+        """Check every plane against n, k and the format (shapes, dtypes, device)."""
+        torch = _torch()
+        if self.k < 128 or self.k % 128:
+            raise ValueError(f"K={self.k} must be a positive multiple of 128")
+        g = self.k // 128
+        cb = self.k // 4 if self.fmt == TERNARY2 else self.k // 2
+        sd = {F16: torch.float16, BF16: torch.bfloat16}.get(self.scale_dtype)
+        if sd is None:
+            raise ValueError(f"scale dtype code {self.scale_dtype} is neither F16 nor BF16")
+        _check_tensor("codes", self.codes, (self.n, cb), (torch.uint8,), device)
+        _check_tensor("scales", self.scales, (self.n, g), (sd,), device)
+        if self.zeros is not None:
+            _check_tensor("zeros", self.zeros, (self.n, (g + 1) // 2), (torch.uint8,), device)
+        if self.perm is not None:
+            _check_tensor("perm", self.perm, (self.k,), (torch.int32,), device)
 
     @property
     def logical_bytes(self) -> int:
@@ -252,8 +291,12 @@ def quantize_rows(x, q=None, x_scale=None):
     if x.dim() != 2 or not x.is_contiguous():
         raise ValueError("x must be a contiguous [M, K] tensor")
     m, k = x.shape
+    _check_tensor("x", x, (m, k), (torch.float32, torch.float16, torch.bfloat16))
     q = torch.empty((m, k), dtype=torch.int8, device=x.device) if q is None else q
     x_scale = torch.empty(m, dtype=torch.float32, device=x.device) if x_scale is None else x_scale
+    _check_tensor("q", q, (m, k), (torch.int8,), x.device)
+    _check_tensor("x_scale", x_scale, (m,), (torch.float32,), x.device)
+    _check_gpu("x", x)
     _check(lib().bpw_quantize_rows(_ptr(x), dtype_code(x.dtype), m, k, _ptr(q), _ptr(x_scale),
                                    _stream(x.device)))
     return q, x_scale
@@ -265,9 +308,15 @@ def quantize_groups(x, q=None, x_scale=None):
     if x.dim() != 2 or not x.is_contiguous():
         raise ValueError("x must be a contiguous [M, K] tensor")
     m, k = x.shape
+    if k % 128:
+        raise ValueError(f"K={k} must be a multiple of 128 for per-group scales")
+    _check_tensor("x", x, (m, k), (torch.float32, torch.float16, torch.bfloat16))
     q = torch.empty((m, k), dtype=torch.int8, device=x.device) if q is None else q
     if x_scale is None:
         x_scale = torch.empty((m, k // 128), dtype=torch.float32, device=x.device)
+    _check_tensor("q", q, (m, k), (torch.int8,), x.device)
+    _check_tensor("x_scale", x_scale, (m, k // 128), (torch.float32,), x.device)
+    _check_gpu("x", x)
     _check(lib().bpw_quantize_groups(_ptr(x), dtype_code(x.dtype), m, k, _ptr(q), _ptr(x_scale),
                                      _stream(x.device)))
     return q, x_scale
@@ -287,6 +336,11 @@ def _workspace(w, m, x_dtype, entry, device, workspace):
         return None, 0
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    if workspace.dim() != 1:
+        raise ValueError("workspace must be a 1-D uint8 tensor")
+    _check_tensor("workspace", workspace, (workspace.numel(),), (torch.uint8,), device)
+    if workspace.numel() < need:
+        raise ValueError(f"workspace has {workspace.numel()} bytes, this call needs {need}")
     return workspace, workspace.numel()
 
 
@@ -296,12 +350,26 @@ def _product(entry: int, w: PackedWeights, x, x_scale=None, out_dtype=None, out=
         raise ValueError("x must be a contiguous [M, K] tensor")
     m = x.shape[0]
     xd = dtype_code(x.dtype)
+    if xd not in (F16, BF16, I8):
+        raise ValueError(f"activations of dtype {x.dtype} are not supported (fp16, bf16 or int8)")
     if xd == I8 and x_scale is not None and x_scale.dim() == 2:
         xd = I8G                                   # one scale per (row, 128-group)
+    _check_tensor("x", x, (m, w.k), (x.dtype,))
+    w.validate(x.device)
+    if xd == I8:
+        if x_scale is None:
+            raise ValueError("int8 activations need x_scale [M]")
+        _check_tensor("x_scale", x_scale, (m,), (torch.float32,), x.device)
+    elif xd == I8G:
+        _check_tensor("x_scale", x_scale, (m, w.k // 128), (torch.float32,), x.device)
+    elif x_scale is not None:
+        raise ValueError("x_scale must be None for fp16/bf16 activations")
     if out is None:
         out_dtype = out_dtype if out_dtype is not None else (torch.float16 if xd in (I8, I8G) else x.dtype)
         out = torch.empty((m, w.n), dtype=out_dtype, device=x.device)
+    _check_tensor("out", out, (m, w.n), (torch.float32, torch.float16, torch.bfloat16), x.device)
     ws, ws_bytes = _workspace(w, m, xd, entry, x.device, workspace)
+    _check_gpu("x", x)
     st = w.struct()
     fn = lib().bpw_gemv_packed if entry == PATH_GEMV else lib().bpw_gemm_packed
     _check(fn(ctypes.byref(st), _ptr(x), xd, _ptr(x_scale), m, _ptr(out), dtype_code(out.dtype),
@@ -322,7 +390,14 @@ def gemm_packed(w: PackedWeights, x, x_scale=None, out_dtype=None, out=None, wor
 def partials(w: PackedWeights, q, path: int, m0: int, m1: int, n0: int, n1: int, workspace=None):
     """Exact int32 group partials of a window (bpw_partials)."""
     torch = _torch()
+    if q.dim() != 2:
+        raise ValueError("q must be an [M, K] int8 tensor")
     m = q.shape[0]
+    _check_tensor("q", q, (m, w.k), (torch.int8,))
+    w.validate(q.device)
+    if not (0 <= m0 < m1 <= m and 0 <= n0 < n1 <= w.n):
+        raise ValueError(f"window [{m0},{m1}) x [{n0},{n1}) outside M={m}, N={w.n}")
+    _check_gpu("q", q)
     g = w.k // 128
     out = torch.empty((m1 - m0, n1 - n0, g), dtype=torch.int32, device=q.device)
     ws, ws_bytes = (None, 0)
@@ -337,6 +412,14 @@ def partials(w: PackedWeights, q, path: int, m0: int, m1: int, n0: int, n1: int,
 def probe(kind: int, src, dst) -> None:
     """HBM probe (bpw_probe): streaming read or copy of ``src.nbytes`` bytes."""
     nbytes = src.numel() * src.element_size()
+    if not src.is_contiguous() or not dst.is_contiguous():
+        raise ValueError("src and dst must be contiguous")
+    if dst.device != src.device:
+        raise ValueError("src and dst must be on one device")
+    need = nbytes if kind == PROBE_COPY else probe_blocks(nbytes) * 4
+    if dst.numel() * dst.element_size() < need:
+        raise ValueError(f"dst holds {dst.numel() * dst.element_size()} bytes, the probe writes {need}")
+    _check_gpu("src", src)
     _check(lib().bpw_probe(kind, _ptr(src), _ptr(dst), nbytes, _stream(src.device)))
 
 
