@@ -3,11 +3,13 @@
 
 Headline step: one ternary x int8 decode GEMV (M=1, K=4096, N=14336, group 128)
 through bpw_gemv_packed, with its int8 activations (one fp32 scale per row)
-already resident in HBM. Weight copies totalling >= 1 GiB are rotated so each
-call streams its weights from HBM rather than the 256 MB Infinity Cache. The K
-timed steps run as one captured HIP graph, bracketed by synchronisation and
-HIP events on the launch stream. value = logical weight bytes (codes + scales)
-per call / time per call.
+already resident in HBM. Weight copies totalling >= 1 GiB are read as a ring
+so each call streams its weights from HBM rather than the 256 MB Infinity
+Cache. The K timed steps run as one captured HIP graph between HIP events on
+the launch stream; the graph is timed 7 times (after an untimed replay, and
+each time after half a ring of untimed calls and a spin kernel that hides the
+host's submission) and the median per call is reported, with the spread.
+value = logical weight bytes (codes + scales) per call / time per call.
 
 Also reported (same JSON line): the complete decode call (quantiser + GEMV),
 the other decode/prefill workloads (ternary decode at M=16, split-K long K,
@@ -15,8 +17,10 @@ per-group activation scales and on the 62 MB prefill weight; 4-bit decode GEMV
 with act order; bf16 prefill GEMM at M=2048; 4-bit x int8 prefill GEMM at
 M=2048; ternary x int8 prefill GEMM; hipBLASLt dense GEMMs at the prefill
 shapes as a platform reference), HBM read/copy probes, the roofline of the
-dominant kernel, and the CPU oracle timed on a bounded sample of the headline
-workload.
+dominant kernel (and its fraction of the read probe at the same byte count),
+the engine clock sampled through amdsmi during each prefill leg (for the
+clock-adjusted MFMA fraction), and the CPU oracle timed on bounded samples of
+the headline and the other workloads, with the host's core count and model.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
 """
@@ -37,6 +41,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 INT8_PEAK_TOPS = 5000.0
+PEAK_CLOCK_GHZ = 2.4        # engine clock of the published peaks
 METRIC = "weight GB/s (% HBM peak) at M=1 GEMV; TFLOP/s (% MFMA peak) at M=2048"
 # Hardware-counter summary of the dominant kernel (HBM bytes per launch from
 # FETCH_SIZE and WRITE_SIZE, scaled by the copy probe), and the sources it was
@@ -86,27 +91,142 @@ def rotated_copies(bpw, planes, min_bytes, max_copies=256):
     return copies
 
 
-def time_graph(torch, calls, steps, warmup):
-    """Capture `steps` calls (call(i) for i in range) into one graph; return ms per call."""
+REPEATS = 7
+SPIN_CYCLES = 4_000_000     # torch's spin kernel: keeps the GPU busy while the host submits a graph
+LAST_SPREAD = {}
+
+
+def time_calls(torch, call, ncopies, steps, warmup, repeats=REPEATS):
+    """Median ms per call of `steps` calls captured in one HIP graph.
+
+    call(c) launches one call that reads weight copy c. The copies form a ring
+    that is read in order; every graph is laid out so that between two reads of
+    one copy at least half the ring is read (>= 512 MB for a >= 1 GiB ring), so
+    the 256 MB Infinity Cache holds none of the timed bytes when a timed graph
+    starts. Sequence: a warm-up graph of `warmup` calls, replayed once; then per
+    repeat a flush graph (half a ring, untimed), torch's spin kernel (the host
+    submits the timed graph while it runs, so submission is not timed), and the
+    timed graph between two events on its stream. Every graph is replayed once
+    before anything is timed, so first-replay costs fall outside the events.
+    """
     stream = torch.cuda.Stream()
-    warm = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(warm, stream=stream):
-        for i in range(max(1, warmup)):
-            calls(i)
-    main = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(main, stream=stream):
-        for i in range(steps):
-            calls(i)
+    half = max(ncopies // 2, 1)
+
+    def capture(first, count):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(count):
+                call((first + i) % ncopies)
+        return g
+
+    timed_first = 0
+    timed = capture(timed_first, steps)
+    # the flush graph ends on the copy just before the timed graph's first copy
+    flush = capture((timed_first - half) % ncopies, half)
+    warm = capture((timed_first + half) % ncopies, max(warmup, 1))
     torch.cuda.synchronize()
-    if warmup > 0:
+    with torch.cuda.stream(stream):
+        timed.replay()                  # first replay of each graph: untimed
+        flush.replay()
         warm.replay()
+        events = []
+        for _ in range(repeats):
+            flush.replay()
+            torch.cuda._sleep(SPIN_CYCLES)
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            timed.replay()
+            ev1.record(stream)
+            events.append((ev0, ev1))
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    main.replay()
-    end.record()
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps
+    per_call = sorted(a.elapsed_time(b) / steps for a, b in events)
+    med = per_call[len(per_call) // 2]
+    LAST_SPREAD.clear()
+    LAST_SPREAD.update({"repeats": repeats, "min_us": per_call[0] * 1e3, "max_us": per_call[-1] * 1e3})
+    del timed, flush, warm
+    return med
+
+
+def spread():
+    return {k: round(v, 3) if isinstance(v, float) else v for k, v in LAST_SPREAD.items()}
+
+
+class ClockSampler:
+    """Mean engine (gfx) clock while a timed region runs, polled through amdsmi on a
+    host thread (read-only queries; no GPU work). None when amdsmi is unavailable."""
+
+    def __init__(self, period_s=0.002):
+        self.period, self.samples, self._stop, self._thread, self._h = period_s, [], None, None, None
+        try:
+            import amdsmi  # noqa: PLC0415
+            amdsmi.amdsmi_init()
+            self._amdsmi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+        except Exception:  # noqa: BLE001 (no amdsmi on this host: clock stays unknown)
+            self._amdsmi = None
+
+    def _read(self):
+        info = self._amdsmi.amdsmi_get_clock_info(self._h, self._amdsmi.AmdSmiClkType.GFX)
+        return float(info["clk"])
+
+    def __enter__(self):
+        import threading  # noqa: PLC0415
+        self.samples = []
+        if self._amdsmi is None:
+            return self
+        self._stop = threading.Event()
+
+        def run():
+            while not self._stop.is_set():
+                try:
+                    self.samples.append(self._read())
+                except Exception:  # noqa: BLE001
+                    return
+                self._stop.wait(self.period)
+        self._thread = threading.Thread(target=run, daemon=True)
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+
+    def mean_ghz(self):
+        return round(sum(self.samples) / len(self.samples) / 1000.0, 3) if self.samples else None
+
+
+CLOCK = None
+
+
+def clocked(fn):
+    """Run fn() under the clock sampler; returns (result, mean gfx clock in GHz or None)."""
+    global CLOCK
+    if CLOCK is None:
+        CLOCK = ClockSampler()
+    with CLOCK:
+        r = fn()
+    return r, CLOCK.mean_ghz()
+
+
+def decode_leg(name, m, k, n, nbytes, ms, ncopies, **extra):
+    gbs = nbytes / (ms * 1e6)
+    return {"workload": name, "M": m, "K": k, "N": n, "weight_bytes": nbytes, "us_per_call": ms * 1e3,
+            "GB_s": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS, "copies": ncopies, "spread": spread(), **extra}
+
+
+def gemm_leg(name, m, k, n, ms, clock_ghz, int8, **extra):
+    ops = 2.0 * m * n * k
+    rate = ops / (ms * 1e9)
+    peak = INT8_PEAK_TOPS if int8 else BF16_PEAK_TFLOPS
+    out = {"workload": name, "M": m, "K": k, "N": n, "us_per_call": ms * 1e3,
+           ("TOP_s" if int8 else "TFLOP_s"): rate,
+           ("frac_int8_mfma_peak" if int8 else "frac_bf16_mfma_peak"): rate / peak,
+           "gfx_clock_ghz": clock_ghz,
+           # the published peak scaled to the engine clock measured during the timed region
+           "frac_clock_adjusted_peak": None if not clock_ghz else rate / (peak * clock_ghz / PEAK_CLOCK_GHZ),
+           "spread": spread(), **extra}
+    return out
 
 
 def bench_ternary_decode(bpw, synth, torch, np, steps, warmup):
@@ -117,13 +237,14 @@ def bench_ternary_decode(bpw, synth, torch, np, steps, warmup):
     q, xs = bpw.quantize_rows(x)
     y = torch.empty((1, w.n), dtype=torch.float16, device="cuda")
     nbytes = copies[0].logical_bytes
-    log(f"[bench] ternary decode GEMV M=1 K={w.k} N={w.n}: {len(copies)} weight copies of {nbytes} B")
-    ms = time_graph(torch, lambda i: bpw.gemv_packed(copies[i % len(copies)], q, xs, out=y), steps, warmup)
+    nc = len(copies)
+    log(f"[bench] ternary decode GEMV M=1 K={w.k} N={w.n}: {nc} weight copies of {nbytes} B")
+    ms = time_calls(torch, lambda c: bpw.gemv_packed(copies[c], q, xs, out=y), nc, steps, warmup)
+    sp = spread()
     # complete decode call: quantise the fp32 row, then the GEMV
-    ms_full = time_graph(torch, lambda i: (bpw.quantize_rows(x, q, xs),
-                                           bpw.gemv_packed(copies[i % len(copies)], q, xs, out=y)),
-                         max(steps // 4, 1), max(warmup // 4, 1))
-    return w, nbytes, ms, ms_full, len(copies)
+    ms_full = time_calls(torch, lambda c: (bpw.quantize_rows(x, q, xs), bpw.gemv_packed(copies[c], q, xs, out=y)),
+                         nc, max(steps // 4, 1), max(warmup // 4, 1))
+    return w, nbytes, ms, sp, ms_full, nc
 
 
 def bench_ternary_decode_large(bpw, synth, torch, np, steps, warmup):
@@ -134,11 +255,8 @@ def bench_ternary_decode_large(bpw, synth, torch, np, steps, warmup):
     copies = rotated_copies(bpw, planes, 1 << 30)
     q, xs = bpw.quantize_rows(to_dev(w.x, "f32", torch, np))
     y = torch.empty((1, w.n), dtype=torch.float16, device="cuda")
-    nbytes = copies[0].logical_bytes
-    ms = time_graph(torch, lambda i: bpw.gemv_packed(copies[i % len(copies)], q, xs, out=y), steps, warmup)
-    return {"workload": "ternary_decode_gemv_large_weight", "M": 1, "K": w.k, "N": w.n, "weight_bytes": nbytes,
-            "us_per_call": ms * 1e3, "GB_s": nbytes / (ms * 1e6), "frac_hbm_peak": nbytes / (ms * 1e6) / HBM_PEAK_GBS,
-            "copies": len(copies)}
+    ms = time_calls(torch, lambda c: bpw.gemv_packed(copies[c], q, xs, out=y), len(copies), steps, warmup)
+    return decode_leg("ternary_decode_gemv_large_weight", 1, w.k, w.n, copies[0].logical_bytes, ms, len(copies))
 
 
 def bench_probe(bpw, torch, kind, nbytes, steps, warmup):
@@ -154,10 +272,10 @@ def bench_probe(bpw, torch, kind, nbytes, steps, warmup):
     else:
         sink = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
         moved, name = 2 * nbytes, "hbm_copy_probe"
-    ms = time_graph(torch, lambda i: bpw.probe(kind, bufs[i % count], sink), steps, warmup)
+    ms = time_calls(torch, lambda c: bpw.probe(kind, bufs[c], sink), count, steps, warmup)
     del bufs
     return {"workload": name, "bytes": nbytes, "bytes_moved": moved, "us_per_call": ms * 1e3,
-            "GB_s": moved / (ms * 1e6), "copies": count}
+            "GB_s": moved / (ms * 1e6), "copies": count, "spread": spread()}
 
 
 def bench_ternary_decode_m(bpw, synth, torch, np, steps, warmup, m=16):
@@ -165,14 +283,10 @@ def bench_ternary_decode_m(bpw, synth, torch, np, steps, warmup, m=16):
     w = synth.ternary_decode(m)
     planes = bpw.prepare_packed_host(bpw.TERNARY2, w.codes, w.scales)
     copies = rotated_copies(bpw, planes, 1 << 30)
-    x = to_dev(w.x, "f32", torch, np)
-    q, xs = bpw.quantize_rows(x)
+    q, xs = bpw.quantize_rows(to_dev(w.x, "f32", torch, np))
     y = torch.empty((m, w.n), dtype=torch.float16, device="cuda")
-    nbytes = copies[0].logical_bytes
-    ms = time_graph(torch, lambda i: bpw.gemv_packed(copies[i % len(copies)], q, xs, out=y), steps, warmup)
-    return {"workload": "ternary_decode_gemv", "M": m, "K": w.k, "N": w.n, "weight_bytes": nbytes,
-            "us_per_call": ms * 1e3, "GB_s": nbytes / (ms * 1e6), "frac_hbm_peak": nbytes / (ms * 1e6) / HBM_PEAK_GBS,
-            "copies": len(copies)}
+    ms = time_calls(torch, lambda c: bpw.gemv_packed(copies[c], q, xs, out=y), len(copies), steps, warmup)
+    return decode_leg("ternary_decode_gemv", m, w.k, w.n, copies[0].logical_bytes, ms, len(copies))
 
 
 def bench_ternary_long_k(bpw, synth, torch, np, steps, warmup, m=16, k=14336, n=4096):
@@ -181,15 +295,12 @@ def bench_ternary_long_k(bpw, synth, torch, np, steps, warmup, m=16, k=14336, n=
     w = synth.ternary_int8(f"long_k_m{m}", 5, m, k, n, 0.005, 0.05, "f16")
     planes = bpw.prepare_packed_host(bpw.TERNARY2, w.codes, w.scales)
     copies = rotated_copies(bpw, planes, 1 << 30)
-    x = to_dev(w.x, "f32", torch, np)
-    q, xs = bpw.quantize_rows(x)
+    q, xs = bpw.quantize_rows(to_dev(w.x, "f32", torch, np))
     y = torch.empty((m, n), dtype=torch.float16, device="cuda")
     ws = torch.empty(max(bpw.workspace_size(copies[0], m, bpw.I8, bpw.PATH_GEMV), 1), dtype=torch.uint8, device="cuda")
-    nbytes = copies[0].logical_bytes
-    ms = time_graph(torch, lambda i: bpw.gemv_packed(copies[i % len(copies)], q, xs, out=y, workspace=ws), steps, warmup)
-    return {"workload": "ternary_decode_gemv_long_k", "M": m, "K": k, "N": n, "weight_bytes": nbytes,
-            "us_per_call": ms * 1e3, "GB_s": nbytes / (ms * 1e6), "frac_hbm_peak": nbytes / (ms * 1e6) / HBM_PEAK_GBS,
-            "copies": len(copies)}
+    ms = time_calls(torch, lambda c: bpw.gemv_packed(copies[c], q, xs, out=y, workspace=ws), len(copies), steps,
+                    warmup)
+    return decode_leg("ternary_decode_gemv_long_k", m, k, n, copies[0].logical_bytes, ms, len(copies))
 
 
 def bench_ternary_decode_groups(bpw, synth, torch, np, steps, warmup, m=1):
@@ -201,14 +312,15 @@ def bench_ternary_decode_groups(bpw, synth, torch, np, steps, warmup, m=1):
     x = to_dev(w.x, "f32", torch, np)
     q, xs = bpw.quantize_groups(x)
     y = torch.empty((m, w.n), dtype=torch.float16, device="cuda")
-    nbytes = copies[0].logical_bytes
-    ms = time_graph(torch, lambda i: bpw.gemv_packed(copies[i % len(copies)], q, xs, out=y), steps, warmup)
-    ms_full = time_graph(torch, lambda i: (bpw.quantize_groups(x, q, xs),
-                                           bpw.gemv_packed(copies[i % len(copies)], q, xs, out=y)),
-                         max(steps // 4, 1), max(warmup // 4, 1))
-    return {"workload": "ternary_decode_gemv_group_scales", "M": m, "K": w.k, "N": w.n, "weight_bytes": nbytes,
-            "us_per_call": ms * 1e3, "GB_s": nbytes / (ms * 1e6), "frac_hbm_peak": nbytes / (ms * 1e6) / HBM_PEAK_GBS,
-            "complete_call_us": ms_full * 1e3, "copies": len(copies)}
+    nc = len(copies)
+    ms = time_calls(torch, lambda c: bpw.gemv_packed(copies[c], q, xs, out=y), nc, steps, warmup)
+    sp = spread()
+    ms_full = time_calls(torch, lambda c: (bpw.quantize_groups(x, q, xs), bpw.gemv_packed(copies[c], q, xs, out=y)),
+                         nc, max(steps // 4, 1), max(warmup // 4, 1))
+    leg = decode_leg("ternary_decode_gemv_group_scales", m, w.k, w.n, copies[0].logical_bytes, ms, nc,
+                     complete_call_us=ms_full * 1e3)
+    leg["spread"] = sp
+    return leg
 
 
 def bench_w4_decode(bpw, synth, torch, np, steps, warmup, m=1):
@@ -218,11 +330,8 @@ def bench_w4_decode(bpw, synth, torch, np, steps, warmup, m=1):
     x = to_dev(w.x, "f16", torch, np)
     y = torch.empty((m, w.n), dtype=torch.float16, device="cuda")
     ws = torch.empty(bpw.workspace_size(copies[0], m, bpw.F16, bpw.PATH_GEMV), dtype=torch.uint8, device="cuda")
-    nbytes = copies[0].logical_bytes
-    ms = time_graph(torch, lambda i: bpw.gemv_packed(copies[i % len(copies)], x, out=y, workspace=ws), steps, warmup)
-    return {"workload": "w4a16_decode_gemv", "M": m, "K": w.k, "N": w.n, "act_order": True,
-            "weight_bytes": nbytes, "us_per_call": ms * 1e3, "GB_s": nbytes / (ms * 1e6),
-            "frac_hbm_peak": nbytes / (ms * 1e6) / HBM_PEAK_GBS, "copies": len(copies)}
+    ms = time_calls(torch, lambda c: bpw.gemv_packed(copies[c], x, out=y, workspace=ws), len(copies), steps, warmup)
+    return decode_leg("w4a16_decode_gemv", m, w.k, w.n, copies[0].logical_bytes, ms, len(copies), act_order=True)
 
 
 def bench_w4_prefill(bpw, synth, torch, np, steps, warmup):
@@ -231,10 +340,9 @@ def bench_w4_prefill(bpw, synth, torch, np, steps, warmup):
     copies = rotated_copies(bpw, planes, 512 << 20, max_copies=18)
     x = to_dev(w.x, "bf16", torch, np)
     y = torch.empty((w.m, w.n), dtype=torch.bfloat16, device="cuda")
-    ms = time_graph(torch, lambda i: bpw.gemm_packed(copies[i % len(copies)], x, out=y), steps, warmup)
-    flop = 2.0 * w.m * w.n * w.k
-    return {"workload": "w4a16_prefill_gemm", "M": w.m, "K": w.k, "N": w.n, "us_per_call": ms * 1e3,
-            "TFLOP_s": flop / (ms * 1e9), "frac_bf16_mfma_peak": flop / (ms * 1e9) / BF16_PEAK_TFLOPS}
+    ms, ghz = clocked(lambda: time_calls(torch, lambda c: bpw.gemm_packed(copies[c], x, out=y), len(copies), steps,
+                                         warmup))
+    return gemm_leg("w4a16_prefill_gemm", w.m, w.k, w.n, ms, ghz, False)
 
 
 def bench_ternary_prefill(bpw, synth, torch, np, steps, warmup):
@@ -242,14 +350,12 @@ def bench_ternary_prefill(bpw, synth, torch, np, steps, warmup):
     planes = bpw.prepare_packed_host(bpw.TERNARY2, w.codes, w.scales)
     w.codes = None
     copies = rotated_copies(bpw, planes, 512 << 20, max_copies=9)
-    x = to_dev(w.x, "f32", torch, np)
-    q, xs = bpw.quantize_rows(x)
+    q, xs = bpw.quantize_rows(to_dev(w.x, "f32", torch, np))
     y = torch.empty((w.m, w.n), dtype=torch.float16, device="cuda")
     ws = torch.empty(bpw.workspace_size(copies[0], w.m, bpw.I8, bpw.PATH_GEMM), dtype=torch.uint8, device="cuda")
-    ms = time_graph(torch, lambda i: bpw.gemm_packed(copies[i % len(copies)], q, xs, out=y, workspace=ws), steps, warmup)
-    ops = 2.0 * w.m * w.n * w.k
-    return {"workload": "ternary_int8_prefill_gemm", "M": w.m, "K": w.k, "N": w.n, "us_per_call": ms * 1e3,
-            "TOP_s": ops / (ms * 1e9), "frac_int8_mfma_peak": ops / (ms * 1e9) / INT8_PEAK_TOPS}
+    ms, ghz = clocked(lambda: time_calls(torch, lambda c: bpw.gemm_packed(copies[c], q, xs, out=y, workspace=ws),
+                                         len(copies), steps, warmup))
+    return gemm_leg("ternary_int8_prefill_gemm", w.m, w.k, w.n, ms, ghz, True)
 
 
 def bench_w4a8_prefill(bpw, synth, torch, np, steps, warmup):
@@ -260,10 +366,9 @@ def bench_w4a8_prefill(bpw, synth, torch, np, steps, warmup):
     q, xs = bpw.quantize_rows(to_dev(w.x, "bf16", torch, np))
     y = torch.empty((w.m, w.n), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(bpw.workspace_size(copies[0], w.m, bpw.I8, bpw.PATH_GEMM), dtype=torch.uint8, device="cuda")
-    ms = time_graph(torch, lambda i: bpw.gemm_packed(copies[i % len(copies)], q, xs, out=y, workspace=ws), steps, warmup)
-    ops = 2.0 * w.m * w.n * w.k
-    return {"workload": "w4a8_prefill_gemm", "M": w.m, "K": w.k, "N": w.n, "us_per_call": ms * 1e3,
-            "TOP_s": ops / (ms * 1e9), "frac_int8_mfma_peak": ops / (ms * 1e9) / INT8_PEAK_TOPS}
+    ms, ghz = clocked(lambda: time_calls(torch, lambda c: bpw.gemm_packed(copies[c], q, xs, out=y, workspace=ws),
+                                         len(copies), steps, warmup))
+    return gemm_leg("w4a8_prefill_gemm", w.m, w.k, w.n, ms, ghz, True, activations="int8 + fp32 row scale")
 
 
 def bench_dense_reference(torch, steps=20, warmup=5):
@@ -301,27 +406,84 @@ def bench_dense_reference(torch, steps=20, warmup=5):
     return out
 
 
-def cpu_baseline(synth, np, budget_s=12.0):
-    """The CPU oracle (unchanged) on the headline workload, repeated for ~budget_s."""
-    from oracle import quant, reference  # noqa: PLC0415 (test infrastructure, this leg only)
+def host_info():
+    """BLAS threads the oracle runs on, the host's CPU count and CPU model."""
     try:
         from threadpoolctl import threadpool_info  # noqa: PLC0415
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
+    except Exception:  # noqa: BLE001
         threads = os.cpu_count() or 1
-    w = synth.ternary_decode(1)
-    nbytes = w.n * w.k // 4 + w.n * (w.k // 128) * 2
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return threads, os.cpu_count(), model
+
+
+def _repeat(fn, budget_s):
+    """Call fn until budget_s has passed (at least once); returns (calls, seconds)."""
     reps, t0 = 0, time.perf_counter()
     while True:
-        q, xs = quant.quantize_rows(w.x)
-        reference.ternary_int8_product(q, xs, w.codes, w.scales)
+        fn()
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
-            break
-    return {"value": nbytes * reps / (el * 1e9), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            return reps, el
+
+
+def cpu_baselines(synth, np, budget_s=12.0):
+    """The CPU oracle, unchanged, timed on bounded samples of the workloads: the headline
+    decode GEMV (quantise + exact int group partials + fp64 fold), the W4A16 decode GEMV
+    (dequantise through g_idx + fp64 product), the W4A16 prefill GEMM (rounded dequant +
+    fp64 dgemm) and a leading row slice of the ternary x int8 prefill GEMM (its full
+    M x N x G int64 partials would take 60 GB; the oracle's cost is linear in M)."""
+    from oracle import quant, reference  # noqa: PLC0415 (test infrastructure, this leg only)
+    threads, cpus, model = host_info()
+    legs = []
+    w = synth.ternary_decode(1)
+    nbytes = w.n * w.k // 4 + w.n * (w.k // 128) * 2
+
+    def headline():
+        q, xs = quant.quantize_rows(w.x)
+        reference.ternary_int8_product(q, xs, w.codes, w.scales)
+    reps, el = _repeat(headline, budget_s)
+    head = {"value": nbytes * reps / (el * 1e9), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"ternary_decode M=1 K={w.k} N={w.n}: quantise + exact int group partials + fp64 fold, "
-                      f"{reps} full calls in {el:.1f} s", "seconds_per_call": el / reps}
+                      f"{reps} full calls in {el:.1f} s", "seconds_per_call": el / reps,
+            "host_cpus": cpus, "cpu_model": model}
+
+    w3 = synth.w4a16_decode(1)
+    b3 = w3.n * w3.k // 2 + w3.n * w3.groups * 2 + w3.n * ((w3.groups + 1) // 2)
+    x3 = w3.x_f32()
+    reps, el = _repeat(lambda: reference.product(
+        x3, reference.weights_int4(w3.codes, w3.scales_f64(), w3.zeros, w3.g_idx)), budget_s / 3)
+    legs.append({"workload": "w4a16_decode_gemv", "M": 1, "K": w3.k, "N": w3.n, "GB_s": b3 * reps / (el * 1e9),
+                 "seconds_per_call": el / reps, "calls": reps})
+    del w3, x3
+
+    w4 = synth.w4a16_prefill()
+    x4 = w4.x_f32()
+    reps, el = _repeat(lambda: reference.product(
+        x4, reference.weights_int4_rounded(w4.codes, w4.scales_f64(), None, None, "bf16")), budget_s / 3)
+    legs.append({"workload": "w4a16_prefill_gemm", "M": w4.m, "K": w4.k, "N": w4.n,
+                 "TFLOP_s": 2.0 * w4.m * w4.n * w4.k * reps / (el * 1e12), "seconds_per_call": el / reps,
+                 "calls": reps})
+    del w4, x4
+
+    rows = 16
+    w5 = synth.leading_rows(synth.ternary_prefill(), rows)
+    q5, xs5 = quant.quantize_rows(w5.x)
+    reps, el = _repeat(lambda: reference.ternary_int8_product(q5, xs5, w5.codes, w5.scales), budget_s / 3)
+    legs.append({"workload": "ternary_int8_prefill_gemm", "M": rows, "K": w5.k, "N": w5.n,
+                 "TOP_s": 2.0 * rows * w5.n * w5.k * reps / (el * 1e12), "seconds_per_call": el / reps,
+                 "calls": reps, "sample": f"leading {rows} of 4096 rows (exact int partials + fp64 fold)"})
+    head["other_workloads"] = legs
+    return head
 
 
 def main():
@@ -346,14 +508,18 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
-    w, nbytes, ms, ms_full, ncopies = bench_ternary_decode(bpw, synth, torch, np, args.steps, args.warmup)
+    w, nbytes, ms, sp, ms_full, ncopies = bench_ternary_decode(bpw, synth, torch, np, args.steps, args.warmup)
     gbs = nbytes / (ms * 1e6)
-    log(f"[bench] ternary decode: {ms * 1e3:.2f} us/call, {gbs:.0f} GB/s; complete call {ms_full * 1e3:.2f} us")
+    log(f"[bench] ternary decode: {ms * 1e3:.3f} us/call (spread {sp}), {gbs:.0f} GB/s; "
+        f"complete call {ms_full * 1e3:.2f} us")
     extra = []
+    read_probe = None
     for kind in (bpw.PROBE_READ, bpw.PROBE_COPY):
         probe = bench_probe(bpw, torch, kind, nbytes, args.steps, args.warmup)
         log(f"[bench] {json.dumps(probe)}")
         extra.append(probe)
+        if kind == bpw.PROBE_READ:
+            read_probe = probe["GB_s"]
         torch.cuda.empty_cache()
     if not args.no_extra:
         runs = ((bench_ternary_decode_m, 900, 300, {"m": 16}), (bench_ternary_long_k, 600, 200, {"m": 16}),
@@ -370,9 +536,10 @@ def main():
             log(f"[bench] {json.dumps(r)}")
             extra.append(r)
         torch.cuda.empty_cache()
-    cpu = None if args.no_cpu else cpu_baseline(synth, np)
+    cpu = None if args.no_cpu else cpu_baselines(synth, np)
     if cpu:
-        log(f"[bench] cpu oracle: {cpu['value']:.3f} GB/s on {cpu['cores']} threads")
+        log(f"[bench] cpu oracle: {cpu['value']:.3f} GB/s on {cpu['cores']} threads "
+            f"({cpu['host_cpus']} host CPUs, {cpu['cpu_model']}); {json.dumps(cpu['other_workloads'])}")
     out = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
@@ -382,6 +549,9 @@ def main():
                    "out": "f16", "rotated_weight_copies": ncopies},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic()},
+        "frac_of_read_probe": round(gbs / read_probe, 4) if read_probe else None,
+        "timing": {"median_of_repeats": sp["repeats"], "per_call_min_us": sp["min_us"],
+                   "per_call_max_us": sp["max_us"]},
         "complete_call_us": round(ms_full * 1e3, 3),
         "cpu_baseline": cpu,
         "other_workloads": extra,

@@ -120,7 +120,7 @@ __device__ __forceinline__ int xcd_swizzle(int bid, int nblocks) {
 // synchronises before the data is read.
 __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(src)
-               : "memory");
+               : "memory", "m0");
 }
 
 // Allow a kernel to launch with more than 64 KB of dynamic LDS (gfx950 has 160 KB

@@ -5,8 +5,10 @@ global->LDS copies, LDS reads into AGPRs), so the compiler does not track them.
 Its waits are tied to the loaded values, which keeps every use of a value
 behind the wait. This test compiles the kernels to gfx950 assembly with the
 library's own flags. It then checks that no instruction writes a register
-while an untracked load into that register is still in flight: a late write
-by the load would clobber an unrelated value, an address for instance.
+while a load into that register is still in flight (a late write by the load
+would clobber an unrelated value, an address for instance), and that no
+instruction reads such a register before the load has landed (it would see a
+stale value: an MFMA operand, a copy out of an AGPR, a spill).
 
 The scan is linear over each kernel body; every group of the main loop ends
 with a full wait, so no load is in flight across the loop edge.
@@ -37,8 +39,12 @@ def _operands(line):
     return [t.strip() for t in parts[1].split(",")] if len(parts) > 1 else []
 
 
+SOURCE_ONLY = ("global_store", "ds_write", "buffer_store", "global_load_lds", "flat_store", "scratch_store")
+
+
 def writes_before_wait(body):
-    """Instructions that write a register an in-flight load will still write."""
+    """Instructions that write a register an in-flight load will still write, or
+    read a register before the in-flight load into it has landed."""
     vm, lgkm, bad = [], [], []
     for no, line in enumerate(body):
         if not line or line.startswith((";", ".")) or line.endswith(":"):
@@ -55,12 +61,19 @@ def writes_before_wait(body):
                 lgkm = lgkm[len(lgkm) - n:] if n else []
             continue
         ops = _operands(line)
-        writes = set()
-        if ops and not op.startswith(("s_", "global_store", "ds_write", "buffer_store", "global_load_lds")):
+        writes, reads = set(), set()
+        if ops and not op.startswith(("s_",) + SOURCE_ONLY):
             writes = _regs(ops[0])
+            srcs = ops[1:]
+        else:
+            srcs = ops
+        for tok in srcs:
+            reads |= _regs(tok.split()[0]) if tok else set()
         for dst, at, text in vm + lgkm:
             if dst & writes:
-                bad.append(f"line {no}: {line}  (load in flight since line {at}: {text})")
+                bad.append(f"line {no}: {line}  (writes a register loaded since line {at}: {text})")
+            elif dst & reads:
+                bad.append(f"line {no}: {line}  (reads a register loaded since line {at}: {text})")
         if op.startswith(("global_", "buffer_", "flat_", "scratch_")):
             loads_reg = op.startswith("global_load") and not op.startswith("global_load_lds")
             vm.append((_regs(ops[0]) if loads_reg else set(), no, line))
@@ -106,3 +119,14 @@ def test_checker_flags_a_clobbered_destination():
     # an AGPR LDS read overwritten before lgkmcnt: flagged
     body = ["ds_read_b128 a[0:3], v1", "v_accvgpr_write_b32 a2, v5", "s_waitcnt lgkmcnt(0)"]
     assert writes_before_wait(body)
+    # its destination read before the wait (an MFMA operand, a copy out of it): flagged
+    body = ["ds_read_b128 a[0:3], v1", "v_mfma_i32_32x32x32_i8 v[0:15], a[0:3], v[20:23], 0", "s_waitcnt lgkmcnt(0)"]
+    assert writes_before_wait(body)
+    body = ["ds_read_b128 a[4:7], v1", "v_accvgpr_read_b32 v9, a6", "s_waitcnt lgkmcnt(0)"]
+    assert writes_before_wait(body)
+    body = ["global_load_dwordx4 v[8:11], v[2:3], off", "global_store_dword v[4:5], v9, off", "s_waitcnt vmcnt(0)"]
+    assert writes_before_wait(body)
+    # the same reads after the wait, and reads of other registers before it: clean
+    body = ["ds_read_b128 a[0:3], v1", "v_accvgpr_read_b32 v9, a6", "s_waitcnt lgkmcnt(0)",
+            "v_mfma_i32_32x32x32_i8 v[0:15], a[0:3], v[20:23], 0"]
+    assert not writes_before_wait(body)
