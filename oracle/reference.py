@@ -20,6 +20,13 @@ is a small integer times an fp16/bf16 scale) and multiplies with BLAS in fp64.
   prompt GEMM): per group an exact integer dot of the int8 activations with
   the codes, the weight offset entering through the group's activation sum;
   here the exact partial ``sum q * (code - zero)`` folded like the ternary one.
+* 4-bit weights x int8 activations in the page's own form -- "TensorFold PR
+  #1176", "What changes": the weight is affine, ``s * code + b`` per group
+  (here ``b = -zero * s``), the activations are int8 with one scale ``a``
+  and an exact fp32 sum per group, and each group contributes
+  ``s * a * (code . q) + b * sum(x)``: the dot on the raw codes 0..15 is
+  exact in integers, the offset enters through the sum of the unquantised
+  activations.
 * Rounded dequantisation for the large-M float path -- the pages' float
   kernels round the dequantised weight to the activation dtype before the
   product ("Kernel experiments", Test 5's batched GEMV; the mate PR's note
@@ -181,3 +188,39 @@ def int4_int8_product(q, x_scale, codes, scales, zeros=None, g_idx=None):
     s = np.asarray(scales, np.float64)
     y = np.einsum("mng,ng->mn", p.astype(np.float64), s) * np.asarray(x_scale, np.float64)[:, None]
     return p, y
+
+
+# ------------------------------------------------- 4-bit x int8, affine form
+def int4_raw_partials(q: np.ndarray, codes: np.ndarray, g_idx=None) -> np.ndarray:
+    """Exact int group dots of the raw 4-bit codes with int8 activations:
+
+        D[m, n, g] = sum over k in group g of q[m, k] * code[n, k],   code in 0..15,
+
+    group(k) = g_idx[k] under act order, else k // 128. |D| <= 127 * 15 * 128 < 2**53,
+    so each group's fp64 matmul of integers is exact; returned as int64.
+    """
+    m, k = q.shape
+    n = codes.shape[0]
+    groups = k // GROUP
+    grp = np.arange(k) // GROUP if g_idx is None else np.asarray(g_idx, np.int64)
+    qf = q.astype(np.float64)
+    out = np.empty((m, n, groups), dtype=np.int64)
+    for g in range(groups):
+        cols = np.flatnonzero(grp == g)
+        out[:, :, g] = (qf[:, cols] @ codes[:, cols].astype(np.float64).T).astype(np.int64)
+    return out
+
+
+def w4a8_affine_product(q, a, sums, codes, scales, zeros=None, g_idx=None):
+    """"TensorFold PR #1176": y[m,n] = sum_g s[n,g] * a[m,g] * D[m,n,g] + b[n,g] * sums[m,g]
+    in fp64, with b = -zero * s (zero 8 for symmetric codes) and D from
+    ``int4_raw_partials``; a and sums come from the group quantiser with the sums
+    (``oracle.quant.quantize_groups_sums``), grouped like the weight. Returns (D, y)."""
+    d = int4_raw_partials(q, codes, g_idx)
+    s = np.asarray(scales, np.float64)
+    z = 8.0 if zeros is None else np.asarray(zeros, np.float64)
+    b = -z * s
+    af = np.asarray(a, np.float64)
+    sf = np.asarray(sums, np.float64)
+    y = np.einsum("mng,ng,mg->mn", d.astype(np.float64), s, af) + sf @ b.T
+    return d, y

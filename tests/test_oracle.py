@@ -596,3 +596,182 @@ def test_quantizer_non_finite_blocks():
     qr, sr = quant.quantize_rows(xr)
     _, y = reference.ternary_int8_product(qr, sr, codes, scales)
     assert np.isnan(y[1]).all() and np.isfinite(y[[0, 2]]).all()
+
+
+# ------------------------------------------------- W4A8 in TensorFold's affine form
+def _nearest_f32(exact: Fraction) -> np.float32:
+    """Brute force: the fp32 value nearest to an exact rational (ties to an even significand)."""
+    c = np.float32(float(exact))
+    cands = {float(c), float(np.nextafter(c, np.float32(np.inf))), float(np.nextafter(c, np.float32(-np.inf)))}
+    best = min(cands, key=lambda v: (abs(Fraction(v) - exact), int(np.float32(v).view(np.uint32)) % 2))
+    return np.float32(best)
+
+
+def test_exact_sum_f32_against_fraction_rounding():
+    rng = np.random.default_rng(7201)
+    cases = [rng.standard_normal(128).astype(np.float32) for _ in range(40)]
+    cases += [(rng.standard_normal(128) * np.exp2(rng.integers(-40, 40, 128))).astype(np.float32) for _ in range(40)]
+    # fp64 sum lands exactly on an fp32 midpoint; the exact sum is on it, above it, below it
+    cases += [np.array([1.0, 2.0 ** -24], np.float32),
+              np.array([1.0, 2.0 ** -24, 2.0 ** -60], np.float32),
+              np.array([1.0, 2.0 ** -24, -(2.0 ** -60)], np.float32),
+              np.array([1.0 + 2.0 ** -23, 2.0 ** -24], np.float32),
+              np.array([3.0e38, 3.0e38, -3.0e38], np.float32),
+              np.zeros(128, np.float32), np.array([-0.0, 0.0], np.float32)]
+    for v in cases:
+        exact = sum((Fraction(float(t)) for t in v), Fraction(0))
+        got = quant.exact_sum_f32(v)
+        want = _nearest_f32(exact)
+        assert got == want, (v[:4], got, want)
+    assert quant.exact_sum_f32(np.array([1.0, 2.0 ** -24, 2.0 ** -60], np.float32)) == np.float32(1.0 + 2.0 ** -23)
+    assert quant.exact_sum_f32(np.array([1.0, 2.0 ** -24, -(2.0 ** -60)], np.float32)) == np.float32(1.0)
+    assert quant.exact_sum_f32(np.array([1.0 + 2.0 ** -23, 2.0 ** -24], np.float32)) == np.float32(1.0 + 2.0 ** -22)
+
+
+def test_quantize_groups_sums_rule():
+    rng = np.random.default_rng(7202)
+    x = rng.standard_normal((4, 512)).astype(np.float32)
+    x[1, 128:256] = 0.0                                        # an all-zero group
+    x[2, 0] = 127.0                                            # amax 127 -> a = 1 exactly
+    q, a, sums = quant.quantize_groups_sums(x)
+    xb = x.reshape(4, 4, 128)
+    # a = fl32(amax / 127), an IEEE division (not the reciprocal multiply of the row quantiser)
+    np.testing.assert_array_equal(a, (np.abs(xb).max(-1) / np.float32(127)).astype(np.float32))
+    assert a[2, 0] == 1.0 and np.array_equal(q[2, :128], np.rint(x[2, :128]).astype(np.int8))
+    assert a[1, 1] == 0.0 and not q[1, 128:256].any() and sums[1, 1] == 0.0
+    qb = q.reshape(4, 4, 128).astype(np.float64)
+    nz = a > 0
+    assert np.abs(q).max() <= 127 and np.all(np.abs(qb).max(-1)[nz] == 127)
+    err = np.abs(qb * a[..., None] - xb)
+    assert np.all(err <= a[..., None] / 2 * (1 + 2.0 ** -20))
+    for i in range(4):
+        for g in range(4):
+            exact = sum((Fraction(float(t)) for t in xb[i, g]), Fraction(0))
+            assert sums[i, g] == _nearest_f32(exact)
+    # a value where the division and the reciprocal multiply round apart: the division wins
+    for amax in rng.uniform(0.5, 8.0, 2000).astype(np.float32):
+        div = np.float32(amax / np.float32(127.0))
+        mul = np.float32(amax * quant.INV127)
+        if div != mul:
+            row = np.zeros((1, 128), np.float32)
+            row[0, 5] = -amax
+            _, aa, _ = quant.quantize_groups_sums(row)
+            assert aa[0, 0] == div
+            break
+    else:
+        pytest.fail("no amax separates the two scale rules")
+
+
+def test_quantize_groups_sums_follows_the_weight_groups():
+    rng = np.random.default_rng(7203)
+    x = rng.standard_normal((3, 512)).astype(np.float32)
+    g_idx = _valid_gidx(rng, 512)
+    perm = reference.act_order_perm(g_idx, 512)
+    q1, a1, s1 = quant.quantize_groups_sums(x, perm)
+    q2, a2, s2 = quant.quantize_groups_sums(np.ascontiguousarray(x[:, perm]))
+    np.testing.assert_array_equal(q1[:, perm], q2)
+    np.testing.assert_array_equal(a1, a2)
+    np.testing.assert_array_equal(s1, s2)
+    # group g of the permuted form is the columns whose g_idx is g
+    for g in range(4):
+        cols = np.flatnonzero(g_idx == g)
+        assert a1[0, g] == np.float32(np.abs(x[0, cols]).max() / np.float32(127))
+
+
+def test_quantize_groups_sums_non_finite_group():
+    x = np.ones((1, 256), np.float32)
+    x[0, 200] = np.inf
+    q, a, s = quant.quantize_groups_sums(x)
+    assert a[0, 0] == np.float32(1.0 / 127.0) and s[0, 0] == 128.0
+    assert np.isnan(a[0, 1]) and np.isnan(s[0, 1]) and not q[0, 128:].any()
+
+
+@pytest.mark.parametrize("m,k,n,act", [(1, 128, 3, False), (3, 256, 4, True), (2, 384, 2, True)])
+def test_int4_raw_partials_brute_force(m, k, n, act):
+    rng = np.random.default_rng(7204 + m * 10 + n)
+    q = rng.integers(-127, 128, size=(m, k), dtype=np.int8)
+    codes = rng.integers(0, 16, size=(n, k), dtype=np.uint8)
+    g_idx = _valid_gidx(rng, k) if act else None
+    d = reference.int4_raw_partials(q, codes, g_idx)
+    for mi in range(m):
+        for ni in range(n):
+            for g in range(k // 128):
+                cols = range(g * 128, g * 128 + 128) if g_idx is None else np.flatnonzero(g_idx == g)
+                assert d[mi, ni, g] == sum(int(q[mi, c]) * int(codes[ni, c]) for c in cols)
+    # extremes: |D| reaches 127 * 15 * 128
+    qx = np.full((1, 128), -127, np.int8)
+    cx = np.full((1, 128), 15, np.uint8)
+    assert reference.int4_raw_partials(qx, cx)[0, 0, 0] == -127 * 15 * 128
+
+
+def _fraction_affine(q, a, sums, codes, scales, zeros, g_idx):
+    m, k = q.shape
+    n = codes.shape[0]
+    out = np.empty((m, n), object)
+    for mi in range(m):
+        for ni in range(n):
+            acc = Fraction(0)
+            for g in range(k // 128):
+                cols = range(g * 128, g * 128 + 128) if g_idx is None else np.flatnonzero(g_idx == g)
+                dot = sum(int(q[mi, c]) * int(codes[ni, c]) for c in cols)
+                s = Fraction(float(scales[ni, g]))
+                z = 8 if zeros is None else int(zeros[ni, g])
+                acc += s * Fraction(float(a[mi, g])) * dot + (-z * s) * Fraction(float(sums[mi, g]))
+            out[mi, ni] = acc
+    return out
+
+
+@pytest.mark.parametrize("zp,act", [(False, False), (True, False), (True, True)])
+def test_w4a8_affine_product_fraction_brute_force(zp, act):
+    """Distinct scales, zero points, activation scales and sums everywhere; dropping the
+    offset term, flipping its sign, or taking it from the quantised sum a * sum(q) in
+    place of the exact sum of x must fail."""
+    rng = np.random.default_rng(7210 + 2 * zp + act)
+    m, k, n = 3, 384, 4
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    codes = rng.integers(0, 16, size=(n, k), dtype=np.uint8)
+    zeros = rng.integers(0, 16, size=(n, 3), dtype=np.uint8) if zp else None
+    scales = rng.uniform(0.001, 0.02, size=(n, 3)).astype(np.float16)
+    g_idx = _valid_gidx(rng, k) if act else None
+    perm = None if g_idx is None else reference.act_order_perm(g_idx, k)
+    q, a, sums = quant.quantize_groups_sums(x, perm)
+    exact = _fraction_affine(q, a, sums, codes, scales, zeros, g_idx)
+    d, y = reference.w4a8_affine_product(q, a, sums, codes, scales, zeros, g_idx)
+    np.testing.assert_array_equal(d, reference.int4_raw_partials(q, codes, g_idx))
+    for i in range(m):
+        for j in range(n):
+            assert abs(Fraction(float(y[i, j])) - exact[i, j]) <= abs(exact[i, j]) * Fraction(1, 10 ** 12)
+
+    def off(yy):
+        return max(abs(Fraction(float(yy[i, j])) - exact[i, j]) / abs(exact[i, j]) for i in range(m) for j in range(n))
+    qsum = np.zeros_like(sums)
+    grp = np.arange(k) // 128 if g_idx is None else g_idx
+    for g in range(3):
+        qsum[:, g] = a[:, g] * q[:, grp == g].astype(np.float32).sum(1)
+    for bad in (np.zeros_like(sums), -sums, qsum):
+        _, yb = reference.w4a8_affine_product(q, a, bad, codes, scales, zeros, g_idx)
+        assert off(yb) > Fraction(1, 10 ** 9)
+
+
+def test_w4a8_affine_product_equals_dequantised_matmul_when_x_is_exact():
+    """Activations built as x = 2^e * q with a +-127 entry in every group: the quantiser
+    returns q, a = 2^e and the exact sum, so the affine form must equal the (separately
+    pinned) dequantised matmul x @ W^T."""
+    rng = np.random.default_rng(7220)
+    m, k, n = 3, 512, 5
+    wl = synth.int4_zp_actorder("t", 71, m, k, n)
+    perm = reference.act_order_perm(wl.g_idx, k)
+    qn = rng.integers(-127, 128, size=(m, k)).astype(np.float64)
+    e = rng.integers(-10, -3, size=(m, 4))
+    for g in range(4):
+        cols = perm[128 * g:128 * (g + 1)]
+        qn[:, cols[7]] = 127.0
+    scale_col = np.empty((m, k))
+    scale_col[:, perm] = np.repeat(np.exp2(e), 128, axis=1)
+    x = (qn * scale_col).astype(np.float32)
+    q, a, sums = quant.quantize_groups_sums(x, perm)
+    np.testing.assert_array_equal(q, qn.astype(np.int8))
+    np.testing.assert_array_equal(a, np.exp2(e).astype(np.float32))
+    _, y = reference.w4a8_affine_product(q, a, sums, wl.codes, wl.scales, wl.zeros, wl.g_idx)
+    want = reference.product(x, reference.weights_int4(wl.codes, wl.scales, wl.zeros, wl.g_idx))
+    np.testing.assert_allclose(y, want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
