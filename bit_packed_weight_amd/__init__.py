@@ -30,6 +30,8 @@ SRC_PQ2_BLOCKS, SRC_PLANES, SRC_CODES_U8 = 1, 2, 3
 PATH_GEMV, PATH_GEMM = 0, 1
 # probes
 PROBE_READ, PROBE_COPY = 0, 1
+# fixed device scratch of bpw_gemv_packed_scratch (bytes, per GPU)
+SCRATCH_BYTES = 16 << 20
 
 FORMAT_NAMES = {"ternary": TERNARY2, "int4_sym": INT4_SYM, "int4_zp": INT4_ZP}
 _STATUS_NAMES = {EINVAL: "EINVAL", ESHAPE: "ESHAPE", EALIGN: "EALIGN", EGIDX: "EGIDX",
@@ -82,6 +84,9 @@ EXPORTS = {
                                     ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                     ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                     ctypes.c_void_p]),
+    "bpw_gemv_packed_scratch": (ctypes.c_int, [ctypes.POINTER(BpwWeights), ctypes.c_void_p, ctypes.c_int,
+                                               ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                               ctypes.c_void_p]),
     "bpw_probe": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                  ctypes.c_void_p]),
     "bpw_probe_blocks": (ctypes.c_int64, [ctypes.c_size_t]),
@@ -344,7 +349,8 @@ def _workspace(w, m, x_dtype, entry, device, workspace):
     return workspace, workspace.numel()
 
 
-def _product(entry: int, w: PackedWeights, x, x_scale=None, out_dtype=None, out=None, workspace=None):
+def _product(entry: int, w: PackedWeights, x, x_scale=None, out_dtype=None, out=None, workspace=None,
+             scratch=False):
     torch = _torch()
     if x.dim() != 2 or not x.is_contiguous():
         raise ValueError("x must be a contiguous [M, K] tensor")
@@ -368,6 +374,13 @@ def _product(entry: int, w: PackedWeights, x, x_scale=None, out_dtype=None, out=
         out_dtype = out_dtype if out_dtype is not None else (torch.float16 if xd in (I8, I8G) else x.dtype)
         out = torch.empty((m, w.n), dtype=out_dtype, device=x.device)
     _check_tensor("out", out, (m, w.n), (torch.float32, torch.float16, torch.bfloat16), x.device)
+    if scratch:
+        # the library's own fixed scratch: nothing is allocated here or in the library
+        _check_gpu("x", x)
+        st = w.struct()
+        _check(lib().bpw_gemv_packed_scratch(ctypes.byref(st), _ptr(x), xd, _ptr(x_scale), m, _ptr(out),
+                                             dtype_code(out.dtype), _stream(x.device)))
+        return out
     ws, ws_bytes = _workspace(w, m, xd, entry, x.device, workspace)
     _check_gpu("x", x)
     st = w.struct()
@@ -380,6 +393,13 @@ def _product(entry: int, w: PackedWeights, x, x_scale=None, out_dtype=None, out=
 def gemv_packed(w: PackedWeights, x, x_scale=None, out_dtype=None, out=None, workspace=None):
     """y = x @ W^T, decode-shaped (bpw_gemv_packed)."""
     return _product(PATH_GEMV, w, x, x_scale, out_dtype, out, workspace)
+
+
+def gemv_packed_scratch(w: PackedWeights, x, x_scale=None, out_dtype=None, out=None):
+    """y = x @ W^T through bpw_gemv_packed_scratch: the decode product with its workspace in
+    the library's fixed per-GPU scratch (no workspace argument, nothing allocated when
+    ``out`` is given). Calls that overlap on one GPU race."""
+    return _product(PATH_GEMV, w, x, x_scale, out_dtype, out, None, scratch=True)
 
 
 def gemm_packed(w: PackedWeights, x, x_scale=None, out_dtype=None, out=None, workspace=None):

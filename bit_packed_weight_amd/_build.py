@@ -18,7 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbpw.so")
 
-SOURCES = ["api.cpp", "prepare.cpp", "quant.hip", "gemv.hip", "gemm_i8.hip", "gemm_w4.hip", "probe.hip"]
+SOURCES = ["api.cpp", "prepare.cpp", "quant.hip", "gemv.hip", "gemm_i8.hip", "gemm_w4.hip", "probe.hip",
+           "scratch.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-variable", "-Wno-unused-function",
           "-Wno-pass-failed", "-I", os.path.join(ROOT, "include")]

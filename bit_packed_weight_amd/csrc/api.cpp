@@ -12,6 +12,7 @@
 
 #include "../../include/bpw.h"
 #include "launch.h"
+#include "product.h"
 #include "status.h"
 
 namespace bpw {
@@ -51,6 +52,8 @@ int hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
+}  // namespace
+
 int check_weights(const bpw_weights* w) {
   if (!w) return fail(BPW_EINVAL, "weights descriptor is NULL");
   if (w->fmt != BPW_TERNARY2 && !is_int4(w->fmt)) return fail(BPW_EINVAL, "unknown weight format %d", w->fmt);
@@ -74,6 +77,8 @@ int check_weights(const bpw_weights* w) {
   if (w->perm && !aligned(w->perm, 4)) return fail(BPW_EALIGN, "perm must be 4-byte aligned");
   return BPW_OK;
 }
+
+namespace {
 
 int check_product(const bpw_weights* w, const void* x, int x_dtype, const float* x_scale,
                   int64_t m, void* y, int y_dtype) {
@@ -104,6 +109,15 @@ int check_product(const bpw_weights* w, const void* x, int x_dtype, const float*
   return BPW_OK;
 }
 
+}  // namespace
+
+int check_product_args(const bpw_weights* w, const void* x, int x_dtype, const float* x_scale, int64_t m,
+                       void* y, int y_dtype) {
+  return check_product(w, x, x_dtype, x_scale, m, y, y_dtype);
+}
+
+int check_current_device() { return check_device(); }
+
 // Workspace bytes for (weights, M, activation type, entry).
 size_t workspace_need(const bpw_weights* w, int64_t m, int x_dtype, int entry) {
   const size_t mk = static_cast<size_t>(m) * static_cast<size_t>(w->k);
@@ -117,6 +131,8 @@ size_t workspace_need(const bpw_weights* w, int64_t m, int x_dtype, int entry) {
   return w->perm ? round_up(mk * 2) : 0;       // gathered 16-bit activations
 }
 
+namespace {
+
 int check_workspace(const bpw_weights* w, int64_t m, int x_dtype, int entry, void* ws, size_t ws_bytes) {
   const size_t need = workspace_need(w, m, x_dtype, entry);
   if (need == 0) return BPW_OK;
@@ -125,6 +141,8 @@ int check_workspace(const bpw_weights* w, int64_t m, int x_dtype, int entry, voi
   if (ws_bytes < need) return fail(BPW_ESHAPE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
   return BPW_OK;
 }
+
+}  // namespace
 
 int run_product(bool gemv, const bpw_weights* w, const void* x, int x_dtype, const float* x_scale,
                 int64_t m, void* y, int y_dtype, void* ws, size_t ws_bytes, void* stream) {
@@ -170,8 +188,6 @@ int run_product(bool gemv, const bpw_weights* w, const void* x, int x_dtype, con
   if (gemv && gemv_w4_fits(m, w->k)) return hip_status(launch_gemv_w4(*w, xs, x_dtype, m, y, y_dtype, s), "4-bit GEMV launch");
   return hip_status(launch_gemm_w4(*w, xs, x_dtype, m, y, y_dtype, s), "4-bit GEMM launch");
 }
-
-}  // namespace
 
 int fail(int status, const char* fmt, ...) {
   char buf[512];

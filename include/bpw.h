@@ -207,6 +207,23 @@ int bpw_gemv_packed(const bpw_weights* w, const void* x, int x_dtype, const floa
                     void* stream);
 
 /*
+ * bpw_gemv_packed for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same product, kernels and results, with no workspace argument. The
+ * workspace comes from a fixed array of BPW_SCRATCH_BYTES in this library's
+ * device memory, one per GPU, held until the process ends; this call never
+ * allocates or frees. A call whose workspace (bpw_workspace_size with
+ * BPW_PATH_GEMV) exceeds BPW_SCRATCH_BYTES returns BPW_ESHAPE before any
+ * launch. Every call on one GPU shares that GPU's array and it keeps the last
+ * call's contents (no call reads bytes it did not write first): calls that
+ * overlap on one GPU (several streams or threads) race and must be ordered by
+ * the caller.
+ */
+#define BPW_SCRATCH_BYTES (16 << 20)
+int bpw_gemv_packed_scratch(const bpw_weights* w, const void* x, int x_dtype, const float* x_scale,
+                            int64_t m, void* y, int y_dtype, void* stream);
+
+/*
  * y = x @ W^T, prefill-shaped (large M). Same arguments and combinations as
  * bpw_gemv_packed, except I8G (BPW_EUNSUPPORTED), plus 4-bit weights x I8.
  * Numerics: ternary x int8 -> as above (int8 MFMA, exact int32 group
