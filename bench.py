@@ -7,15 +7,19 @@ already resident in HBM. Weight copies totalling >= 1 GiB are read as a ring
 so each call streams its weights from HBM rather than the 256 MB Infinity
 Cache. The K timed steps run as one captured HIP graph between HIP events on
 the launch stream; the graph is timed 7 times (after an untimed replay, and
-each time after half a ring of untimed calls and a spin kernel that hides the
-host's submission) and the median per call is reported, with the spread.
+each time after a spin kernel that hides the host's submission and half a
+ring of untimed calls) next to a one-call graph timed the same way, and the
+median of (T(K) - T(1)) / (K - 1) is reported, with the spread: the
+difference cancels the fixed cost of a graph replay and its events.
 value = logical weight bytes (codes + scales) per call / time per call.
 
 Also reported (same JSON line): the complete decode call (quantiser + GEMV),
 the other decode/prefill workloads (ternary decode at M=16, split-K long K,
 per-group activation scales and on the 62 MB prefill weight; 4-bit decode GEMV
 with act order; bf16 prefill GEMM at M=2048; 4-bit x int8 prefill GEMM at
-M=2048; ternary x int8 prefill GEMM; hipBLASLt dense GEMMs at the prefill
+M=2048, with row scales and in the affine form (scale and exact sum per row
+and weight group); ternary x int8 prefill GEMM with row scales and with
+per-group scales; hipBLASLt dense GEMMs at the prefill
 shapes as a platform reference), HBM read/copy probes, the roofline of the
 dominant kernel (and its fraction of the read probe at the same byte count),
 the engine clock sampled through amdsmi during each prefill leg (for the
@@ -23,6 +27,7 @@ clock-adjusted MFMA fraction), and the CPU oracle timed on bounded samples of
 the headline and the other workloads, with the host's core count and model.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
+                       [--legs LEG,...|all|none] [--repeats R]
 """
 from __future__ import annotations
 
@@ -92,23 +97,33 @@ def rotated_copies(bpw, planes, min_bytes, max_copies=256):
 
 
 REPEATS = 7
-SPIN_CYCLES = 4_000_000     # torch's spin kernel: keeps the GPU busy while the host submits a graph
+SPIN_CYCLES = 1_000_000     # torch's spin kernel (~0.4 ms): the GPU stays busy while the host submits a graph
 LAST_SPREAD = {}
 
 
-def time_calls(torch, call, ncopies, steps, warmup, repeats=REPEATS):
+def time_calls(torch, call, ncopies, steps, warmup, repeats=None):
     """Median ms per call of `steps` calls captured in one HIP graph.
 
     call(c) launches one call that reads weight copy c. The copies form a ring
-    that is read in order; every graph is laid out so that between two reads of
-    one copy at least half the ring is read (>= 512 MB for a >= 1 GiB ring), so
-    the 256 MB Infinity Cache holds none of the timed bytes when a timed graph
-    starts. Sequence: a warm-up graph of `warmup` calls, replayed once; then per
-    repeat a flush graph (half a ring, untimed), torch's spin kernel (the host
-    submits the timed graph while it runs, so submission is not timed), and the
-    timed graph between two events on its stream. Every graph is replayed once
-    before anything is timed, so first-replay costs fall outside the events.
+    read in order, and every timed graph is preceded by a flush graph of half a
+    ring (>= 512 MB for a >= 1 GiB ring) that ends on the copy just before the
+    timed graph's first one, so the 256 MB Infinity Cache holds none of the
+    timed bytes when timing starts. Each timed graph runs after torch's spin
+    kernel, so the host's submission of the graph is not timed, between two
+    events on its stream.
+
+    The spin kernel runs first, then the flush, then the timed graph, so the
+    GPU goes straight from a half ring of the same calls into the timed ones.
+
+    A graph replay bracketed by events costs a fixed ~12 us beyond its calls
+    (graph boundary and event packets, measured: 20 calls per graph read
+    5.42 us per call, 2070 read 4.79). So each repeat times the `steps`-call
+    graph T_K and a one-call graph T_1 the same way, and the figure per call is
+    (T_K - T_1) / (K - 1): the cost of the calls beyond the first, with the
+    boundary cancelled. The median over `repeats` repeats is returned; the
+    spread and the undifferenced T_K / K go to LAST_SPREAD.
     """
+    repeats = REPEATS if repeats is None else repeats
     stream = torch.cuda.Stream()
     half = max(ncopies // 2, 1)
 
@@ -119,31 +134,42 @@ def time_calls(torch, call, ncopies, steps, warmup, repeats=REPEATS):
                 call((first + i) % ncopies)
         return g
 
-    timed_first = 0
-    timed = capture(timed_first, steps)
-    # the flush graph ends on the copy just before the timed graph's first copy
-    flush = capture((timed_first - half) % ncopies, half)
-    warm = capture((timed_first + half) % ncopies, max(warmup, 1))
+    k = max(int(steps), 1)
+    one_first = half                                  # the one-call graph reads the copy half a ring away
+    timed = capture(0, k)
+    one = capture(one_first, 1)
+    flush_k = capture((0 - half) % ncopies, half)     # ends on the copy before timed's first
+    flush_1 = capture((one_first - half) % ncopies, half)
+    warm = capture(half // 2, max(warmup, 1))
     torch.cuda.synchronize()
+    pairs = []
     with torch.cuda.stream(stream):
-        timed.replay()                  # first replay of each graph: untimed
-        flush.replay()
-        warm.replay()
-        events = []
+        for g in (timed, one, flush_k, flush_1, warm):     # first replay of each graph: untimed
+            g.replay()
         for _ in range(repeats):
-            flush.replay()
-            torch.cuda._sleep(SPIN_CYCLES)
-            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            ev0.record(stream)
-            timed.replay()
-            ev1.record(stream)
-            events.append((ev0, ev1))
+            evs = []
+            for flush, g in ((flush_k, timed), (flush_1, one)):
+                torch.cuda._sleep(SPIN_CYCLES)
+                flush.replay()
+                ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                ev0.record(stream)
+                g.replay()
+                ev1.record(stream)
+                evs.append((ev0, ev1))
+            pairs.append(evs)
     torch.cuda.synchronize()
-    per_call = sorted(a.elapsed_time(b) / steps for a, b in events)
-    med = per_call[len(per_call) // 2]
+    tk = [a.elapsed_time(b) for (a, b), _ in pairs]
+    t1 = [a.elapsed_time(b) for _, (a, b) in pairs]
+    if k > 1:
+        per = sorted((x - y) / (k - 1) for x, y in zip(tk, t1))
+    else:
+        per = sorted(t1)
+    med = per[len(per) // 2]
     LAST_SPREAD.clear()
-    LAST_SPREAD.update({"repeats": repeats, "min_us": per_call[0] * 1e3, "max_us": per_call[-1] * 1e3})
-    del timed, flush, warm
+    LAST_SPREAD.update({"repeats": repeats, "min_us": per[0] * 1e3, "max_us": per[-1] * 1e3,
+                        "graph_us_per_call": sorted(tk)[len(tk) // 2] / k * 1e3,
+                        "one_call_graph_us": sorted(t1)[len(t1) // 2] * 1e3})
+    del timed, one, flush_k, flush_1, warm
     return med
 
 
@@ -152,8 +178,9 @@ def spread():
 
 
 class ClockSampler:
-    """Mean engine (gfx) clock while a timed region runs, polled through amdsmi on a
-    host thread (read-only queries; no GPU work). None when amdsmi is unavailable."""
+    """Engine (gfx) clock while a timed region runs, polled through amdsmi on a host
+    thread (read-only queries; no GPU work): the SMU metrics' per-XCD current clocks
+    (mean over XCDs) and the clock-info reading. None when amdsmi is unavailable."""
 
     def __init__(self, period_s=0.002):
         self.period, self.samples, self._stop, self._thread, self._h = period_s, [], None, None, None
@@ -166,8 +193,23 @@ class ClockSampler:
             self._amdsmi = None
 
     def _read(self):
-        info = self._amdsmi.amdsmi_get_clock_info(self._h, self._amdsmi.AmdSmiClkType.GFX)
-        return float(info["clk"])
+        out = {}
+        try:
+            met = self._amdsmi.amdsmi_get_gpu_metrics_info(self._h)
+            clks = [float(c) for c in met.get("current_gfxclks", []) if isinstance(c, (int, float)) and c > 0]
+            if clks:
+                out["xcd"] = sum(clks) / len(clks)
+            avg = met.get("average_gfxclk_frequency")
+            if isinstance(avg, (int, float)) and avg > 0:
+                out["avg"] = float(avg)
+        except Exception:  # noqa: BLE001
+            pass
+        try:
+            info = self._amdsmi.amdsmi_get_clock_info(self._h, self._amdsmi.AmdSmiClkType.GFX)
+            out["info"] = float(info["clk"])
+        except Exception:  # noqa: BLE001
+            pass
+        return out
 
     def __enter__(self):
         import threading  # noqa: PLC0415
@@ -178,10 +220,10 @@ class ClockSampler:
 
         def run():
             while not self._stop.is_set():
-                try:
-                    self.samples.append(self._read())
-                except Exception:  # noqa: BLE001
+                r = self._read()
+                if not r:
                     return
+                self.samples.append(r)
                 self._stop.wait(self.period)
         self._thread = threading.Thread(target=run, daemon=True)
         self._thread.start()
@@ -192,21 +234,23 @@ class ClockSampler:
             self._stop.set()
             self._thread.join()
 
-    def mean_ghz(self):
-        return round(sum(self.samples) / len(self.samples) / 1000.0, 3) if self.samples else None
+    def mean_ghz(self, key):
+        v = [r[key] for r in self.samples if key in r]
+        return round(sum(v) / len(v) / 1000.0, 3) if v else None
 
 
 CLOCK = None
 
 
 def clocked(fn):
-    """Run fn() under the clock sampler; returns (result, mean gfx clock in GHz or None)."""
+    """Run fn() under the clock sampler; returns (result, {source: mean gfx clock in GHz})."""
     global CLOCK
     if CLOCK is None:
         CLOCK = ClockSampler()
     with CLOCK:
         r = fn()
-    return r, CLOCK.mean_ghz()
+    return r, {"smu_xcd_current": CLOCK.mean_ghz("xcd"), "smu_average": CLOCK.mean_ghz("avg"),
+               "clock_info": CLOCK.mean_ghz("info"), "samples": len(CLOCK.samples)}
 
 
 def decode_leg(name, m, k, n, nbytes, ms, ncopies, **extra):
@@ -215,16 +259,17 @@ def decode_leg(name, m, k, n, nbytes, ms, ncopies, **extra):
             "GB_s": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS, "copies": ncopies, "spread": spread(), **extra}
 
 
-def gemm_leg(name, m, k, n, ms, clock_ghz, int8, **extra):
+def gemm_leg(name, m, k, n, ms, clocks, int8, **extra):
     ops = 2.0 * m * n * k
     rate = ops / (ms * 1e9)
     peak = INT8_PEAK_TOPS if int8 else BF16_PEAK_TFLOPS
+    ghz = clocks.get("smu_xcd_current") or clocks.get("smu_average") or clocks.get("clock_info")
     out = {"workload": name, "M": m, "K": k, "N": n, "us_per_call": ms * 1e3,
            ("TOP_s" if int8 else "TFLOP_s"): rate,
            ("frac_int8_mfma_peak" if int8 else "frac_bf16_mfma_peak"): rate / peak,
-           "gfx_clock_ghz": clock_ghz,
-           # the published peak scaled to the engine clock measured during the timed region
-           "frac_clock_adjusted_peak": None if not clock_ghz else rate / (peak * clock_ghz / PEAK_CLOCK_GHZ),
+           "gfx_clock_ghz": clocks,
+           # the published peak scaled to the engine clock sampled during the timed region
+           "frac_clock_adjusted_peak": None if not ghz else rate / (peak * ghz / PEAK_CLOCK_GHZ),
            "spread": spread(), **extra}
     return out
 
@@ -371,6 +416,44 @@ def bench_w4a8_prefill(bpw, synth, torch, np, steps, warmup):
     return gemm_leg("w4a8_prefill_gemm", w.m, w.k, w.n, ms, ghz, True, activations="int8 + fp32 row scale")
 
 
+def bench_w4a8_affine_prefill(bpw, synth, torch, np, steps, warmup):
+    """The 4-bit prefill weights against int8 activations in the affine form of the int8
+    prompt GEMM (per row and weight group: scale a and the exact sum of x): the GEMM
+    alone, and the complete call with the group quantiser in front of it."""
+    w = synth.w4a16_prefill()
+    planes = bpw.prepare_packed_host(bpw.INT4_SYM, w.codes, w.scales, scale_dtype=bpw.BF16)
+    copies = rotated_copies(bpw, planes, 512 << 20, max_copies=18)
+    x = to_dev(w.x, "bf16", torch, np)
+    q, xss = bpw.quantize_groups_sums(x)
+    y = torch.empty((w.m, w.n), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(bpw.workspace_size(copies[0], w.m, bpw.I8GS, bpw.PATH_GEMM), dtype=torch.uint8, device="cuda")
+    nc = len(copies)
+    ms, ghz = clocked(lambda: time_calls(torch, lambda c: bpw.gemm_packed(copies[c], q, xss, out=y, workspace=ws),
+                                         nc, steps, warmup))
+    leg = gemm_leg("w4a8_affine_prefill_gemm", w.m, w.k, w.n, ms, ghz, True,
+                   activations="int8 + (scale, exact sum) per row and group")
+    ms_full = time_calls(torch, lambda c: (bpw.quantize_groups_sums(x, None, q, xss),
+                                           bpw.gemm_packed(copies[c], q, xss, out=y, workspace=ws)),
+                         nc, max(steps // 2, 2), max(warmup // 2, 1))
+    leg["complete_call_us"] = ms_full * 1e3
+    return leg
+
+
+def bench_ternary_groups_prefill(bpw, synth, torch, np, steps, warmup):
+    """The ternary prefill workload with one activation scale per (row, 128-group)."""
+    w = synth.ternary_prefill()
+    planes = bpw.prepare_packed_host(bpw.TERNARY2, w.codes, w.scales)
+    w.codes = None
+    copies = rotated_copies(bpw, planes, 512 << 20, max_copies=9)
+    q, xs = bpw.quantize_groups(to_dev(w.x, "f32", torch, np))
+    y = torch.empty((w.m, w.n), dtype=torch.float16, device="cuda")
+    ws = torch.empty(bpw.workspace_size(copies[0], w.m, bpw.I8G, bpw.PATH_GEMM), dtype=torch.uint8, device="cuda")
+    ms, ghz = clocked(lambda: time_calls(torch, lambda c: bpw.gemm_packed(copies[c], q, xs, out=y, workspace=ws),
+                                         len(copies), steps, warmup))
+    return gemm_leg("ternary_int8_group_scales_prefill_gemm", w.m, w.k, w.n, ms, ghz, True,
+                    activations="int8 + fp32 scale per row and 128-group")
+
+
 def bench_dense_reference(torch, steps=20, warmup=5):
     """The platform's dense GEMMs (hipBLASLt through torch) at the two prefill shapes, with
     no quantisation: context for the MFMA fractions, not part of the library. Event-timed
@@ -486,6 +569,23 @@ def cpu_baselines(synth, np, budget_s=12.0):
     return head
 
 
+# Extra legs: name -> (function, steps, warm-up calls, keyword arguments).
+LEGS = {
+    "t2_m16": (bench_ternary_decode_m, 900, 300, {"m": 16}),
+    "t2_long_k": (bench_ternary_long_k, 600, 200, {"m": 16}),
+    "t2_large": (bench_ternary_decode_large, 600, 200, {}),
+    "t2_groups_m1": (bench_ternary_decode_groups, 900, 300, {"m": 1}),
+    "t2_groups_m16": (bench_ternary_decode_groups, 900, 300, {"m": 16}),
+    "w4_m1": (bench_w4_decode, 900, 300, {"m": 1}),
+    "w4_m8": (bench_w4_decode, 900, 300, {"m": 8}),
+    "bf16_prefill": (bench_w4_prefill, 30, 6, {}),
+    "w4a8_prefill": (bench_w4a8_prefill, 30, 6, {}),
+    "t2_prefill": (bench_ternary_prefill, 12, 3, {}),
+    "w4a8_affine_prefill": (bench_w4a8_affine_prefill, 30, 6, {}),
+    "t2_groups_prefill": (bench_ternary_groups_prefill, 12, 3, {}),
+}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -493,7 +593,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=690)
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--legs", default="all",
+                    help="comma-separated extra legs to run (default all; 'none' = headline and probes): "
+                         + ",".join(LEGS))
+    ap.add_argument("--repeats", type=int, default=7, help="timed repeats per leg (median reported)")
     args = ap.parse_args()
+    global REPEATS
+    REPEATS = max(1, args.repeats)
+    legs = list(LEGS) if args.legs == "all" else [] if args.legs == "none" else args.legs.split(",")
+    unknown = [x for x in legs if x not in LEGS and x != "dense_ref"]
+    if unknown:
+        ap.error(f"unknown legs {unknown}")
     if args.gpus != 1:
         print("bench.py: the benchmark runs on one GPU only; --gpus must be 1 "
               "(the multi-GPU sharding of the path is described, not implemented)", file=sys.stderr)
@@ -522,20 +632,21 @@ def main():
             read_probe = probe["GB_s"]
         torch.cuda.empty_cache()
     if not args.no_extra:
-        runs = ((bench_ternary_decode_m, 900, 300, {"m": 16}), (bench_ternary_long_k, 600, 200, {"m": 16}),
-                (bench_ternary_decode_large, 600, 200, {}), (bench_ternary_decode_groups, 900, 300, {"m": 1}),
-                (bench_ternary_decode_groups, 900, 300, {"m": 16}), (bench_w4_decode, 900, 300, {"m": 1}),
-                (bench_w4_decode, 900, 300, {"m": 8}), (bench_w4_prefill, 30, 6, {}), (bench_w4a8_prefill, 30, 6, {}),
-                (bench_ternary_prefill, 12, 3, {}))
-        for fn, steps, warm, kw in runs:
+        for name in legs:
+            if name == "dense_ref":
+                continue
+            fn, steps, warm, kw = LEGS[name]
+            if args.steps < 200:            # short runs (counter passes): fewer calls per leg
+                steps, warm = max(2, min(steps, args.steps)), max(1, min(warm, args.warmup))
             r = fn(bpw, synth, torch, np, steps, warm, **kw)
-            log(f"[bench] {json.dumps(r)}")
+            log(f"[bench] {name}: {json.dumps(r)}")
             extra.append(r)
             torch.cuda.empty_cache()
-        for r in bench_dense_reference(torch):
-            log(f"[bench] {json.dumps(r)}")
-            extra.append(r)
-        torch.cuda.empty_cache()
+        if args.legs == "all" or "dense_ref" in legs:
+            for r in bench_dense_reference(torch):
+                log(f"[bench] {json.dumps(r)}")
+                extra.append(r)
+            torch.cuda.empty_cache()
     cpu = None if args.no_cpu else cpu_baselines(synth, np)
     if cpu:
         log(f"[bench] cpu oracle: {cpu['value']:.3f} GB/s on {cpu['cores']} threads "
@@ -551,7 +662,9 @@ def main():
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic()},
         "frac_of_read_probe": round(gbs / read_probe, 4) if read_probe else None,
         "timing": {"median_of_repeats": sp["repeats"], "per_call_min_us": sp["min_us"],
-                   "per_call_max_us": sp["max_us"]},
+                   "per_call_max_us": sp["max_us"], "graph_us_per_call": sp["graph_us_per_call"],
+                   "one_call_graph_us": sp["one_call_graph_us"],
+                   "method": "(T(K calls) - T(1 call)) / (K - 1), each graph after a spin and a half-ring flush"},
         "complete_call_us": round(ms_full * 1e3, 3),
         "cpu_baseline": cpu,
         "other_workloads": extra,

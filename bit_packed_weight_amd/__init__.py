@@ -22,12 +22,14 @@ LIB_PATH = os.path.join(_HERE, "libbpw.so")
 OK, EINVAL, ESHAPE, EALIGN, EGIDX, EUNSUPPORTED, EHIP = range(7)
 # weight formats
 TERNARY2, INT4_SYM, INT4_ZP = 1, 2, 3
-# element types (I8G: int8 activations with one scale per (row, 128-group))
-F32, F16, BF16, I8, I32, I8G = 0, 1, 2, 3, 4, 5
+# element types (I8G: int8 activations with one scale per (row, 128-group);
+# I8GS: int8 with (scale, exact sum) per (row, weight group))
+F32, F16, BF16, I8, I32, I8G, I8GS = 0, 1, 2, 3, 4, 5, 6
 # prepare sources
 SRC_PQ2_BLOCKS, SRC_PLANES, SRC_CODES_U8 = 1, 2, 3
-# partial-sum cores / workspace entries
-PATH_GEMV, PATH_GEMM = 0, 1
+# partial-sum cores / workspace entries (PATH_GEMM_RAW: partials only, the core of
+# the per-(row, group) GEMM: ternary code - 1, 4-bit raw codes)
+PATH_GEMV, PATH_GEMM, PATH_GEMM_RAW = 0, 1, 2
 # probes
 PROBE_READ, PROBE_COPY = 0, 1
 # fixed device scratch of bpw_gemv_packed_scratch (bytes, per GPU)
@@ -72,6 +74,8 @@ EXPORTS = {
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "bpw_quantize_groups": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "bpw_quantize_groups_sums": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "bpw_workspace_size": (ctypes.c_int, [ctypes.POINTER(BpwWeights), ctypes.c_int64, ctypes.c_int,
                                           ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]),
     "bpw_gemv_packed": (ctypes.c_int, [ctypes.POINTER(BpwWeights), ctypes.c_void_p, ctypes.c_int,
@@ -327,6 +331,30 @@ def quantize_groups(x, q=None, x_scale=None):
     return q, x_scale
 
 
+def quantize_groups_sums(x, perm=None, q=None, x_scale_sum=None):
+    """Group quantiser with exact group sums (bpw_quantize_groups_sums): returns
+    (q [M,K] int8, x_scale_sum [M,K/128,2] fp32 of (a, sum) pairs). ``perm`` is the
+    prepared weight's act-order permutation (int32 [K] on the device) or None."""
+    torch = _torch()
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [M, K] tensor")
+    m, k = x.shape
+    if k % 128:
+        raise ValueError(f"K={k} must be a multiple of 128 for per-group scales")
+    _check_tensor("x", x, (m, k), (torch.float32, torch.float16, torch.bfloat16))
+    if perm is not None:
+        _check_tensor("perm", perm, (k,), (torch.int32,), x.device)
+    q = torch.empty((m, k), dtype=torch.int8, device=x.device) if q is None else q
+    if x_scale_sum is None:
+        x_scale_sum = torch.empty((m, k // 128, 2), dtype=torch.float32, device=x.device)
+    _check_tensor("q", q, (m, k), (torch.int8,), x.device)
+    _check_tensor("x_scale_sum", x_scale_sum, (m, k // 128, 2), (torch.float32,), x.device)
+    _check_gpu("x", x)
+    _check(lib().bpw_quantize_groups_sums(_ptr(x), dtype_code(x.dtype), m, k, _ptr(perm), _ptr(q),
+                                          _ptr(x_scale_sum), _stream(x.device)))
+    return q, x_scale_sum
+
+
 def workspace_size(w: PackedWeights, m: int, x_dtype: int, entry: int) -> int:
     out = ctypes.c_size_t()
     st = w.struct()
@@ -360,6 +388,8 @@ def _product(entry: int, w: PackedWeights, x, x_scale=None, out_dtype=None, out=
         raise ValueError(f"activations of dtype {x.dtype} are not supported (fp16, bf16 or int8)")
     if xd == I8 and x_scale is not None and x_scale.dim() == 2:
         xd = I8G                                   # one scale per (row, 128-group)
+    elif xd == I8 and x_scale is not None and x_scale.dim() == 3:
+        xd = I8GS                                  # (scale, exact sum) per (row, weight group)
     _check_tensor("x", x, (m, w.k), (x.dtype,))
     w.validate(x.device)
     if xd == I8:
@@ -368,10 +398,12 @@ def _product(entry: int, w: PackedWeights, x, x_scale=None, out_dtype=None, out=
         _check_tensor("x_scale", x_scale, (m,), (torch.float32,), x.device)
     elif xd == I8G:
         _check_tensor("x_scale", x_scale, (m, w.k // 128), (torch.float32,), x.device)
+    elif xd == I8GS:
+        _check_tensor("x_scale", x_scale, (m, w.k // 128, 2), (torch.float32,), x.device)
     elif x_scale is not None:
         raise ValueError("x_scale must be None for fp16/bf16 activations")
     if out is None:
-        out_dtype = out_dtype if out_dtype is not None else (torch.float16 if xd in (I8, I8G) else x.dtype)
+        out_dtype = out_dtype if out_dtype is not None else (torch.float16 if xd in (I8, I8G, I8GS) else x.dtype)
         out = torch.empty((m, w.n), dtype=out_dtype, device=x.device)
     _check_tensor("out", out, (m, w.n), (torch.float32, torch.float16, torch.bfloat16), x.device)
     if scratch:
@@ -421,7 +453,7 @@ def partials(w: PackedWeights, q, path: int, m0: int, m1: int, n0: int, n1: int,
     g = w.k // 128
     out = torch.empty((m1 - m0, n1 - n0, g), dtype=torch.int32, device=q.device)
     ws, ws_bytes = (None, 0)
-    if path == PATH_GEMM:
+    if path in (PATH_GEMM, PATH_GEMM_RAW):
         ws, ws_bytes = _workspace(w, m, I8, PATH_GEMM, q.device, workspace)
     st = w.struct()
     _check(lib().bpw_partials(ctypes.byref(st), _ptr(q), m, path, m0, m1, n0, n1, _ptr(out),

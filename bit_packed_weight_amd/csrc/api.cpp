@@ -96,6 +96,10 @@ int check_product(const bpw_weights* w, const void* x, int x_dtype, const float*
     // "TensorFold PR #1176": 4-bit weights against int8 activations on the int8 matrix core.
     if (!x_scale) return fail(BPW_EINVAL, "int8 activations need x_scale [M]");
     if (!aligned(x_scale, 4)) return fail(BPW_EALIGN, "x_scale must be 4-byte aligned");
+  } else if (x_dtype == BPW_I8GS) {
+    // The same page's affine form: (a, sum) per row and weight group.
+    if (!x_scale) return fail(BPW_EINVAL, "BPW_I8GS activations need x_scale [M][K/128][2]");
+    if (!aligned(x_scale, 8)) return fail(BPW_EALIGN, "x_scale of BPW_I8GS must be 8-byte aligned");
   } else {
     if (x_dtype != BPW_F16 && x_dtype != BPW_BF16)
       return fail(BPW_EUNSUPPORTED, "4-bit weights take fp16, bf16 or int8 (row scale) activations (x_dtype %d given)",
@@ -122,12 +126,13 @@ int check_current_device() { return check_device(); }
 size_t workspace_need(const bpw_weights* w, int64_t m, int x_dtype, int entry) {
   const size_t mk = static_cast<size_t>(m) * static_cast<size_t>(w->k);
   if (w->fmt == BPW_TERNARY2) {
-    if (x_dtype == BPW_I8G) return 0;                // decode kernels only, no staging
-    if (entry == BPW_PATH_GEMV && gemv_t2_fits(m, w->k))   // fp32 split-K slices for long K
+    if (x_dtype == BPW_I8G && entry == BPW_PATH_GEMV && gemv_t2_group_fits(m, w->k))
+      return 0;                                // decode kernels, no staging
+    if (x_dtype != BPW_I8G && entry == BPW_PATH_GEMV && gemv_t2_fits(m, w->k))   // fp32 split-K slices for long K
       return round_up(gemv_t2_split_bytes(m, w->n, w->k, false));
     return round_up(mk);                       // plane-ordered int8 activations
   }
-  if (x_dtype == BPW_I8) return round_up(mk);  // nibble-ordered int8 activations
+  if (x_dtype == BPW_I8 || x_dtype == BPW_I8GS) return round_up(mk);  // nibble-ordered int8 activations
   return w->perm ? round_up(mk * 2) : 0;       // gathered 16-bit activations
 }
 
@@ -148,30 +153,31 @@ int run_product(bool gemv, const bpw_weights* w, const void* x, int x_dtype, con
                 int64_t m, void* y, int y_dtype, void* ws, size_t ws_bytes, void* stream) {
   const int entry = gemv ? BPW_PATH_GEMV : BPW_PATH_GEMM;
   if (int st = check_product(w, x, x_dtype, x_scale, m, y, y_dtype)) return st;
-  if (x_dtype == BPW_I8G) {
-    // "Kernel experiments", Test 6: one activation scale per 128-group, folded
-    // with the weight scale of the same group. Decode kernels only.
-    if (!gemv)
-      return fail(BPW_EUNSUPPORTED, "per-group activation scales (BPW_I8G) are supported by bpw_gemv_packed only");
-    if (!gemv_t2_group_fits(m, w->k))
-      return fail(BPW_EUNSUPPORTED, "per-group activation scales need M <= 32 (M=%lld)", (long long)m);
-  }
-  if (is_int4(w->fmt) && x_dtype == BPW_I8 && gemv)
+  if (is_int4(w->fmt) && (x_dtype == BPW_I8 || x_dtype == BPW_I8GS) && gemv)
     return fail(BPW_EUNSUPPORTED, "4-bit weights with int8 activations run through bpw_gemm_packed only");
   if (int st = check_workspace(w, m, x_dtype, entry, ws, ws_bytes)) return st;
   if (int st = check_device()) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (is_int4(w->fmt) && x_dtype == BPW_I8) {
+  if (is_int4(w->fmt) && (x_dtype == BPW_I8 || x_dtype == BPW_I8GS)) {
     int8_t* qn = static_cast<int8_t*>(ws);
     if (int st = hip_status(launch_int8_nibbles(static_cast<const int8_t*>(x), w->perm, m, w->k, qn, s),
                             "int8 nibble reorder launch"))
       return st;
+    if (x_dtype == BPW_I8GS)   // "TensorFold PR #1176": s * a * (code . q) + b * sum(x) per group
+      return hip_status(launch_gemm_g(*w, qn, x_scale, m, y, y_dtype, s), "4-bit x int8 affine GEMM launch");
     return hip_status(launch_gemm_w4a8(*w, qn, x_scale, m, y, y_dtype, s), "4-bit x int8 GEMM launch");
   }
   if (w->fmt == BPW_TERNARY2) {
     const int8_t* q = static_cast<const int8_t*>(x);
-    if (x_dtype == BPW_I8G)
+    if (x_dtype == BPW_I8G && gemv && gemv_t2_group_fits(m, w->k))
       return hip_status(launch_gemv_t2(*w, q, x_scale, m, y, y_dtype, true, nullptr, 0, s), "ternary GEMV launch");
+    if (x_dtype == BPW_I8G) {
+      // "Kernel experiments", Test 7: partial * x_scale * w_scale per 128-group, on the
+      // prefill kernel with one activation scale per (row, group).
+      int8_t* qp = static_cast<int8_t*>(ws);
+      if (int st = hip_status(launch_int8_planes(q, m, w->k, qp, s), "int8 plane reorder launch")) return st;
+      return hip_status(launch_gemm_g(*w, qp, x_scale, m, y, y_dtype, s), "ternary GEMM launch");
+    }
     if (gemv && gemv_t2_fits(m, w->k))
       return hip_status(launch_gemv_t2(*w, q, x_scale, m, y, y_dtype, false, ws, ws_bytes, s), "ternary GEMV launch");
     int8_t* qp = static_cast<int8_t*>(ws);
@@ -241,6 +247,23 @@ extern "C" int bpw_quantize_groups(const void* x, int x_dtype, int64_t m, int64_
                     "group quantiser launch");
 }
 
+extern "C" int bpw_quantize_groups_sums(const void* x, int x_dtype, int64_t m, int64_t k, const int32_t* perm,
+                                        int8_t* q, float* x_scale_sum, void* stream) {
+  if (!x || !q || !x_scale_sum) return fail(BPW_EINVAL, "x / q / x_scale_sum is NULL");
+  if (x_dtype != BPW_F32 && x_dtype != BPW_F16 && x_dtype != BPW_BF16)
+    return fail(BPW_EUNSUPPORTED, "quantiser input dtype %d unsupported (F32, F16, BF16)", x_dtype);
+  if (m < 1 || m > (int64_t(1) << 30) || k < 128 || k > (int64_t(1) << 30) || k % 128 != 0)
+    return fail(BPW_ESHAPE, "M=%lld must be in 1..2^30 and K=%lld a multiple of 128 up to 2^30", (long long)m,
+                (long long)k);
+  if (!aligned(x, x_dtype == BPW_F32 ? 4 : 2) || !aligned(q, 16) || !aligned(x_scale_sum, 8) ||
+      (perm && !aligned(perm, 4)))
+    return fail(BPW_EALIGN, "x / q / x_scale_sum / perm misaligned (q 16-byte, x_scale_sum 8-byte)");
+  if (int st = check_device()) return st;
+  return hip_status(launch_quantize_groups_sums(x, x_dtype, perm, m, k, q, x_scale_sum,
+                                                static_cast<hipStream_t>(stream)),
+                    "group quantiser (with sums) launch");
+}
+
 extern "C" int bpw_workspace_size(const bpw_weights* w, int64_t m, int x_dtype, int entry,
                                   size_t* bytes) {
   if (int st = check_weights(w)) return st;
@@ -274,12 +297,13 @@ extern "C" int bpw_partials(const bpw_weights* w, const int8_t* q, int64_t m, in
   if (!(0 <= m0 && m0 < m1 && m1 <= m) || !(0 <= n0 && n0 < n1 && n1 <= w->n))
     return fail(BPW_ESHAPE, "window [%lld,%lld) x [%lld,%lld) outside M=%lld, N=%lld", (long long)m0,
                 (long long)m1, (long long)n0, (long long)n1, (long long)m, (long long)w->n);
-  if (path != BPW_PATH_GEMV && path != BPW_PATH_GEMM) return fail(BPW_EINVAL, "unknown path %d", path);
-  if (w->fmt != BPW_TERNARY2 && path != BPW_PATH_GEMM)
-    return fail(BPW_EUNSUPPORTED, "partials of 4-bit weights come from the GEMM core only");
+  if (path != BPW_PATH_GEMV && path != BPW_PATH_GEMM && path != BPW_PATH_GEMM_RAW)
+    return fail(BPW_EINVAL, "unknown path %d", path);
+  if (w->fmt != BPW_TERNARY2 && path == BPW_PATH_GEMV)
+    return fail(BPW_EUNSUPPORTED, "partials of 4-bit weights come from the GEMM cores only");
   if (path == BPW_PATH_GEMV && !gemv_t2_fits(m, w->k))
     return fail(BPW_ESHAPE, "the GEMV core takes M <= 32");
-  if (path == BPW_PATH_GEMM) {
+  if (path != BPW_PATH_GEMV) {
     if (int st = check_workspace(w, m, BPW_I8, BPW_PATH_GEMM, workspace, workspace_bytes)) return st;
   }
   if (int st = check_device()) return st;
@@ -289,9 +313,13 @@ extern "C" int bpw_partials(const bpw_weights* w, const int8_t* q, int64_t m, in
   int8_t* qp = static_cast<int8_t*>(workspace);
   if (w->fmt != BPW_TERNARY2) {
     if (int st = hip_status(launch_int8_nibbles(q, w->perm, m, w->k, qp, s), "int8 nibble reorder launch")) return st;
+    if (path == BPW_PATH_GEMM_RAW)
+      return hip_status(launch_gemm_g_partials(*w, qp, m, m0, m1, n0, n1, out, s), "GEMM partials launch");
     return hip_status(launch_gemm_w4a8_partials(*w, qp, m, m0, m1, n0, n1, out, s), "GEMM partials launch");
   }
   if (int st = hip_status(launch_int8_planes(q, m, w->k, qp, s), "int8 plane reorder launch")) return st;
+  if (path == BPW_PATH_GEMM_RAW)
+    return hip_status(launch_gemm_g_partials(*w, qp, m, m0, m1, n0, n1, out, s), "GEMM partials launch");
   return hip_status(launch_gemm_t2_partials(*w, qp, m, m0, m1, n0, n1, out, s), "GEMM partials launch");
 }
 

@@ -113,16 +113,6 @@ __device__ __forceinline__ int xcd_swizzle(int bid, int nblocks) {
   return base + local;
 }
 
-// Direct global -> LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4):
-// lane i's 16 bytes land at LDS byte address lds_base + 16 * i (lds_base must be
-// wave-uniform). Issued from inline assembly so that the compiler does not add
-// its own conservative waits on later LDS reads; the caller waits (vmcnt) and
-// synchronises before the data is read.
-__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(src)
-               : "memory", "m0");
-}
-
 // Allow a kernel to launch with more than 64 KB of dynamic LDS (gfx950 has 160 KB
 // per CU). Called on the host before such a launch; cheap after the first call.
 template <typename K>

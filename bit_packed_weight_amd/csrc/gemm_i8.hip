@@ -31,6 +31,7 @@
 // come in nibble order: within each 8 bytes of a row, the even-indexed
 // elements, then the odd ones, in the chunk arrangement of the plane order.
 #include "device.h"
+#include "lds_dma.h"
 #include "launch.h"
 #include "store.h"
 
@@ -379,6 +380,433 @@ __global__ __launch_bounds__(NT, 1) void gemm_t2_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Per-(token, group) activation scales on the int8 matrix core:
+//  * the affine 4-bit x int8 product of "TensorFold PR #1176" ("What changes":
+//    per group s * a * (code . q) + b * sum(x), the dot on the raw codes 0..15,
+//    with b = -zero * s here), FX_AFF_SYM (zero 8) and FX_AFF_ZP;
+//  * ternary weights x int8 with one activation scale per (row, 128-group),
+//    FX_T2G ("Kernel experiments", Test 7: acc += partial * x_scale * w_scale).
+//
+// Same tile as gemm_t2_kernel (128 tokens x 256 weight rows, 4 waves; wave w
+// owns weight rows [64w, 64w + 64) and all 128 tokens), but every MFMA takes
+// the weights as its first operand, so lane l of a 32 x 32 result holds token
+// 32 i + (l & 31) and 16 weight rows: the token's activation scale and sum are
+// one value per lane. The weight scales of each group are staged in LDS as
+// fp32 by the workgroup (one row per thread) and read 16 at a time, for one
+// 32-row weight tile, just before that tile's chains. Chains run weight tile
+// by weight tile, (0,0) (1,0) (2,0) (3,0) then (0,1) .. (3,1), over A operands
+// of the four token tiles kept in AGPRs (read one tile ahead during the first
+// weight tile's chains), so only one tile's scales and B operands are live.
+//
+// Affine fold: the int32 dot D (|D| <= 127 * 15 * 128 < 2^24) converts to fp32
+// exactly; t = fma(D, a, -8 * sum) for symmetric codes (b = -8 s, so s * t is
+// the group's term), t = D * a with zero points; then acc += s * t, and with
+// zero points acc += b * sum. (The page saves the conversion by starting each
+// chain at the bit pattern of 12582912.0f and removing it in the same fma that
+// applies a; the rounding of that fma's constant costs up to one unit of D per
+// group, an absolute error that broke the 1e-3 parity bound on outputs near
+// zero, so the exact form is used.)
+// Ternary: acc += s * (float(P) * xs).
+enum { FX_T2G = 0, FX_AFF_SYM = 1, FX_AFF_ZP = 2 };
+constexpr int LDS_G_SCALE = LDS_BYTES;               // [2][256] fp32 weight scales of a group
+constexpr int LDS_G_BIAS = LDS_BYTES + 2048;         // [2][256] fp32 b = -zero * scale (zero points)
+constexpr int STAGE_ROW = 68;                        // epilogue stage row (floats): 16-byte aligned, fewer conflicts
+constexpr int LDS_G_BYTES = LDS_BYTES + 4096 > 4 * 32 * STAGE_ROW * 4 ? LDS_BYTES + 4096 : 4 * 32 * STAGE_ROW * 4;
+
+// 16-byte LDS read into VGPRs, untracked like ds_read_agpr: ds_wait_v4 must run
+// before the registers are used.
+template <int OFF>
+__device__ __forceinline__ void ds_read_v(v4f& dst, uint32_t addr) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(dst) : "v"(addr), "i"(OFF));
+}
+__device__ __forceinline__ void ds_wait_v4(v4f (&a)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]));
+}
+
+template <typename TOut, bool PARTIALS, int FX>
+__global__ __launch_bounds__(NT, 1) void gemm_g_kernel(
+    const int8_t* __restrict__ qp, const float* __restrict__ xsc,
+    const uint8_t* __restrict__ codes, const uint16_t* __restrict__ wscale,
+    const uint8_t* __restrict__ zeros, int bf_scale, int M, int N, int K,
+    TOut* __restrict__ y, int32_t* __restrict__ pout, int pm0, int pm1, int pn0, int pn1,
+    int mt0, int mtiles, int nt0, int ntiles) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  constexpr bool W4 = FX != FX_T2G;
+  constexpr bool ZP = FX == FX_AFF_ZP;
+  const int G = K >> 7;
+  const int KB = W4 ? (K >> 1) : (K >> 2);
+  const int ZB = (G + 1) >> 1;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int mt, nt;
+  tile_coords(xcd_swizzle(blockIdx.x, mtiles * ntiles), mtiles, ntiles, mt, nt);
+  mt += mt0;
+  nt += nt0;
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int n = lane & 31, h = lane >> 5;
+  const uint32_t sbase = static_cast<uint32_t>(reinterpret_cast<size_t>(smem));
+
+  // A (activations, plane or nibble order): the same direct loads, swizzle and
+  // AGPR reads as gemm_t2_kernel.
+  const int a_row0 = 32 * wave + (lane >> 3);
+  const int8_t* a_base[2] = {qp + 16 * ((lane & 7) ^ ((lane >> 4) & 7)),
+                             qp + 16 * ((lane & 7) ^ ((4 + (lane >> 4)) & 7))};
+  int a_row[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) a_row[t] = min(m0 + a_row0 + 8 * t, M - 1);
+  const uint32_t lds0 = sbase + wave * 4096;
+  auto a_load = [&](int g, int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int8_t* src = a_base[t & 1] + static_cast<size_t>(a_row[t]) * K + g * 128;
+      lds_dma16(src, __builtin_amdgcn_readfirstlane(lds0 + buf * A_BYTES + t * 1024));
+    }
+  };
+  uint32_t a_addr[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) a_addr[t] = sbase + n * A_ROW + 16 * ((2 * t + h) ^ ((n >> 1) & 7));
+  auto a_read = [&](auto BUFC, auto IC, v4i (&dst)[4]) __attribute__((always_inline)) {
+    constexpr int OFF = decltype(BUFC)::value * A_BYTES + decltype(IC)::value * 32 * A_ROW;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) ds_read_agpr<OFF>(dst[t], a_addr[t]);
+  };
+
+  // B (weights): lane row 32 j + n of the wave's 64, as in gemm_t2_kernel.
+  const uint8_t* b_src[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const size_t row = static_cast<size_t>(min(n0 + 64 * wave + 32 * j + n, N - 1));
+    b_src[j] = codes + row * KB + (W4 ? 32 : 16) * h;
+  }
+  struct Raw {
+    v4u c[2][W4 ? 2 : 1];
+  };
+  auto raw_load = [&](Raw& r, int g) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (W4) {
+        r.c[j][0] = *reinterpret_cast<const v4u*>(b_src[j] + g * 64);
+        r.c[j][W4 ? 1 : 0] = *reinterpret_cast<const v4u*>(b_src[j] + g * 64 + 16);
+      } else {
+        r.c[j][0] = *reinterpret_cast<const v4u*>(b_src[j] + g * 32);
+      }
+    }
+  };
+  // Raw 4-bit codes (0..15) as MFMA bytes in nibble order (low nibbles of a
+  // dword, then its high nibbles), or ternary codes as signed -1/0/1/2 bytes.
+  auto decode = [&](const Raw& r, int j, v4i (&b)[4]) __attribute__((always_inline)) {
+    if (W4) {
+      const uint32_t d[8] = {r.c[j][0].x, r.c[j][0].y, r.c[j][0].z, r.c[j][0].w,
+                             r.c[j][W4 ? 1 : 0].x, r.c[j][W4 ? 1 : 0].y, r.c[j][W4 ? 1 : 0].z, r.c[j][W4 ? 1 : 0].w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        b[t] = v4i{static_cast<int>(d[2 * t] & 0x0F0F0F0Fu), static_cast<int>((d[2 * t] >> 4) & 0x0F0F0F0Fu),
+                   static_cast<int>(d[2 * t + 1] & 0x0F0F0F0Fu), static_cast<int>((d[2 * t + 1] >> 4) & 0x0F0F0F0Fu)};
+    } else {
+      const v4u& c = r.c[j][0];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        b[t] = v4i{static_cast<int>(code_plane_signed(c.x, t)), static_cast<int>(code_plane_signed(c.y, t)),
+                   static_cast<int>(code_plane_signed(c.z, t)), static_cast<int>(code_plane_signed(c.w, t))};
+    }
+  };
+
+  // Weight scale (and zero point) of row n0 + tid, staged per group: raw bits
+  // loaded a group ahead, converted and written to LDS at the group's end.
+  const size_t srow = static_cast<size_t>(min(n0 + tid, N - 1));
+  const uint16_t* s_row = wscale + srow * G;
+  const uint8_t* z_row = ZP ? zeros + srow * ZB : nullptr;
+  auto stage_scale = [&](uint16_t sbits, uint32_t zbyte, int g, int buf) __attribute__((always_inline)) {
+    const float sv = (W4 && bf_scale) ? bf16_to_f32(sbits) : __half2float(__builtin_bit_cast(__half, sbits));
+    float* sl = reinterpret_cast<float*>(smem + LDS_G_SCALE + buf * 1024);
+    sl[tid] = sv;
+    if (ZP) {
+      const float z = static_cast<float>((zbyte >> (4 * (g & 1))) & 15u);
+      reinterpret_cast<float*>(smem + LDS_G_BIAS + buf * 1024)[tid] = -z * sv;   // exact
+    }
+  };
+  // This lane's weight rows of tile j: 64 wave + 32 j + 8 q + 4 h + p for element
+  // 4 q + p of the chain result.
+  const uint32_t s_addr = sbase + LDS_G_SCALE + (64 * wave + 4 * h) * 4;
+  auto s_read = [&](auto BUFC, auto JC, v4f (&sv)[4], v4f (&bv)[4]) __attribute__((always_inline)) {
+    constexpr int OFF = decltype(BUFC)::value * 1024 + decltype(JC)::value * 128;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (q == 0) ds_read_v<OFF>(sv[0], s_addr);
+      if (q == 1) ds_read_v<OFF + 32>(sv[1], s_addr);
+      if (q == 2) ds_read_v<OFF + 64>(sv[2], s_addr);
+      if (q == 3) ds_read_v<OFF + 96>(sv[3], s_addr);
+    }
+    if (ZP) {
+      ds_read_v<OFF + 2048>(bv[0], s_addr);
+      ds_read_v<OFF + 2048 + 32>(bv[1], s_addr);
+      ds_read_v<OFF + 2048 + 64>(bv[2], s_addr);
+      ds_read_v<OFF + 2048 + 96>(bv[3], s_addr);
+    }
+  };
+
+  // Token values of this lane (token 32 i + n of the tile), loaded a group ahead:
+  // affine (a, sum) pairs of [M][G][2], ternary scales of [M][G].
+  const float* tok_src[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const size_t mm = static_cast<size_t>(min(m0 + 32 * i + n, M - 1));
+    tok_src[i] = PARTIALS ? nullptr : xsc + mm * G * (W4 ? 2 : 1);
+  }
+  struct Tok {
+    float a[4], x[4];
+  };
+  auto tok_load = [&](Tok& t, int g) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (PARTIALS) {                    // the partials entry has no token values (xsc is NULL)
+        t.a[i] = t.x[i] = 0.0f;
+        continue;
+      }
+      if (W4) {
+        const float2 v = *reinterpret_cast<const float2*>(tok_src[i] + 2 * g);
+        t.a[i] = v.x;
+        t.x[i] = v.y;
+      } else {
+        t.a[i] = tok_src[i][g];
+        t.x[i] = 0.0f;
+      }
+    }
+  };
+  // Per-lane fold constants of a group: av (a or xs), cv (the fma constant), sx (sum).
+  float av[4], cv[4], sx[4];
+  auto tok_set = [&](const Tok& t) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      av[i] = t.a[i];
+      sx[i] = t.x[i];
+      cv[i] = FX == FX_AFF_SYM ? -8.0f * t.x[i] : 0.0f;     // exact
+    }
+  };
+
+  v16f acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
+
+  v4f sv[4], bv[4];       // the current weight tile's scales (and b) for elements 4q + p
+#pragma unroll
+  for (int q = 0; q < 4; ++q) sv[q] = bv[q] = v4f{};
+  // Fold (or, for the partials entry, store) chain (i, j) of group g.
+  auto fold = [&](const v16i& d, int i, int j, int g) __attribute__((always_inline)) {
+    if (PARTIALS) {
+      const int mm = m0 + 32 * i + n;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int nn = n0 + 64 * wave + 32 * j + d_row(r, h);
+        if (mm >= pm0 && mm < pm1 && nn >= pn0 && nn < pn1)
+          pout[(static_cast<size_t>(mm - pm0) * (pn1 - pn0) + (nn - pn0)) * G + g] = d[r];
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float s1 = sv[r >> 2][r & 3];
+        if (W4) {
+          const float t = fmaf(static_cast<float>(d[r]), av[i], cv[i]);
+          acc[i][j][r] = fmaf(t, s1, acc[i][j][r]);
+          if (ZP) acc[i][j][r] = fmaf(bv[r >> 2][r & 3], sx[i], acc[i][j][r]);
+        } else {
+          acc[i][j][r] = fmaf(static_cast<float>(d[r]) * av[i], s1, acc[i][j][r]);
+        }
+      }
+    }
+  };
+  auto chain = [&](const v4i (&b)[4], const v4i (&a)[4]) __attribute__((always_inline)) {
+    v16i d = __builtin_amdgcn_mfma_i32_32x32x32_i8(b[0], a[0], v16i{}, 0, 0, 0);
+#pragma unroll
+    for (int t = 1; t < 4; ++t) d = __builtin_amdgcn_mfma_i32_32x32x32_i8(b[t], a[t], d, 0, 0, 0);
+    return d;
+  };
+
+  v4i aop[4][4];          // A operands (AGPRs) of the four token tiles
+  v4i bop[4];             // B operands of the weight tile in use
+  v16i dprev = {};        // the chain whose fold is pending
+  Raw raw;
+  Tok tok;
+
+  // Prologue: group 0's activations, codes, token values and staged scales.
+  a_load(0, 0);
+  raw_load(raw, 0);
+  tok_load(tok, 0);
+  {
+    const uint16_t sb = s_row[0];
+    const uint32_t zb = ZP ? static_cast<uint32_t>(z_row[0]) : 0u;
+    __builtin_amdgcn_s_waitcnt(0);
+    stage_scale(sb, zb, 0, 0);
+  }
+  __syncthreads();
+  decode(raw, 0, bop);
+
+  auto group = [&](int g, auto BUFC) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(BUFC)::value;
+    const int gn = min(g + 1, G - 1);
+    a_read(IntC<BUF>{}, IntC<0>{}, aop[0]);
+    a_load(gn, BUF ^ 1);
+    // the previous group's last chain, with that group's tile-1 scales and token values
+    if (g > 0) fold(dprev, 3, 1, g - 1);
+    tok_set(tok);
+    s_read(IntC<BUF>{}, IntC<0>{}, sv, bv);
+    ds_wait_agpr(aop[0]);
+    ds_wait_v4(sv);
+    if (ZP) ds_wait_v4(bv);
+    __builtin_amdgcn_sched_barrier(0);
+    // weight tile 0: chains (0,0) .. (3,0); token tile i + 1 is read during chain (i,0)
+    v16i d = chain(bop, aop[0]);
+    a_read(IntC<BUF>{}, IntC<1>{}, aop[1]);
+    dprev = d;
+    __builtin_amdgcn_sched_barrier(0);
+    Raw nraw;
+    raw_load(nraw, gn);
+    Tok ntok;
+    tok_load(ntok, gn);
+    const uint16_t nsb = s_row[gn];
+    const uint32_t nzb = ZP ? static_cast<uint32_t>(z_row[gn >> 1]) : 0u;
+    __builtin_amdgcn_sched_barrier(0);
+    auto slot0 = [&](auto IC) __attribute__((always_inline)) {
+      constexpr int i = decltype(IC)::value;
+      ds_wait_agpr(aop[i]);
+      const v16i dd = chain(bop, aop[i]);
+      fold(dprev, i - 1, 0, g);
+      if (i < 3) a_read(IntC<BUF>{}, IntC<(i < 3 ? i + 1 : 3)>{}, aop[i < 3 ? i + 1 : 3]);
+      dprev = dd;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, ZP ? 16 : 12, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    slot0(IntC<1>{});
+    slot0(IntC<2>{});
+    slot0(IntC<3>{});
+    // weight tile 1: its B operands replace tile 0's, its scales come after the
+    // fold of chain (3,0), which still uses tile 0's
+    decode(raw, 1, bop);
+    {
+      const v16i dd = chain(bop, aop[0]);
+      fold(dprev, 3, 0, g);
+      dprev = dd;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, ZP ? 16 : 12, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    s_read(IntC<BUF>{}, IntC<1>{}, sv, bv);
+    ds_wait_v4(sv);
+    if (ZP) ds_wait_v4(bv);
+    __builtin_amdgcn_sched_barrier(0);
+    auto slot1 = [&](auto IC) __attribute__((always_inline)) {
+      constexpr int i = decltype(IC)::value;
+      const v16i dd = chain(bop, aop[i]);
+      fold(dprev, i - 1, 1, g);
+      if (i == 3) decode(nraw, 0, bop);      // next group's tile 0, after the last chain's issue
+      dprev = dd;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, i == 3 ? 16 : (ZP ? 16 : 12), 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    slot1(IntC<1>{});
+    slot1(IntC<2>{});
+    slot1(IntC<3>{});
+    raw = nraw;
+    tok = ntok;
+    __builtin_amdgcn_s_waitcnt(0);     // direct A loads, codes, scales and token values have landed
+    stage_scale(nsb, nzb, gn, BUF ^ 1);
+    __syncthreads();
+  };
+  int g = 0;
+  for (; g + 1 < G; g += 2) {
+    group(g, IntC<0>{});
+    group(g + 1, IntC<1>{});
+  }
+  if (g < G) group(g, IntC<0>{});
+  fold(dprev, 3, 1, G - 1);
+  if (PARTIALS) return;
+
+  // Epilogue: per token tile, the wave's 32 x 64 block goes through LDS (rows
+  // of STAGE_ROW floats), written as lane = token row, read out as 4-value row
+  // segments of the output.
+  __syncthreads();
+  float* stage = reinterpret_cast<float*>(smem + wave * 32 * STAGE_ROW * 4);
+  const bool vec = (N & 3) == 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<v4f*>(stage + n * STAGE_ROW + 32 * j + 8 * q + 4 * h) =
+            v4f{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int row = 4 * q + (lane >> 4), c4 = 4 * (lane & 15);
+      const v4f v4 = *reinterpret_cast<const v4f*>(stage + row * STAGE_ROW + c4);
+      const int mm = m0 + 32 * i + row, nn = n0 + 64 * wave + c4;
+      if (mm < M) {
+        const float v[4] = {v4.x, v4.y, v4.z, v4.w};
+        TOut* dst = y + static_cast<size_t>(mm) * N + nn;
+        if (vec && nn + 3 < N) {
+          store_out4(dst, v);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (nn + e < N) store_out(dst + e, v[e]);
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+template <typename TOut, int FX>
+hipError_t go_g(const bpw_weights& w, const int8_t* qp, const float* xs, int m, TOut* y, hipStream_t s) {
+  const int n = static_cast<int>(w.n), k = static_cast<int>(w.k);
+  const int mtiles = (m + BM - 1) / BM, ntiles = (n + BN - 1) / BN;
+  gemm_g_kernel<TOut, false, FX><<<mtiles * ntiles, NT, LDS_G_BYTES, s>>>(
+      qp, xs, static_cast<const uint8_t*>(w.codes), static_cast<const uint16_t*>(w.scales),
+      static_cast<const uint8_t*>(w.zeros), w.scale_dtype == BPW_BF16, m, n, k, y, nullptr, 0, 0, 0, 0, 0, mtiles, 0,
+      ntiles);
+  return hipGetLastError();
+}
+
+template <int FX>
+hipError_t go_g_out(const bpw_weights& w, const int8_t* qp, const float* xs, int m, void* y, int y_dtype,
+                    hipStream_t s) {
+  switch (y_dtype) {
+    case BPW_F32: return go_g<float, FX>(w, qp, xs, m, static_cast<float*>(y), s);
+    case BPW_F16: return go_g<__half, FX>(w, qp, xs, m, static_cast<__half*>(y), s);
+    default: return go_g<uint16_t, FX>(w, qp, xs, m, static_cast<uint16_t*>(y), s);
+  }
+}
+
+template <int FX>
+hipError_t go_g_partials(const bpw_weights& w, const int8_t* qp, int64_t m, int64_t m0, int64_t m1, int64_t n0,
+                         int64_t n1, int32_t* out, hipStream_t s) {
+  const int n = static_cast<int>(w.n), k = static_cast<int>(w.k);
+  const int mt0 = static_cast<int>(m0 / BM), mt1 = static_cast<int>((m1 - 1) / BM);
+  const int nt0 = static_cast<int>(n0 / BN), nt1 = static_cast<int>((n1 - 1) / BN);
+  const int mtiles = mt1 - mt0 + 1, ntiles = nt1 - nt0 + 1;
+  // The partials instance never loads token values.
+  gemm_g_kernel<float, true, FX><<<mtiles * ntiles, NT, LDS_G_BYTES, s>>>(
+      qp, nullptr, static_cast<const uint8_t*>(w.codes),
+      static_cast<const uint16_t*>(w.scales), static_cast<const uint8_t*>(w.zeros), w.scale_dtype == BPW_BF16,
+      static_cast<int>(m), n, k, nullptr, out, static_cast<int>(m0), static_cast<int>(m1), static_cast<int>(n0),
+      static_cast<int>(n1), mt0, mtiles, nt0, ntiles);
+  return hipGetLastError();
+}
+
 template <typename TOut, int WF>
 hipError_t go(const bpw_weights& w, const int8_t* qp, const float* xs, int m, TOut* y,
               hipStream_t s) {
@@ -434,6 +862,21 @@ hipError_t launch_gemm_w4a8(const bpw_weights& w, const int8_t* q_nibbles, const
   const int mi = static_cast<int>(m);
   return w.fmt == BPW_INT4_ZP ? go_out<WF_I4Z>(w, q_nibbles, x_scale, mi, y, y_dtype, s)
                               : go_out<WF_I4>(w, q_nibbles, x_scale, mi, y, y_dtype, s);
+}
+
+hipError_t launch_gemm_g(const bpw_weights& w, const int8_t* q_ordered, const float* x_scale, int64_t m, void* y,
+                         int y_dtype, hipStream_t s) {
+  const int mi = static_cast<int>(m);
+  if (w.fmt == BPW_TERNARY2) return go_g_out<FX_T2G>(w, q_ordered, x_scale, mi, y, y_dtype, s);
+  return w.fmt == BPW_INT4_ZP ? go_g_out<FX_AFF_ZP>(w, q_ordered, x_scale, mi, y, y_dtype, s)
+                              : go_g_out<FX_AFF_SYM>(w, q_ordered, x_scale, mi, y, y_dtype, s);
+}
+
+hipError_t launch_gemm_g_partials(const bpw_weights& w, const int8_t* q_ordered, int64_t m, int64_t m0, int64_t m1,
+                                  int64_t n0, int64_t n1, int32_t* out, hipStream_t s) {
+  if (w.fmt == BPW_TERNARY2) return go_g_partials<FX_T2G>(w, q_ordered, m, m0, m1, n0, n1, out, s);
+  return w.fmt == BPW_INT4_ZP ? go_g_partials<FX_AFF_ZP>(w, q_ordered, m, m0, m1, n0, n1, out, s)
+                              : go_g_partials<FX_AFF_SYM>(w, q_ordered, m, m0, m1, n0, n1, out, s);
 }
 
 hipError_t launch_gemm_w4a8_partials(const bpw_weights& w, const int8_t* q_nibbles, int64_t m,

@@ -17,6 +17,7 @@
 // agree); then one 16-byte code load per lane and weight tile feeds all four
 // steps.
 #include "device.h"
+#include "lds_dma.h"
 #include "launch.h"
 #include "store.h"
 

@@ -16,6 +16,11 @@ hipError_t launch_quantize_rows(const void* x, int x_dtype, int64_t m, int64_t k
 // One scale per (row, 128-group): x_scale [M][K/128]. K % 128 == 0.
 hipError_t launch_quantize_groups(const void* x, int x_dtype, int64_t m, int64_t k, int8_t* q,
                                   float* x_scale, hipStream_t s);
+// int8 codes with one scale a = amax / 127 and the exact fp32 sum per (row, weight
+// group): group g is the columns perm[128 g ..] (identity when perm is NULL);
+// xs [M][K/128][2] holds the (a, sum) pairs. K % 128 == 0.
+hipError_t launch_quantize_groups_sums(const void* x, int x_dtype, const int32_t* perm, int64_t m, int64_t k,
+                                       int8_t* q, float* xs, hipStream_t s);
 // q [M][K] natural order -> plane order inside each 128-group (element 4u+t of a
 // 64-element half-group goes to position 32t + 16*half + u).
 hipError_t launch_int8_planes(const int8_t* q, int64_t m, int64_t k, int8_t* q_planes,
@@ -61,6 +66,14 @@ hipError_t launch_gemm_w4a8(const bpw_weights& w, const int8_t* q_nibbles, const
 hipError_t launch_gemm_w4a8_partials(const bpw_weights& w, const int8_t* q_nibbles, int64_t m,
                                      int64_t m0, int64_t m1, int64_t n0, int64_t n1, int32_t* out,
                                      hipStream_t s);
+// Per-(token, group) activation values on the int8 matrix core: ternary weights
+// with x_scale [M][G] (q in plane order), or 4-bit weights in the affine form with
+// x_scale [M][G][2] = (a, sum) pairs (q in nibble order).
+hipError_t launch_gemm_g(const bpw_weights& w, const int8_t* q_ordered, const float* x_scale, int64_t m, void* y,
+                         int y_dtype, hipStream_t s);
+// Its int32 core: ternary P (code - 1) or 4-bit raw-code dots D.
+hipError_t launch_gemm_g_partials(const bpw_weights& w, const int8_t* q_ordered, int64_t m, int64_t m0, int64_t m1,
+                                  int64_t n0, int64_t n1, int32_t* out, hipStream_t s);
 hipError_t launch_gemm_w4(const bpw_weights& w, const void* x_sorted, int x_dtype, int64_t m,
                           void* y, int y_dtype, hipStream_t s);
 

@@ -1,4 +1,5 @@
-// Activation operand kernels: int8 row and group quantisers, int8 plane
+// Activation operand kernels: int8 row and group quantisers, the group
+// quantiser with exact group sums (4-bit x int8 in its affine form), int8 plane
 // reorder (ternary GEMM), int8 nibble reorder (4-bit x int8 GEMM, with the
 // act-order gather), act-order column gather for 16-bit activations.
 //
@@ -113,6 +114,102 @@ __global__ __launch_bounds__(256) void quantize_groups_kernel(const T* __restric
   }
 }
 
+// Double-double (hi, lo) arithmetic in fp64 for exact group sums: two_sum
+// returns s = fl(a + b) and the exact rounding error e, so a + b == s + e.
+__device__ __forceinline__ void two_sum(double a, double b, double& s, double& e) {
+  s = a + b;
+  const double bb = s - a;
+  e = (a - (s - bb)) + (b - bb);
+}
+
+// The fp32 value next to finite f, upward (up) or downward, by its bit pattern.
+__device__ __forceinline__ float next_f32(float f, bool up) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) == 0) return __uint_as_float(up ? 1u : 0x80000001u);
+  const bool away = (static_cast<int32_t>(u) >= 0) == up;              // moving away from zero
+  return __uint_as_float(away ? u + 1 : u - 1);
+}
+
+// The fp32 nearest (ties to even) to hi + lo, where |lo| <= ulp(hi) / 2. Rounding
+// hi alone gives it unless hi is exactly halfway between two fp32 values; then a
+// nonzero lo decides the side.
+__device__ __forceinline__ float dd_to_f32(double hi, double lo) {
+  const float f = static_cast<float>(hi);                         // round to nearest even
+  const double df = static_cast<double>(f);
+  if (lo == 0.0 || df == hi || !__builtin_isfinite(f)) return f;
+  const float g = next_f32(f, hi > df);
+  if ((df + static_cast<double>(g)) * 0.5 != hi) return f;      // hi is not a midpoint
+  return ((lo > 0.0) == (static_cast<double>(g) > df)) ? g : f;  // the side of hi + lo
+}
+
+// "TensorFold PR #1176" (tf_w4a8_quantize): one wave per (row, weight group).
+// Group g of a row is the columns perm[128 g .. 128 g + 127] (the identity
+// without act order), two per lane. a = fl32(amax / 127) with an IEEE
+// division; q = clamp(round_half_even(x / a), -127, 127), written back to its
+// own column; the group's sum of x is exact: each lane's two values are added
+// with two_sum in fp64, the 64 (hi, lo) pairs are combined in a butterfly of
+// two_sum steps (every lane ends with the same pair: each step is symmetric
+// in its operands), and the pair is rounded once to fp32. This is exact
+// whenever the group's nonzero values span at most 2^73 in magnitude (always
+// for fp16 inputs); beyond that the smallest values add with a relative error
+// below 2^-104 of the sum. Output pairs (a, sum) go to xs[(row * G + g) * 2].
+// A group holding a NaN or an infinity gets a = sum = NaN and zero codes.
+// perm entries outside [0, K) read as zero and their code is not written.
+template <typename T, bool PERM>
+__global__ __launch_bounds__(256) void quantize_groups_sums_kernel(const T* __restrict__ x,
+                                                                   const int32_t* __restrict__ perm,
+                                                                   int64_t units, int64_t k,
+                                                                   int8_t* __restrict__ q,
+                                                                   float* __restrict__ xs) {
+  const int lane = threadIdx.x & 63;
+  const int64_t groups = k >> 7;
+  for (int64_t u = blockIdx.x * 4ll + (threadIdx.x >> 6); u < units; u += gridDim.x * 4ll) {   // whole waves
+    const int64_t row = u / groups, g = u - row * groups;
+    const int64_t j = g * 128 + 2 * lane;
+    uint32_t c0 = static_cast<uint32_t>(j), c1 = static_cast<uint32_t>(j + 1);
+    if (PERM) {
+      c0 = static_cast<uint32_t>(perm[j]);
+      c1 = static_cast<uint32_t>(perm[j + 1]);
+    }
+    const bool in0 = c0 < static_cast<uint64_t>(k), in1 = c1 < static_cast<uint64_t>(k);
+    const T* xr = x + row * k;
+    const float v0 = in0 ? ld(xr + c0) : 0.0f, v1 = in1 ? ld(xr + c1) : 0.0f;
+    float amax = fmaxf(fabsf(v0), fabsf(v1));
+    const float nonfinite = fmaf(v0, 0.0f, v1 * 0.0f);
+    if (nonfinite != nonfinite) amax = __builtin_inff();
+    double hi, lo;
+    two_sum(static_cast<double>(v0), static_cast<double>(v1), hi, lo);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      amax = fmaxf(amax, __shfl_xor(amax, off));
+      const double ohi = __shfl_xor(hi, off), olo = __shfl_xor(lo, off);
+      double sh, se;
+      two_sum(hi, ohi, sh, se);
+      const double t = (lo + olo) + se;
+      hi = sh + t;                                                // fast two_sum: |sh| >= |t|
+      lo = t - (hi - sh);
+    }
+    const bool bad = __builtin_isinf(amax);        // the same in every lane of the wave
+    const float a = bad ? __builtin_nanf("") : amax / 127.0f;   // IEEE division
+    const float div = a > 0.0f ? a : 1.0f;
+    const float r0 = bad ? 0.0f : fminf(fmaxf(rintf(v0 / div), -127.0f), 127.0f);   // ties to even
+    const float r1 = bad ? 0.0f : fminf(fmaxf(rintf(v1 / div), -127.0f), 127.0f);
+    int8_t* qr = q + row * k;
+    if (PERM) {
+      if (in0) qr[c0] = static_cast<int8_t>(static_cast<int>(r0));
+      if (in1) qr[c1] = static_cast<int8_t>(static_cast<int>(r1));
+    } else {
+      const uint32_t pair = (static_cast<uint32_t>(static_cast<int>(r0)) & 0xFFu) |
+                            ((static_cast<uint32_t>(static_cast<int>(r1)) & 0xFFu) << 8);
+      *reinterpret_cast<uint16_t*>(qr + j) = static_cast<uint16_t>(pair);
+    }
+    if (lane == 0) {
+      const float sum = bad ? __builtin_nanf("") : dd_to_f32(hi, lo);
+      *reinterpret_cast<float2*>(xs + 2 * u) = float2{a, sum};
+    }
+  }
+}
+
 // One thread per (row, group, half): 64 natural bytes -> four 16-byte plane chunks.
 __global__ __launch_bounds__(256) void int8_planes_kernel(const int8_t* __restrict__ q,
                                                           int64_t m, int64_t k,
@@ -155,7 +252,10 @@ __global__ __launch_bounds__(256) void int8_nibbles_kernel(const int8_t* __restr
       for (int i = 0; i < 16; ++i) {
         uint32_t v = 0;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) v |= static_cast<uint32_t>(qr[pj[4 * i + b]]) << (8 * b);
+        for (int b = 0; b < 4; ++b) {
+          const uint32_t c = static_cast<uint32_t>(pj[4 * i + b]);     // out-of-range entries read as 0
+          v |= (c < static_cast<uint64_t>(k) ? static_cast<uint32_t>(qr[c]) : 0u) << (8 * b);
+        }
         d[i] = v;
       }
     } else {
@@ -202,7 +302,8 @@ __global__ __launch_bounds__(256) void gather_cols_kernel(const uint16_t* __rest
   for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < total; i += gridDim.x * 256ll) {
     const int64_t row = i / k;
     const int64_t j = i - row * k;
-    out[i] = x[row * k + perm[j]];
+    const uint32_t c = static_cast<uint32_t>(perm[j]);               // out-of-range entries read as 0
+    out[i] = c < static_cast<uint64_t>(k) ? x[row * k + c] : static_cast<uint16_t>(0);
   }
 }
 
@@ -246,6 +347,28 @@ hipError_t launch_quantize_groups(const void* x, int x_dtype, int64_t m, int64_t
     case BPW_F32: quantize_groups_go<float>(x, m, k, q, x_scale, s); break;
     case BPW_F16: quantize_groups_go<__half>(x, m, k, q, x_scale, s); break;
     default: quantize_groups_go<uint16_t>(x, m, k, q, x_scale, s); break;
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+void quantize_groups_sums_go(const void* x, const int32_t* perm, int64_t m, int64_t k, int8_t* q, float* xs,
+                             hipStream_t s) {
+  const int64_t units = m * (k / 128);
+  if (perm)
+    quantize_groups_sums_kernel<T, true><<<grid_for(units, 4), 256, 0, s>>>(static_cast<const T*>(x), perm, units, k,
+                                                                           q, xs);
+  else
+    quantize_groups_sums_kernel<T, false><<<grid_for(units, 4), 256, 0, s>>>(static_cast<const T*>(x), nullptr, units,
+                                                                            k, q, xs);
+}
+
+hipError_t launch_quantize_groups_sums(const void* x, int x_dtype, const int32_t* perm, int64_t m, int64_t k,
+                                       int8_t* q, float* xs, hipStream_t s) {
+  switch (x_dtype) {
+    case BPW_F32: quantize_groups_sums_go<float>(x, perm, m, k, q, xs, s); break;
+    case BPW_F16: quantize_groups_sums_go<__half>(x, perm, m, k, q, xs, s); break;
+    default: quantize_groups_sums_go<uint16_t>(x, perm, m, k, q, xs, s); break;
   }
   return hipGetLastError();
 }

@@ -58,6 +58,12 @@ extern "C" {
  * Accepted by bpw_gemv_packed for ternary weights ("Kernel experiments",
  * Test 6: the quantiser's scale is per group of 128 activations). */
 #define BPW_I8G 5
+/* int8 activations with, per (row, weight group), one fp32 scale a and the
+ * exact fp32 sum of the unquantised activations: x_scale [M][K/128][2] holding
+ * (a, sum) pairs, as written by bpw_quantize_groups_sums. Accepted by
+ * bpw_gemm_packed for 4-bit weights ("TensorFold PR #1176", "What changes":
+ * the int8 prompt GEMM takes s * a * (code . q) + b * sum(x) per group). */
+#define BPW_I8GS 6
 
 /* ---- source layouts accepted by bpw_prepare_packed ------------------- */
 #define BPW_SRC_PQ2_BLOCKS 1 /* ternary only: [N][G][34] = fp16 scale (little-endian) + 32 code bytes */
@@ -67,6 +73,7 @@ extern "C" {
 /* ---- partial-sum cores for bpw_partials ------------------------------ */
 #define BPW_PATH_GEMV 0
 #define BPW_PATH_GEMM 1
+#define BPW_PATH_GEMM_RAW 2 /* bpw_partials only: raw-code dots of the I8GS GEMM core */
 
 /* ---- HBM probes for bpw_probe ---------------------------------------- */
 #define BPW_PROBE_READ 0 /* read every byte of src (16-byte loads), write one word per block to dst */
@@ -171,6 +178,28 @@ int bpw_quantize_groups(const void* x, int x_dtype, int64_t m, int64_t k, int8_t
                         void* stream);
 
 /*
+ * int8 activation quantiser of the 4-bit x int8 prefill in its affine form
+ * ("TensorFold PR #1176", "What changes": tf_w4a8_quantize writes each
+ * activation group as int8 codes with one fp32 scale a = amax / 127 and the
+ * group's exact fp32 sum). Here a group is one weight group: the 128 columns
+ * perm[128 g .. 128 g + 127] of a row (columns 128 g .. when perm is NULL), so
+ * that a and the sum pair with the weight's scale and zero point of group g.
+ *   a[m,g]   = fl32(max_{k in g} |x[m,k]| / 127)            (IEEE division)
+ *   q[m,k]   = clamp(round_half_even(x[m,k] / (a > 0 ? a : 1)), -127, 127)
+ *   sum[m,g] = the exact sum of x[m,k] over the group, rounded once to fp32
+ *              (exact whenever the group's nonzero values span at most 2^73
+ *              in magnitude, always for fp16 inputs)
+ * A group holding a NaN or an infinity gets a = sum = NaN and zero codes.
+ * x: device [M][K] of x_dtype (F32/F16/BF16), K a multiple of 128;
+ * perm: device int32 [K] (the prepared weight's perm) or NULL; entries outside
+ *   [0, K) are read as zero and their codes are not written;
+ * q: device int8 [M][K], codes in the columns of x, 16-byte aligned;
+ * x_scale_sum: device fp32 [M][K/128][2], (a, sum) pairs, 8-byte aligned.
+ */
+int bpw_quantize_groups_sums(const void* x, int x_dtype, int64_t m, int64_t k, const int32_t* perm, int8_t* q,
+                             float* x_scale_sum, void* stream);
+
+/*
  * Device workspace (bytes, 256-byte aligned start) that bpw_gemv_packed /
  * bpw_gemm_packed need for this weight, M and activation type; 0 if none.
  * entry: BPW_PATH_GEMV or BPW_PATH_GEMM. Host only.
@@ -225,18 +254,30 @@ int bpw_gemv_packed_scratch(const bpw_weights* w, const void* x, int x_dtype, co
 
 /*
  * y = x @ W^T, prefill-shaped (large M). Same arguments and combinations as
- * bpw_gemv_packed, except I8G (BPW_EUNSUPPORTED), plus 4-bit weights x I8.
+ * bpw_gemv_packed, plus 4-bit weights x I8 or I8GS.
  * Numerics: ternary x int8 -> as above (int8 MFMA, exact int32 group
  * partials). 4-bit x F16/BF16 -> each weight is dequantised to the activation dtype,
  * round-to-nearest-even of (code - zero) * scale, then multiplied on MFMA with
  * fp32 accumulation (the float path of the mate PR: unpack int4 to the
  * activation type before the matrix instruction).
  * 4-bit x I8 ("TensorFold PR #1176", the int8 prompt GEMM: a 4-bit code is an
- * exact int8, so the group dot runs exactly on the int8 matrix instruction):
+ * exact int8, so the group dot runs exactly on the int8 matrix instruction),
+ * with one activation scale per row:
  * P[m,n,g] = sum_{k in g} q[m,k] * (code[n,k] - zero[n,g]) in exact int32
  * (zero 8 for INT4_SYM), then y = x_scale[m] * sum_g scale[n,g] * P[m,n,g] in
  * fp32. With act order, q is gathered through perm. Needs a workspace of
  * M * K bytes (a reordered copy of q).
+ * 4-bit x I8GS (the same page's affine form, its own formula): with
+ * b[n,g] = -zero[n,g] * scale[n,g] (zero 8 for INT4_SYM),
+ *   D[m,n,g] = sum_{k in g} q[m,k] * code[n,k]   (raw codes 0..15, exact int32)
+ *   y[m,n]   = sum_g scale[n,g] * a[m,g] * D[m,n,g] + b[n,g] * sum[m,g]   (fp32)
+ * where (a, sum) = x_scale[m][g][0..1] from bpw_quantize_groups_sums run with
+ * the weight's perm. Each group's int32 D is converted exactly to fp32 and
+ * folded as scale * fma(D, a, -8 * sum) (symmetric codes) or
+ * scale * (D * a) + b * sum (zero points). Needs a workspace of M * K bytes.
+ * Ternary x I8G (one activation scale per (row, 128-group), "Kernel
+ * experiments", Test 7's fold partial * x_scale * w_scale per group):
+ * y = sum_g x_scale[m,g] * scale[n,g] * P[m,n,g]; workspace M * K bytes.
  */
 int bpw_gemm_packed(const bpw_weights* w, const void* x, int x_dtype, const float* x_scale,
                     int64_t m, void* y, int y_dtype, void* workspace, size_t workspace_bytes,
@@ -248,7 +289,9 @@ int bpw_gemm_packed(const bpw_weights* w, const void* x, int x_dtype, const floa
  * for m0 <= m < m1, n0 <= n < n1, computed by the same kernel core as the
  * product, with value = code - 1 (TERNARY2) or code - zero (INT4_*; group g
  * in act order, q gathered through perm). Path BPW_PATH_GEMV: TERNARY2 and
- * M <= 32 only; BPW_PATH_GEMM: any format and M. q: device int8 [M][K].
+ * M <= 32 only; BPW_PATH_GEMM: any format and M; BPW_PATH_GEMM_RAW: INT4_*
+ * only, value = code (the raw-code dots D of the I8GS product, from its
+ * kernel). q: device int8 [M][K].
  * out: device int32 [(m1-m0)][(n1-n0)][G]. workspace as for the product.
  */
 int bpw_partials(const bpw_weights* w, const int8_t* q, int64_t m, int path, int64_t m0,

@@ -164,12 +164,19 @@ def test_gemv_ternary_group_scales(m, k, n, out):
     assert_close(host(y), y_ref, out, f"gemv ternary group scales m={m} k={k} n={n}")
 
 
-def test_group_scales_refused_where_unsupported():
+def test_group_scales_through_both_entries():
+    # The decode GEMV and the prefill GEMM both take per-group scales; on the
+    # same inputs each meets the parity rule (their fp32 fold orders differ).
     w = ternary_case(4, 256, 64, 9)
     pw = prepare(w)
     q, xs = bpw.quantize_groups(to_dev(w.x, "f32"))
-    with pytest.raises(bpw.BpwError, match="bpw_gemv_packed only"):
-        bpw.gemm_packed(pw, q, xs)
+    y1 = bpw.gemv_packed(pw, q, xs)
+    y2 = bpw.gemm_packed(pw, q, xs)
+    torch.cuda.synchronize()
+    q_ref, xs_ref = quant.quantize_groups(w.x)
+    _, y_ref = reference.ternary_int8_product_group_scales(q_ref, xs_ref, w.codes, w.scales)
+    assert_close(host(y1), y_ref, "f16", "group scales, decode entry")
+    assert_close(host(y2), y_ref, "f16", "group scales, prefill entry")
 
 
 @pytest.mark.parametrize("m,k,n", [(1, 256, 300), (130, 1024, 520), (300, 640, 257), (64, 128, 256)])

@@ -188,9 +188,15 @@ def test_product_validation_statuses():
 def test_group_scale_validation():
     lib = bpw.lib()
     w = _weights(k=4096, n=300)
+    # the prefill entry takes per-group scales too, on its plane-ordered copy of q (M * K bytes)
     st = lib.bpw_gemm_packed(ctypes.byref(w), 65536, bpw.I8G, 1024, 4, 131072, bpw.F16, None, 0, None)
-    assert st == bpw.EUNSUPPORTED and "bpw_gemv_packed only" in bpw.last_error()
-    assert _gemv(_weights(k=256), x_dtype=bpw.I8G, m=33) == bpw.EUNSUPPORTED     # decode shapes only
+    assert st == bpw.EINVAL and "16384-byte device workspace" in bpw.last_error()
+    need = ctypes.c_size_t(7)
+    assert lib.bpw_workspace_size(ctypes.byref(w), 4, bpw.I8G, bpw.PATH_GEMM, ctypes.byref(need)) == 0
+    assert need.value == 4 * 4096
+    # beyond 32 rows the decode entry routes to the same prefill kernel
+    assert _gemv(_weights(k=256), x_dtype=bpw.I8G, m=33) == bpw.EINVAL
+    assert "workspace" in bpw.last_error()
     assert _gemv(_weights(k=256), x_dtype=bpw.I8G, xs=None) == bpw.EINVAL
     assert _gemv(_weights(k=256), x_dtype=bpw.I8G, xs=1026) == bpw.EALIGN
     assert _gemv(_weights(bpw.INT4_SYM), x_dtype=bpw.I8G) == bpw.EUNSUPPORTED
@@ -203,6 +209,35 @@ def test_group_scale_validation():
     assert quant(65536, bpw.I8, 2, 256, 131072, 1024, None) == bpw.EUNSUPPORTED
     assert quant(65536, bpw.F32, 2, 256, 131080, 1024, None) == bpw.EALIGN      # q 16-byte aligned
     assert quant(None, bpw.F32, 2, 256, 131072, 1024, None) == bpw.EINVAL
+
+
+def test_affine_w4a8_validation():
+    lib = bpw.lib()
+    w4 = _weights(bpw.INT4_SYM, k=512, n=300)
+    # the affine form (BPW_I8GS) is 4-bit x int8 on the prefill entry only
+    assert _gemv(w4, x_dtype=bpw.I8GS) == bpw.EUNSUPPORTED and "bpw_gemm_packed" in bpw.last_error()
+    assert _gemv(_weights(k=512), x_dtype=bpw.I8GS) == bpw.EUNSUPPORTED               # ternary: not this form
+    st = lib.bpw_gemm_packed(ctypes.byref(w4), 65536, bpw.I8GS, 1024, 4, 131072, bpw.F16, None, 0, None)
+    assert st == bpw.EINVAL and "2048-byte device workspace" in bpw.last_error()
+    st = lib.bpw_gemm_packed(ctypes.byref(w4), 65536, bpw.I8GS, 1028, 4, 131072, bpw.F16, None, 0, None)
+    assert st == bpw.EALIGN                                                             # (a, sum) pairs: 8 bytes
+    st = lib.bpw_gemm_packed(ctypes.byref(w4), 65536, bpw.I8GS, None, 4, 131072, bpw.F16, None, 0, None)
+    assert st == bpw.EINVAL
+    need = ctypes.c_size_t()
+    assert lib.bpw_workspace_size(ctypes.byref(w4), 4, bpw.I8GS, bpw.PATH_GEMM, ctypes.byref(need)) == 0
+    assert need.value == 2048
+    quant = lib.bpw_quantize_groups_sums
+    assert quant(65536, bpw.F32, 2, 200, None, 131072, 1024, None) == bpw.ESHAPE          # K % 128
+    assert quant(65536, bpw.I8, 2, 256, None, 131072, 1024, None) == bpw.EUNSUPPORTED
+    assert quant(65536, bpw.F32, 2, 256, None, 131080, 1024, None) == bpw.EALIGN          # q 16-byte aligned
+    assert quant(65536, bpw.F32, 2, 256, None, 131072, 1028, None) == bpw.EALIGN          # pairs 8-byte aligned
+    assert quant(65536, bpw.F32, 2, 256, 4098, 131072, 1024, None) == bpw.EALIGN          # perm 4-byte aligned
+    assert quant(None, bpw.F32, 2, 256, None, 131072, 1024, None) == bpw.EINVAL
+    # raw-code partials: a known path, 4-bit or ternary, with the GEMM workspace
+    st = lib.bpw_partials(ctypes.byref(w4), 65536, 4, bpw.PATH_GEMM_RAW, 0, 4, 0, 300, 131072, None, 0, None)
+    assert st == bpw.EINVAL and "workspace" in bpw.last_error()
+    st = lib.bpw_partials(ctypes.byref(w4), 65536, 4, 3, 0, 4, 0, 300, 131072, None, 0, None)
+    assert st == bpw.EINVAL and "unknown path" in bpw.last_error()
 
 
 def test_workspace_sizes():

@@ -98,7 +98,8 @@ def kernel_bodies(asm, pattern):
         yield name, [line.strip() for line in asm[start:asm.find(".Lfunc_end", start)].splitlines()]
 
 
-@pytest.mark.parametrize("src,pattern", [("gemm_i8.hip", "gemm_t2_kernel"), ("gemm_w4.hip", "gemm_w4_kernel")])
+@pytest.mark.parametrize("src,pattern", [("gemm_i8.hip", "gemm_t2_kernel"), ("gemm_i8.hip", "gemm_g_kernel"),
+                                         ("gemm_w4.hip", "gemm_w4_kernel")])
 def test_no_register_reuse_under_inflight_loads(src, pattern, tmp_path):
     asm = compile_asm(src, tmp_path)
     found = 0
