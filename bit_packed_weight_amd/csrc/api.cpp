@@ -26,11 +26,21 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 bool is_int4(int fmt) { return fmt == BPW_INT4_SYM || fmt == BPW_INT4_ZP; }
 bool is_out_dtype(int d) { return d == BPW_F32 || d == BPW_F16 || d == BPW_BF16; }
 
-// gfx950 check, once per device: the kernels are compiled for gfx950 only.
-int check_device() {
+// The device a call runs on: the current device, which must also be the
+// stream's device (kernels launch on the stream, and the workspace and operand
+// pointers are the caller's allocations on it); gfx950 checked once per device
+// (the kernels are compiled for gfx950 only).
+int check_device(hipStream_t stream) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(BPW_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (stream) {
+    hipDevice_t sdev = 0;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return fail(BPW_EHIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+    if (static_cast<int>(sdev) != dev)
+      return fail(BPW_EINVAL, "the stream belongs to device %d but device %d is current", static_cast<int>(sdev), dev);
+  }
   static std::mutex mu;
   static int checked[64] = {0};   // 0 unknown, 1 ok, 2 wrong architecture
   std::lock_guard<std::mutex> lock(mu);
@@ -120,7 +130,7 @@ int check_product_args(const bpw_weights* w, const void* x, int x_dtype, const f
   return check_product(w, x, x_dtype, x_scale, m, y, y_dtype);
 }
 
-int check_current_device() { return check_device(); }
+int check_current_device(void* stream) { return check_device(static_cast<hipStream_t>(stream)); }
 
 // Workspace bytes for (weights, M, activation type, entry).
 size_t workspace_need(const bpw_weights* w, int64_t m, int x_dtype, int entry) {
@@ -156,8 +166,8 @@ int run_product(bool gemv, const bpw_weights* w, const void* x, int x_dtype, con
   if (is_int4(w->fmt) && (x_dtype == BPW_I8 || x_dtype == BPW_I8GS) && gemv)
     return fail(BPW_EUNSUPPORTED, "4-bit weights with int8 activations run through bpw_gemm_packed only");
   if (int st = check_workspace(w, m, x_dtype, entry, ws, ws_bytes)) return st;
-  if (int st = check_device()) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (int st = check_device(s)) return st;
   if (is_int4(w->fmt) && (x_dtype == BPW_I8 || x_dtype == BPW_I8GS)) {
     int8_t* qn = static_cast<int8_t*>(ws);
     if (int st = hip_status(launch_int8_nibbles(static_cast<const int8_t*>(x), w->perm, m, w->k, qn, s),
@@ -227,7 +237,7 @@ extern "C" int bpw_quantize_rows(const void* x, int x_dtype, int64_t m, int64_t 
     return fail(BPW_ESHAPE, "M=%lld, K=%lld must be in 1..2^30", (long long)m, (long long)k);
   if (!aligned(x, x_dtype == BPW_F32 ? 4 : 2) || !aligned(x_scale, 4))
     return fail(BPW_EALIGN, "x / x_scale misaligned for their dtypes");
-  if (int st = check_device()) return st;
+  if (int st = check_device(static_cast<hipStream_t>(stream))) return st;
   return hip_status(launch_quantize_rows(x, x_dtype, m, k, q, x_scale, static_cast<hipStream_t>(stream)),
                     "quantiser launch");
 }
@@ -242,7 +252,7 @@ extern "C" int bpw_quantize_groups(const void* x, int x_dtype, int64_t m, int64_
                 (long long)k);
   if (!aligned(x, x_dtype == BPW_F32 ? 4 : 2) || !aligned(q, 16) || !aligned(x_scale, 4))
     return fail(BPW_EALIGN, "x / q / x_scale misaligned (q must be 16-byte aligned)");
-  if (int st = check_device()) return st;
+  if (int st = check_device(static_cast<hipStream_t>(stream))) return st;
   return hip_status(launch_quantize_groups(x, x_dtype, m, k, q, x_scale, static_cast<hipStream_t>(stream)),
                     "group quantiser launch");
 }
@@ -258,7 +268,7 @@ extern "C" int bpw_quantize_groups_sums(const void* x, int x_dtype, int64_t m, i
   if (!aligned(x, x_dtype == BPW_F32 ? 4 : 2) || !aligned(q, 16) || !aligned(x_scale_sum, 8) ||
       (perm && !aligned(perm, 4)))
     return fail(BPW_EALIGN, "x / q / x_scale_sum / perm misaligned (q 16-byte, x_scale_sum 8-byte)");
-  if (int st = check_device()) return st;
+  if (int st = check_device(static_cast<hipStream_t>(stream))) return st;
   return hip_status(launch_quantize_groups_sums(x, x_dtype, perm, m, k, q, x_scale_sum,
                                                 static_cast<hipStream_t>(stream)),
                     "group quantiser (with sums) launch");
@@ -306,8 +316,8 @@ extern "C" int bpw_partials(const bpw_weights* w, const int8_t* q, int64_t m, in
   if (path != BPW_PATH_GEMV) {
     if (int st = check_workspace(w, m, BPW_I8, BPW_PATH_GEMM, workspace, workspace_bytes)) return st;
   }
-  if (int st = check_device()) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (int st = check_device(s)) return st;
   if (path == BPW_PATH_GEMV)
     return hip_status(launch_gemv_t2_partials(*w, q, m, m0, m1, n0, n1, out, s), "GEMV partials launch");
   int8_t* qp = static_cast<int8_t*>(workspace);
@@ -331,6 +341,6 @@ extern "C" int bpw_probe(int kind, const void* src, void* dst, size_t bytes, voi
   if (bytes == 0 || bytes % 16) return fail(BPW_ESHAPE, "bytes must be a positive multiple of 16");
   if (!aligned(src, 16) || !aligned(dst, kind == BPW_PROBE_COPY ? 16 : 4))
     return fail(BPW_EALIGN, "src / dst misaligned");
-  if (int st = check_device()) return st;
+  if (int st = check_device(static_cast<hipStream_t>(stream))) return st;
   return hip_status(launch_probe(kind, src, dst, bytes, static_cast<hipStream_t>(stream)), "probe launch");
 }

@@ -16,8 +16,9 @@ int check_weights(const bpw_weights* w);
 // the host, without looking at a workspace or the device.
 int check_product_args(const bpw_weights* w, const void* x, int x_dtype, const float* x_scale, int64_t m,
                        void* y, int y_dtype);
-// The current device is a gfx950 (checked once per device).
-int check_current_device();
+// The current device is the stream's device (when the stream is not NULL) and
+// a gfx950 (checked once per device).
+int check_current_device(void* stream);
 // Device workspace bytes a product needs for (weights, M, activation type,
 // entry), rounded up to 256; the descriptor must already be valid.
 size_t workspace_need(const bpw_weights* w, int64_t m, int x_dtype, int entry);

@@ -68,7 +68,7 @@ extern "C" int bpw_gemv_packed_scratch(const bpw_weights* w, const void* x, int 
                 "this call needs %zu bytes of workspace; the fixed scratch holds %d (use bpw_gemv_packed "
                 "with a caller workspace)",
                 need, BPW_SCRATCH_BYTES);
-  if (int st = check_current_device()) return st;
+  if (int st = check_current_device(stream)) return st;
   void* ws = nullptr;
   if (need > 0) {
     if (int st = scratch_ptr(&ws)) return st;

@@ -11,7 +11,10 @@
  * "TensorFold PR #1176" (4-bit weights against int8 activations on the int8
  * matrix instruction).
  *
- * Conventions for every entry point:
+ * Conventions for every entry point (the shape of the pages' own interfaces:
+ * "Kernel experiments", Test 1's prepare step validates its input and raises
+ * naming the violated condition before any work, and Test 23's launcher takes
+ * caller-allocated buffers, the current stream and returns an int status):
  *  - "host" pointers are ordinary CPU memory; "device" pointers are GPU memory
  *    owned by the caller (e.g. allocated through PyTorch). The library never
  *    allocates or frees device memory and never synchronises a stream, except
@@ -111,14 +114,22 @@ typedef struct bpw_sizes {
   size_t codes, scales, zeros, perm; /* bytes of each prepared plane (0 = absent) */
 } bpw_sizes;
 
-/* Library version (major * 10000 + minor * 100 + patch). */
+/* Library version (major * 10000 + minor * 100 + patch); library metadata,
+ * not from the pages. */
 int bpw_version(void);
 
-/* Thread-local text of the last error of this thread ("" after success). */
+/* Thread-local text of the last error of this thread ("" after success): the
+ * text names the violated invariant, as the pages' prepare and launch steps
+ * do in their exceptions ("Kernel experiments", Tests 1 and 23). */
 const char* bpw_last_error(void);
 
 /*
- * Byte sizes of the prepared planes for an N x K weight of format fmt.
+ * Byte sizes of the prepared planes for an N x K weight of format fmt
+ * ("Kernel experiments", Test 1: separate code and scale buffers keep exactly
+ * 34 bytes per 128-weight block, 32 of codes and a 2-byte scale; the mate PR's
+ * 4-bit codes add half a byte per weight, a zero-point nibble per group and,
+ * with act order, the K-entry permutation). scale_dtype (F16 or BF16) sets
+ * the scale plane's element size; the zero plane is present for INT4_ZP.
  * Logical weight bytes per product = codes + scales + zeros (the perm plane is
  * K int32 and is read once per call, not per row). Host only; never touches
  * the GPU.
@@ -202,12 +213,20 @@ int bpw_quantize_groups_sums(const void* x, int x_dtype, int64_t m, int64_t k, c
 /*
  * Device workspace (bytes, 256-byte aligned start) that bpw_gemv_packed /
  * bpw_gemm_packed need for this weight, M and activation type; 0 if none.
+ * The caller allocates it, as the pages' launchers allocate their intermediate
+ * buffers before the launch ("Kernel experiments", Test 23: the quantised
+ * fragments and, when K is split, the fp32 partial buffer [split][M][N]).
  * entry: BPW_PATH_GEMV or BPW_PATH_GEMM. Host only.
  */
 int bpw_workspace_size(const bpw_weights* w, int64_t m, int x_dtype, int entry, size_t* bytes);
 
 /*
- * y = x @ W^T, decode-shaped (tuned for M <= 16; any M >= 1 accepted).
+ * y = x @ W^T, decode-shaped (tuned for M <= 16; any M >= 1 accepted): the
+ * pages' GEMV, with W the dequantised weight of the prepared planes
+ * ("Kernel experiments", Test 6: per 128-group an exact integer dot of int8
+ * activations with the ternary values, folded with the activation and weight
+ * scales; the mate PR: int4 codes minus zero points times the group scale,
+ * against fp16/bf16 activations, with act order).
  * Supported (fmt, x_dtype): TERNARY2 x I8 (x_scale device fp32 [M] required),
  * TERNARY2 x I8G (x_scale device fp32 [M][K/128]; M <= 32, larger M and the
  * GEMM entry return BPW_EUNSUPPORTED), INT4_SYM / INT4_ZP x F16 or BF16
@@ -299,7 +318,9 @@ int bpw_partials(const bpw_weights* w, const int8_t* q, int64_t m, int path, int
                  size_t workspace_bytes, void* stream);
 
 /*
- * Memory-system probe used to calibrate byte counters: BPW_PROBE_READ reads
+ * Memory-system probe ("Kernel experiments", Test 24: bandwidth probes that
+ * only load, to separate the access pattern from the arithmetic), used to
+ * calibrate byte counters and as the streaming ceiling: BPW_PROBE_READ reads
  * `bytes` from src (device, 16-byte aligned, bytes % 16 == 0) and writes one
  * uint32 per workgroup into dst (device, at least bpw_probe_blocks(bytes) * 4
  * bytes); BPW_PROBE_COPY copies `bytes` from src to dst.

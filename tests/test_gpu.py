@@ -398,6 +398,21 @@ def test_workload_w4a16_prefill_sampled():
     assert_close(host(y)[np.ix_(rows, cols)], y_ref, "bf16", "w4a16_prefill sampled")
 
 
+def test_workload_w4a16_prefill_full():
+    """Every output of the 4-bit prefill workload (M=2048, K=4096, N=14336) against the
+    fp64 oracle (bf16-rounded dequantised weights, then a dgemm)."""
+    w = synth.w4a16_prefill()
+    pw = prepare(w)
+    y = bpw.gemm_packed(pw, to_dev(w.x, "bf16"))
+    torch.cuda.synchronize()
+    yh = host(y)
+    del y
+    wt = reference.weights_int4_rounded(w.codes, w.scales_f64(), None, None, "bf16")
+    y_ref = reference.product(w.x_f32(), wt)
+    del wt
+    assert_close(yh, y_ref, "bf16", "w4a16_prefill full")
+
+
 def test_workload_ternary_prefill_sampled():
     w = synth.ternary_prefill()
     pw = bpw.prepare_packed(bpw.TERNARY2, w.codes, w.scales, device=DEV)
@@ -414,7 +429,7 @@ def test_workload_ternary_prefill_sampled():
     assert_close(host(y)[np.ix_(rows, cols)], y_ref, "f16", "ternary_int8_prefill sampled")
     # int32 group partials on corner and random windows, through the GEMM core
     wins = [(0, 64, 0, 256), (w.m - 64, w.m, w.n - 256, w.n), (0, 64, w.n - 256, w.n), (w.m - 64, w.m, 0, 256)]
-    for _ in range(2):
+    for _ in range(4):                                    # four random windows beside the corners
         a, b = int(rng.integers(0, w.m - 64)), int(rng.integers(0, w.n - 256))
         wins.append((a, a + 64, b, b + 256))
     for (m0, m1, n0, n1) in wins:
