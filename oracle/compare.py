@@ -8,6 +8,12 @@ last place of the output dtype at the reference value:
 
     |y - y_ref| <= 1e-3 * max(|y_ref|, tau) + ulp_out(y_ref) / 2,
     tau = 1e-3 * rms(y_ref).
+
+Outputs accumulated in fp32 over K products carry a rounding error that scales
+with the sum of the products' magnitudes, not with the result: where the
+products cancel (|y_ref| far below tau) no fp32 accumulation meets the floor
+above. When the caller passes abs_sum = sum_k |x_k * w_k| for each output (and
+K), the bound gains the usual estimate of that error, sqrt(K) * 2**-24 * abs_sum.
 """
 from __future__ import annotations
 
@@ -31,7 +37,10 @@ def ulp(v: np.ndarray, dtype: str) -> np.ndarray:
     return np.ldexp(1.0, e - (SIG_BITS[dtype] - 1))
 
 
-def compare(y, y_ref, dtype: str, rel: float = 1e-3) -> dict:
+U32 = 2.0 ** -24            # fp32 unit roundoff
+
+
+def compare(y, y_ref, dtype: str, rel: float = 1e-3, abs_sum=None, k: int = 0) -> dict:
     y = np.asarray(y, np.float64)
     y_ref = np.asarray(y_ref, np.float64)
     if y.shape != y_ref.shape:
@@ -40,6 +49,11 @@ def compare(y, y_ref, dtype: str, rel: float = 1e-3) -> dict:
     tau = rel * rms
     err = np.abs(y - y_ref)
     bound = rel * np.maximum(np.abs(y_ref), tau) + 0.5 * ulp(y_ref, dtype)
+    if abs_sum is not None:
+        abs_sum = np.asarray(abs_sum, np.float64)
+        if abs_sum.shape != y_ref.shape or k < 1:
+            raise ValueError("abs_sum must match y_ref's shape and k must be >= 1")
+        bound = bound + np.sqrt(k) * U32 * abs_sum
     finite = bool(np.all(np.isfinite(y)))
     denom = np.maximum(np.abs(y_ref), tau if tau > 0 else 1e-300)
     return {

@@ -102,3 +102,20 @@ def test_compare_reports_worst_ratio():
     bound = 1e-3 * 4.0 + 0.5 * compare.ulp(4.0, "f32")
     r = compare.compare([4.0 + 0.5 * bound], [4.0], "f32")
     assert r["ok"] and abs(r["worst_ratio"] - 0.5) < 1e-9
+
+
+def test_compare_fp32_accumulation_term():
+    # y_ref = [1, 0]: at the zero entry the bound is 1e-3 * tau + 2**-25 (f16) without
+    # the term; with abs_sum = 100 and K = 4096 it gains sqrt(4096) * 2**-24 * 100.
+    tau = 1e-3 * np.sqrt(0.5)
+    b0 = 1e-3 * tau + 2.0 ** -25
+    extra = 64.0 * 2.0 ** -24 * 100.0
+    y_ref = [1.0, 0.0]
+    assert not compare.compare([1.0, 1.5 * b0], y_ref, "f16")["ok"]
+    assert compare.compare([1.0, 0.99 * (b0 + extra)], y_ref, "f16", abs_sum=[1.0, 100.0], k=4096)["ok"]
+    assert not compare.compare([1.0, 1.01 * (b0 + extra)], y_ref, "f16", abs_sum=[1.0, 100.0], k=4096)["ok"]
+    # the term scales with sqrt(K) and with abs_sum, entry by entry
+    assert not compare.compare([1.0, 0.99 * (b0 + extra)], y_ref, "f16", abs_sum=[1.0, 100.0], k=1024)["ok"]
+    assert not compare.compare([1.0, 0.99 * (b0 + extra)], y_ref, "f16", abs_sum=[100.0, 1.0], k=4096)["ok"]
+    with pytest.raises(ValueError):
+        compare.compare([1.0], [1.0], "f16", abs_sum=[1.0, 2.0], k=4)

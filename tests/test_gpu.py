@@ -44,7 +44,7 @@ def prepare(w: synth.Workload):
 
 # ------------------------------------------------------------------ quantiser
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
-@pytest.mark.parametrize("m,k", [(1, 512), (5, 4096), (3, 1000), (64, 8192)])
+@pytest.mark.parametrize("m,k", [(1, 512), (5, 4096), (3, 1000), (64, 8192), (2, 1002), (2, 20480), (1, 14336)])
 def test_quantize_rows_bit_exact(dtype, m, k):
     rng = np.random.default_rng(m * 7 + k)
     x = (rng.standard_normal((m, k)) * rng.uniform(0.01, 50, size=(m, 1))).astype(np.float32)
@@ -408,9 +408,17 @@ def test_workload_w4a16_prefill_full():
     yh = host(y)
     del y
     wt = reference.weights_int4_rounded(w.codes, w.scales_f64(), None, None, "bf16")
-    y_ref = reference.product(w.x_f32(), wt)
+    xf = w.x_f32()
+    y_ref = reference.product(xf, wt)
+    # sum_k |x w| per output: the scale of the fp32 accumulation error (near-zero
+    # outputs cancel; the plain rule's floor is below one fp32 rounding there)
+    abs_sum = reference.product(np.abs(xf), np.abs(wt))
     del wt
-    assert_close(yh, y_ref, "bf16", "w4a16_prefill full")
+    r = compare.compare(yh, y_ref, "bf16", abs_sum=abs_sum, k=w.k)
+    assert r["ok"], f"w4a16_prefill full: {r}"
+    # without the accumulation term the rule holds for all but a handful of near-zero outputs
+    plain = compare.compare(yh, y_ref, "bf16")
+    assert plain["worst_ratio"] < 2.0 and plain["rel_rms"] < 2.5e-3, plain
 
 
 def test_workload_ternary_prefill_sampled():
