@@ -86,6 +86,107 @@ __global__ __launch_bounds__(kQThreads) void quantize_rows_kernel(const T* __res
   if (threadIdx.x == 0) x_scale[row] = scale;
 }
 
+// Max over the 64 lanes of a wave (exact in any order): DPP steps within each
+// 16-lane row, then the four row maxima read into scalars.
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false)));
+  const int vi = __builtin_bit_cast(int, v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(vi, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(vi, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(vi, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(vi, 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+__device__ __forceinline__ void ld4(const float* p, float (&v)[4]) {
+  const v4f t = *reinterpret_cast<const v4f*>(p);
+  v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+}
+__device__ __forceinline__ void ld4(const __half* p, float (&v)[4]) {
+  const v2u t = *reinterpret_cast<const v2u*>(p);
+  v[0] = __half2float(__builtin_bit_cast(__half, static_cast<uint16_t>(t.x)));
+  v[1] = __half2float(__builtin_bit_cast(__half, static_cast<uint16_t>(t.x >> 16)));
+  v[2] = __half2float(__builtin_bit_cast(__half, static_cast<uint16_t>(t.y)));
+  v[3] = __half2float(__builtin_bit_cast(__half, static_cast<uint16_t>(t.y >> 16)));
+}
+__device__ __forceinline__ void ld4(const uint16_t* p, float (&v)[4]) {
+  const v2u t = *reinterpret_cast<const v2u*>(p);
+  v[0] = __uint_as_float(t.x << 16);
+  v[1] = __uint_as_float(t.x & 0xFFFF0000u);
+  v[2] = __uint_as_float(t.y << 16);
+  v[3] = __uint_as_float(t.y & 0xFFFF0000u);
+}
+
+// The row quantiser for rows whose K is a multiple of 4 with 4-element-aligned
+// vector access: one workgroup of 1024 threads per row, thread t holding the
+// 4 elements at 4t + 4096 j (j < V4), so a 4096-column row is one 16-byte (fp32)
+// or 8-byte (16-bit) load per thread. The row max is a DPP reduction in each
+// wave and a max over the 16 wave maxima through LDS (exact in any order); the
+// rule and the non-finite handling are those of quantize_rows_kernel, and each
+// thread stores its 4 codes as one 32-bit word.
+template <typename T, int V4>
+__global__ __launch_bounds__(1024) void quantize_rows_vec_kernel(const T* __restrict__ x, int64_t k,
+                                                                 int8_t* __restrict__ q,
+                                                                 float* __restrict__ x_scale) {
+  __shared__ float wmax[16];
+  const int64_t row = blockIdx.x;
+  const T* xr = x + row * k;
+  int8_t* qr = q + row * k;
+  const int tid = threadIdx.x;
+  float v[V4][4];
+  float amax = 0.0f, nonfinite = 0.0f;
+#pragma unroll
+  for (int j = 0; j < V4; ++j) {
+    const int64_t i = 4 * static_cast<int64_t>(tid) + 4096 * j;
+    if (i < k) {
+      ld4(xr + i, v[j]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[j][e] = 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      amax = fmaxf(amax, fabsf(v[j][e]));
+      nonfinite = fmaf(v[j][e], 0.0f, nonfinite);
+    }
+  }
+  if (nonfinite != nonfinite) amax = __builtin_inff();
+  amax = wave_max(amax);
+  if ((tid & 63) == 0) wmax[tid >> 6] = amax;
+  __syncthreads();
+  amax = wmax[0];
+#pragma unroll
+  for (int w = 1; w < 16; ++w) amax = fmaxf(amax, wmax[w]);
+  if (__builtin_isinf(amax)) {                      // the whole workgroup takes this branch
+#pragma unroll
+    for (int j = 0; j < V4; ++j) {
+      const int64_t i = 4 * static_cast<int64_t>(tid) + 4096 * j;
+      if (i < k) *reinterpret_cast<uint32_t*>(qr + i) = 0u;
+    }
+    if (tid == 0) x_scale[row] = __builtin_nanf("");
+    return;
+  }
+  const float scale = amax * (1.0f / 127.0f);      // fp32 reciprocal constant, one rounding
+  const float div = scale > 0.0f ? scale : 1.0f;
+#pragma unroll
+  for (int j = 0; j < V4; ++j) {
+    const int64_t i = 4 * static_cast<int64_t>(tid) + 4096 * j;
+    if (i < k) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float r = fminf(fmaxf(rintf(v[j][e] / div), -127.0f), 127.0f);   // IEEE division, ties to even
+        word |= (static_cast<uint32_t>(static_cast<int>(r)) & 0xFFu) << (8 * e);
+      }
+      *reinterpret_cast<uint32_t*>(qr + i) = word;
+    }
+  }
+  if (tid == 0) x_scale[row] = scale;
+}
+
 // One wave per (row, 128-group) unit, the same rule with the group's own max:
 // unit u covers x[128u, 128u + 128) because rows are K = 128 G long, and its
 // scale goes to x_scale[u] ([M][G] row-major). Two values per lane.
@@ -318,6 +419,19 @@ int grid_for(int64_t items, int per_block) {
 
 template <typename T>
 void quantize_go(const void* x, int64_t m, int64_t k, int8_t* q, float* x_scale, hipStream_t s) {
+  const size_t va = sizeof(T) * 4;                 // one thread's 4 elements: 16 (fp32) or 8 bytes
+  if (k % 4 == 0 && k <= 4 * 4096 && reinterpret_cast<uintptr_t>(x) % va == 0 &&
+      reinterpret_cast<uintptr_t>(q) % 4 == 0) {
+    const T* xt = static_cast<const T*>(x);
+    const dim3 g(static_cast<unsigned>(m));
+    switch ((k + 4095) / 4096) {
+      case 1: quantize_rows_vec_kernel<T, 1><<<g, 1024, 0, s>>>(xt, k, q, x_scale); break;
+      case 2: quantize_rows_vec_kernel<T, 2><<<g, 1024, 0, s>>>(xt, k, q, x_scale); break;
+      case 3: quantize_rows_vec_kernel<T, 3><<<g, 1024, 0, s>>>(xt, k, q, x_scale); break;
+      default: quantize_rows_vec_kernel<T, 4><<<g, 1024, 0, s>>>(xt, k, q, x_scale); break;
+    }
+    return;
+  }
   dim3 grid(static_cast<unsigned>(m)), block(kQThreads);
   if (k <= 32 * kQThreads)
     quantize_rows_kernel<T, true><<<grid, block, 0, s>>>(static_cast<const T*>(x), k, q, x_scale);
