@@ -40,6 +40,15 @@ __device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t 
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
+// (v & mask) | bits in one v_and_or_b32. The mask goes in an SGPR (gfx9 VOP3
+// encodings take no literal), bits in a VGPR: the compiler otherwise emits a
+// separate AND and OR, each with its literal.
+__device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t mask, uint32_t bits) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(v), "s"(mask), "v"(bits));
+  return r;
+}
+
 // 4x4 byte transpose: out_t = [i0.byte t, i1.byte t, i2.byte t, i3.byte t].
 __device__ __forceinline__ void transpose4x4(uint32_t i0, uint32_t i1, uint32_t i2, uint32_t i3,
                                              uint32_t& o0, uint32_t& o1, uint32_t& o2,

@@ -789,38 +789,124 @@ __global__ __launch_bounds__(512) void gemv_w4_skinny_kernel(
 // values code - zero (magic 1024 trick) and v_dot2_f32_f16 accumulates;
 // bf16: codes and activations go through exact fp32 values and the zero point
 // is applied as zero * sum(x). The group scale multiplies the fp32 partial.
-template <int R, int CH, bool BF, bool ZP, typename TOut>
-__global__ __launch_bounds__(256) void gemv_w4_row_kernel(
+//
+// PERM (act order, the mate PR's "Act order" section: the activation is
+// gathered with the permutation that sorted K by group): the gather runs
+// inside this kernel. A workgroup loads x and the permutation first, then
+// its scales and code stream; while the codes are in flight it
+// stages x in LDS, writes x[perm[k']] to a second LDS array and every lane
+// reads its activations from there. The barriers wait on LDS traffic only
+// (the code loads, issued later, stay in flight across them).
+constexpr int kRowW4PermWaves = 4;
+
+template <int R, int CH, bool BF, bool ZP, typename TOut, bool PERM>
+__global__ __launch_bounds__(PERM ? 64 * kRowW4PermWaves : 256) void gemv_w4_row_kernel(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ wscale,
-    const uint8_t* __restrict__ zeros, const uint16_t* __restrict__ x, int N, int K,
-    TOut* __restrict__ y) {
-  const int lane = threadIdx.x & 63;
-  const int row0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * R;
-  if (row0 >= N) return;                        // whole wave; this kernel has no barriers
+    const uint8_t* __restrict__ zeros, const uint16_t* __restrict__ x, const int32_t* __restrict__ perm,
+    int N, int K, TOut* __restrict__ y) {
+  constexpr int NW = PERM ? kRowW4PermWaves : 4;
+  extern __shared__ __align__(16) uint16_t xstage[];      // PERM: [K] x, then [K] x[perm]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int row0 = (blockIdx.x * NW + (tid >> 6)) * R;
+  if (!PERM && row0 >= N) return;               // whole wave (without PERM the kernel has no barriers)
   const int KB = K >> 1, G = K >> 7, ZB = (G + 1) >> 1;
+  // Activations of this lane: x[1024c + 16 lane + e], e = 0..15 (PERM: read
+  // from LDS after the gather; the staging loads come first).
+  v4u xv[CH][2];
+  // 16-byte chunks per thread of x (K / 8 of them) and of the permutation (K / 4)
+  constexpr int XPT = PERM ? (CH * 128 + 64 * NW - 1) / (64 * NW) : 1;
+  constexpr int PPT = PERM ? (CH * 256 + 64 * NW - 1) / (64 * NW) : 1;
+  v4u xin[XPT];
+  v4i pin[PPT];
+  if (PERM) {
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int idx = tid + i * 64 * NW;
+      xin[i] = idx < (K >> 3) ? reinterpret_cast<const v4u*>(x)[idx] : v4u{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int idx = tid + i * 64 * NW;
+      pin[i] = idx < (K >> 2) ? reinterpret_cast<const v4i*>(perm)[idx] : v4i{0, 0, 0, 0};
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const v4u* src = reinterpret_cast<const v4u*>(x + c * 1024 + lane * 16);
+      xv[c][0] = src[0];
+      xv[c][1] = src[1];
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
   v2u cw[R][CH];
-  float sv[R][CH];
-  int zv[R][CH];
+  // A row's scales (G <= 64) and zero bytes in one load each: lane l holds
+  // those of group l (byte l); each lane takes its own from there.
+  int sall[R], zall[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const size_t row = static_cast<size_t>(min(row0 + r, N - 1));
+    sall[r] = wscale[row * G + min(lane, G - 1)];
+    zall[r] = ZP ? zeros[row * ZB + min(lane, ZB - 1)] : 0;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // the code stream, in the order it is consumed
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const size_t row = static_cast<size_t>(min(row0 + r, N - 1));
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       cw[r][c] = load_stream<v2u>(codes + row * KB + c * 512 + lane * 8);
-      const int g = 8 * c + (lane >> 3);
-      const uint16_t sb = wscale[row * G + g];
-      sv[r][c] = BF ? bf16_to_f32(sb) : __half2float(__builtin_bit_cast(__half, sb));
-      zv[r][c] = ZP ? ((zeros[row * ZB + (g >> 1)] >> (4 * (g & 1))) & 15) : 8;
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
-  // Activations of this lane: x[1024c + 16 lane + e], e = 0..15.
-  v4u xv[CH][2];
+  if (PERM) {
+    uint16_t* xr = xstage;
+    uint16_t* xg = xstage + K;
 #pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    const v4u* src = reinterpret_cast<const v4u*>(x + c * 1024 + lane * 16);
-    xv[c][0] = src[0];
-    xv[c][1] = src[1];
+    for (int i = 0; i < XPT; ++i) {
+      const int idx = tid + i * 64 * NW;
+      if (idx < (K >> 3)) reinterpret_cast<v4u*>(xr)[idx] = xin[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int idx = tid + i * 64 * NW;
+      if (idx < (K >> 2)) {
+        // entries outside 0..K-1 read as 0 (the prepare step stores a permutation)
+        const v4i p = pin[i];
+        const uint32_t e0 = static_cast<uint32_t>(p.x) < static_cast<uint32_t>(K) ? xr[p.x] : 0;
+        const uint32_t e1 = static_cast<uint32_t>(p.y) < static_cast<uint32_t>(K) ? xr[p.y] : 0;
+        const uint32_t e2 = static_cast<uint32_t>(p.z) < static_cast<uint32_t>(K) ? xr[p.z] : 0;
+        const uint32_t e3 = static_cast<uint32_t>(p.w) < static_cast<uint32_t>(K) ? xr[p.w] : 0;
+        reinterpret_cast<v2u*>(xg)[idx] = v2u{e0 | (e1 << 16), e2 | (e3 << 16)};
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const v4u* src = reinterpret_cast<const v4u*>(xg + c * 1024 + lane * 16);
+      xv[c][0] = src[0];
+      xv[c][1] = src[1];
+    }
+  } else {
+    // keep the activation permutes below the code loads
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      asm volatile("" : "+v"(xv[c][0]));
+      asm volatile("" : "+v"(xv[c][1]));
+    }
   }
+  float sv[R][CH];
+  int zv[R][CH];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int g = 8 * c + (lane >> 3);
+      const uint16_t sb = static_cast<uint16_t>(__shfl(sall[r], g));
+      sv[r][c] = BF ? bf16_to_f32(sb) : __half2float(__builtin_bit_cast(__half, sb));
+      zv[r][c] = ZP ? ((__shfl(zall[r], g >> 1) >> (4 * (g & 1))) & 15) : 8;
+    }
   float acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = 0.0f;
@@ -838,21 +924,33 @@ __global__ __launch_bounds__(256) void gemv_w4_row_kernel(
         xp[c][4 * d + 3] = __builtin_bit_cast(h2, perm_b32(v.w, v.y, 0x07060302u));
       }
     }
+    // Code pairs (s, s + 4) of a packed dword as exact fp16 code - zero: the
+    // low nibble of a byte under the exponent of 1024 (0x6400 | c = 1024 + c),
+    // the high nibble, left in place, under the exponent of 64
+    // (0x5400 | c << 4 = 64 + c); subtracting 1024 + z or 64 + z leaves c - z.
+    const uint32_t m1024 = 0x64006400u, m64 = 0x54005400u;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
-        const uint32_t mz = 0xE400u | static_cast<uint32_t>(zv[r][c]);   // fp16 -(1024 + z)
-        const h2 nz = __builtin_bit_cast(h2, mz | (mz << 16));
+        const uint32_t z = static_cast<uint32_t>(zv[r][c]);
+        const uint32_t n1024 = 0xE400u | z, n64 = 0xD400u | (z << 4);   // fp16 -(1024 + z), -(64 + z)
+        const h2 nz1024 = __builtin_bit_cast(h2, n1024 | (n1024 << 16));
+        const h2 nz64 = __builtin_bit_cast(h2, n64 | (n64 << 16));
         const uint32_t wv[2] = {cw[r][c].x, cw[r][c].y};
         float p = 0.0f;
 #pragma unroll
-        for (int d = 0; d < 2; ++d)
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const h2 cz = __builtin_bit_cast(h2, ((wv[d] >> (4 * s)) & 0x000F000Fu) | 0x64006400u) + nz;
-            p = __builtin_amdgcn_fdot2(cz, xp[c][4 * d + s], p, false);
-          }
+        for (int d = 0; d < 2; ++d) {
+          const uint32_t w8 = wv[d] >> 8;
+          const h2 c0 = __builtin_bit_cast(h2, and_or(wv[d], 0x000F000Fu, m1024)) + nz1024;   // codes 0, 4
+          const h2 c1 = __builtin_bit_cast(h2, and_or(wv[d], 0x00F000F0u, m64)) + nz64;      // codes 1, 5
+          const h2 c2 = __builtin_bit_cast(h2, and_or(w8, 0x000F000Fu, m1024)) + nz1024;     // codes 2, 6
+          const h2 c3 = __builtin_bit_cast(h2, and_or(w8, 0x00F000F0u, m64)) + nz64;         // codes 3, 7
+          p = __builtin_amdgcn_fdot2(c0, xp[c][4 * d + 0], p, false);
+          p = __builtin_amdgcn_fdot2(c1, xp[c][4 * d + 1], p, false);
+          p = __builtin_amdgcn_fdot2(c2, xp[c][4 * d + 2], p, false);
+          p = __builtin_amdgcn_fdot2(c3, xp[c][4 * d + 3], p, false);
+        }
         acc[r] = fmaf(sv[r][c], p, acc[r]);
       }
     }
@@ -1173,9 +1271,36 @@ hipError_t w4_skinny(const bpw_weights& w, const uint16_t* x, int m, TOut* y, hi
 template <int CH, bool BF, bool ZP, typename TOut>
 void w4_row_go(const bpw_weights& w, const uint16_t* x, TOut* y, hipStream_t s) {
   const int n = static_cast<int>(w.n), k = static_cast<int>(w.k);
-  gemv_w4_row_kernel<kRowW4, CH, BF, ZP, TOut><<<row_blocks(n, kRowW4), 256, 0, s>>>(
+  gemv_w4_row_kernel<kRowW4, CH, BF, ZP, TOut, false><<<row_blocks(n, kRowW4), 256, 0, s>>>(
       static_cast<const uint8_t*>(w.codes), static_cast<const uint16_t*>(w.scales),
-      static_cast<const uint8_t*>(w.zeros), x, n, k, y);
+      static_cast<const uint8_t*>(w.zeros), x, nullptr, n, k, y);
+}
+
+// Act order at M = 1: x in its original column order and the permutation go
+// to the kernel, which gathers in LDS (2 * K halfwords).
+template <int CH, bool BF, bool ZP, typename TOut>
+void w4_row_perm_go(const bpw_weights& w, const uint16_t* x, TOut* y, hipStream_t s) {
+  const int n = static_cast<int>(w.n), k = static_cast<int>(w.k);
+  constexpr int rows = kRowW4 * kRowW4PermWaves;
+  gemv_w4_row_kernel<kRowW4, CH, BF, ZP, TOut, true>
+      <<<(n + rows - 1) / rows, 64 * kRowW4PermWaves, 4ull * k, s>>>(
+          static_cast<const uint8_t*>(w.codes), static_cast<const uint16_t*>(w.scales),
+          static_cast<const uint8_t*>(w.zeros), x, w.perm, n, k, y);
+}
+
+template <bool BF, bool ZP, typename TOut>
+hipError_t w4_perm_dispatch_f(const bpw_weights& w, const uint16_t* x, TOut* y, hipStream_t s) {
+  switch (w.k / 1024) {
+    case 1: w4_row_perm_go<1, BF, ZP>(w, x, y, s); break;
+    case 2: w4_row_perm_go<2, BF, ZP>(w, x, y, s); break;
+    case 3: w4_row_perm_go<3, BF, ZP>(w, x, y, s); break;
+    case 4: w4_row_perm_go<4, BF, ZP>(w, x, y, s); break;
+    case 5: w4_row_perm_go<5, BF, ZP>(w, x, y, s); break;
+    case 6: w4_row_perm_go<6, BF, ZP>(w, x, y, s); break;
+    case 7: w4_row_perm_go<7, BF, ZP>(w, x, y, s); break;
+    default: w4_row_perm_go<8, BF, ZP>(w, x, y, s); break;
+  }
+  return hipGetLastError();
 }
 
 template <bool BF, bool ZP, typename TOut>
@@ -1253,6 +1378,29 @@ hipError_t launch_gemv_t2_partials(const bpw_weights& w, const int8_t* q, int64_
     return t2_long<float, true>(w, q, nullptr, mi, static_cast<float*>(nullptr), out, static_cast<int>(m0),
                                 static_cast<int>(m1), static_cast<int>(n0), static_cast<int>(n1), s);
   return hipErrorInvalidValue;
+}
+
+bool gemv_w4_perm_fits(const bpw_weights& w, int64_t m, const void* x) {
+  return w.perm != nullptr && w4_row_ok(m, w.k) && reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
+         reinterpret_cast<uintptr_t>(w.perm) % 16 == 0;
+}
+
+hipError_t launch_gemv_w4_perm(const bpw_weights& w, const void* x, int x_dtype, void* y, int y_dtype,
+                               hipStream_t s) {
+  const uint16_t* xh = static_cast<const uint16_t*>(x);
+  const bool bf = x_dtype == BPW_BF16, zp = w.fmt == BPW_INT4_ZP;
+#define BPW_W4P(TOut_)                                                                           \
+  {                                                                                              \
+    TOut_* yo = static_cast<TOut_*>(y);                                                          \
+    if (bf) return zp ? w4_perm_dispatch_f<true, true>(w, xh, yo, s) : w4_perm_dispatch_f<true, false>(w, xh, yo, s); \
+    return zp ? w4_perm_dispatch_f<false, true>(w, xh, yo, s) : w4_perm_dispatch_f<false, false>(w, xh, yo, s);       \
+  }
+  switch (y_dtype) {
+    case BPW_F32: BPW_W4P(float)
+    case BPW_F16: BPW_W4P(__half)
+    default: BPW_W4P(uint16_t)
+  }
+#undef BPW_W4P
 }
 
 hipError_t launch_gemv_w4(const bpw_weights& w, const void* x_sorted, int x_dtype, int64_t m,

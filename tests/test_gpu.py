@@ -5,6 +5,8 @@ Each case names its workload, shape and seed in the test id. Integer results
 outputs must satisfy oracle.compare's rule (1e-3 relative plus half an output
 ulp). Inputs come from synth; both sides compute from them independently.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -253,7 +255,7 @@ def w4_reference(w: synth.Workload, rounded: bool):
 @pytest.mark.parametrize("fmt,x_dtype,act_order", [("int4_zp", "f16", True), ("int4_zp", "f16", False),
                                                    ("int4_sym", "bf16", False), ("int4_sym", "f16", False),
                                                    ("int4_zp", "bf16", True)])
-@pytest.mark.parametrize("m,k,n", [(1, 640, 333), (1, 2048, 301), (1, 8192, 66), (3, 128, 64), (8, 5120, 200),
+@pytest.mark.parametrize("m,k,n", [(1, 640, 333), (1, 2048, 301), (1, 8192, 66), (1, 3072, 13), (3, 128, 64), (8, 5120, 200),
                                    (16, 1024, 97), (32, 256, 130),
                                    # streaming skinny kernel: 16..48 groups, 4..6 per wave, ragged waves and tiles
                                    (2, 2048, 1000), (16, 6144, 777), (5, 4224, 3000), (12, 2560, 9000)])
@@ -263,6 +265,28 @@ def test_gemv_w4_parity(fmt, x_dtype, act_order, m, k, n):
     y = bpw.gemv_packed(pw, to_dev(w.x, x_dtype))
     torch.cuda.synchronize()
     assert_close(host(y), w4_reference(w, rounded=False), x_dtype, f"gemv {fmt} {x_dtype} m={m} k={k} n={n}")
+
+
+# Act order at M = 1 gathers inside the GEMV when the permutation plane is
+# 16-byte aligned; a plane that is only 4-byte aligned (what the boundary
+# requires) takes the separate gather launch. Both must give the same bits.
+@pytest.mark.parametrize("x_dtype", ["f16", "bf16"])
+def test_w4_act_order_fused_and_separate_gather_agree(x_dtype):
+    m, k, n = 1, 5120, 700
+    w = w4_case("int4_zp", m, k, n, 77, True, x_dtype)
+    pw = prepare(w)
+    x = to_dev(w.x, x_dtype)
+    pbig = torch.zeros(k + 1, dtype=torch.int32, device=DEV)
+    pbig[1:] = pw.perm
+    pw_off = dataclasses.replace(pw, perm=pbig[1:])
+    assert pw_off.perm.data_ptr() % 16 == 4
+    ws = torch.empty(bpw.workspace_size(pw, m, bpw.F16 if x_dtype == "f16" else bpw.BF16, bpw.PATH_GEMV),
+                     dtype=torch.uint8, device=DEV)
+    y_fused = bpw.gemv_packed(pw, x, workspace=ws)
+    y_sep = bpw.gemv_packed(pw_off, x, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y_fused.view(torch.int16), y_sep.view(torch.int16))
+    assert_close(host(y_fused), w4_reference(w, rounded=False), x_dtype, f"fused act-order gather {x_dtype}")
 
 
 # Bit-identical repeats, outputs of one token row independent of the other
