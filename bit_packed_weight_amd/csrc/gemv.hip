@@ -798,6 +798,7 @@ __global__ __launch_bounds__(512) void gemv_w4_skinny_kernel(
 // reads its activations from there. The barriers wait on LDS traffic only
 // (the code loads, issued later, stay in flight across them).
 constexpr int kRowW4PermWaves = 4;
+constexpr int kRowW4Perm = 2;                 // rows per wave (4 spill into two waves per SIMD)
 
 template <int R, int CH, bool BF, bool ZP, typename TOut, bool PERM>
 __global__ __launch_bounds__(PERM ? 64 * kRowW4PermWaves : 256) void gemv_w4_row_kernel(
@@ -813,21 +814,21 @@ __global__ __launch_bounds__(PERM ? 64 * kRowW4PermWaves : 256) void gemv_w4_row
   // Activations of this lane: x[1024c + 16 lane + e], e = 0..15 (PERM: read
   // from LDS after the gather; the staging loads come first).
   v4u xv[CH][2];
-  // 16-byte chunks per thread of x (K / 8 of them) and of the permutation (K / 4)
-  constexpr int XPT = PERM ? (CH * 128 + 64 * NW - 1) / (64 * NW) : 1;
-  constexpr int PPT = PERM ? (CH * 256 + 64 * NW - 1) / (64 * NW) : 1;
+  // PERM: 16-byte chunks per thread of x (K / 8 of them) and 32-byte chunks
+  // of the permutation (K / 8); here K = 1024 * CH exactly.
+  constexpr int NX = CH * 128;
+  constexpr int XPT = PERM ? (NX + 64 * NW - 1) / (64 * NW) : 1;
   v4u xin[XPT];
-  v4i pin[PPT];
+  v4i pin[XPT][2];
   if (PERM) {
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
       const int idx = tid + i * 64 * NW;
-      xin[i] = idx < (K >> 3) ? reinterpret_cast<const v4u*>(x)[idx] : v4u{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int idx = tid + i * 64 * NW;
-      pin[i] = idx < (K >> 2) ? reinterpret_cast<const v4i*>(perm)[idx] : v4i{0, 0, 0, 0};
+      if (i + 1 < XPT || NX % (64 * NW) == 0 || idx < NX) {
+        xin[i] = reinterpret_cast<const v4u*>(x)[idx];
+        pin[i][0] = reinterpret_cast<const v4i*>(perm)[2 * idx];
+        pin[i][1] = reinterpret_cast<const v4i*>(perm)[2 * idx + 1];
+      }
     }
   } else {
 #pragma unroll
@@ -839,14 +840,16 @@ __global__ __launch_bounds__(PERM ? 64 * kRowW4PermWaves : 256) void gemv_w4_row
   }
   __builtin_amdgcn_sched_barrier(0);
   v2u cw[R][CH];
-  // A row's scales (G <= 64) and zero bytes in one load each: lane l holds
-  // those of group l (byte l); each lane takes its own from there.
+  // A row's scales and zero points (G <= 64) in one load each: lane l reads
+  // those of group l (its zero-point byte holds groups l and l ^ 1); each
+  // lane later takes its own groups' values from there by lane shuffles.
   int sall[R], zall[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const size_t row = static_cast<size_t>(min(row0 + r, N - 1));
-    sall[r] = wscale[row * G + min(lane, G - 1)];
-    zall[r] = ZP ? zeros[row * ZB + min(lane, ZB - 1)] : 0;
+    const int gl = min(lane, G - 1);
+    sall[r] = wscale[row * G + gl];
+    zall[r] = ZP ? zeros[row * ZB + (gl >> 1)] : 0;
   }
   __builtin_amdgcn_sched_barrier(0);
   // the code stream, in the order it is consumed
@@ -865,20 +868,25 @@ __global__ __launch_bounds__(PERM ? 64 * kRowW4PermWaves : 256) void gemv_w4_row
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
       const int idx = tid + i * 64 * NW;
-      if (idx < (K >> 3)) reinterpret_cast<v4u*>(xr)[idx] = xin[i];
+      if (i + 1 < XPT || NX % (64 * NW) == 0 || idx < NX) reinterpret_cast<v4u*>(xr)[idx] = xin[i];
     }
     __syncthreads();
+    // x[perm[k']] for 8 consecutive k', written in the pair order of the
+    // decode below: (x_s, x_{s+4}) for s = 0..3 of each 8.
 #pragma unroll
-    for (int i = 0; i < PPT; ++i) {
+    for (int i = 0; i < XPT; ++i) {
       const int idx = tid + i * 64 * NW;
-      if (idx < (K >> 2)) {
-        // entries outside 0..K-1 read as 0 (the prepare step stores a permutation)
-        const v4i p = pin[i];
-        const uint32_t e0 = static_cast<uint32_t>(p.x) < static_cast<uint32_t>(K) ? xr[p.x] : 0;
-        const uint32_t e1 = static_cast<uint32_t>(p.y) < static_cast<uint32_t>(K) ? xr[p.y] : 0;
-        const uint32_t e2 = static_cast<uint32_t>(p.z) < static_cast<uint32_t>(K) ? xr[p.z] : 0;
-        const uint32_t e3 = static_cast<uint32_t>(p.w) < static_cast<uint32_t>(K) ? xr[p.w] : 0;
-        reinterpret_cast<v2u*>(xg)[idx] = v2u{e0 | (e1 << 16), e2 | (e3 << 16)};
+      if (i + 1 < XPT || NX % (64 * NW) == 0 || idx < NX) {
+        // an entry outside 0..K-1 reads column K - 1 (the prepare step stores a
+        // permutation; this only keeps every LDS read inside x)
+        const uint32_t km = static_cast<uint32_t>(K - 1);
+        const int pe[8] = {pin[i][0].x, pin[i][0].y, pin[i][0].z, pin[i][0].w,
+                           pin[i][1].x, pin[i][1].y, pin[i][1].z, pin[i][1].w};
+        uint32_t e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e[j] = xr[min(static_cast<uint32_t>(pe[j]), km)];
+        reinterpret_cast<v4u*>(xg)[idx] =
+            v4u{e[0] | (e[4] << 16), e[1] | (e[5] << 16), e[2] | (e[6] << 16), e[3] | (e[7] << 16)};
       }
     }
     __syncthreads();
@@ -896,32 +904,60 @@ __global__ __launch_bounds__(PERM ? 64 * kRowW4PermWaves : 256) void gemv_w4_row
       asm volatile("" : "+v"(xv[c][1]));
     }
   }
+  // Per group (lane l = group l): the fp32 scale, the zero point and, for
+  // fp16, the packed fp16 constants -(1024 + z) and -(64 + z) of the decode
+  // below; each lane then takes those of its chunk's group.
   float sv[R][CH];
   int zv[R][CH];
+  uint32_t nzl[R][CH], nzh[R][CH];
 #pragma unroll
-  for (int r = 0; r < R; ++r)
+  for (int r = 0; r < R; ++r) {
+    const uint16_t sb = static_cast<uint16_t>(sall[r]);
+    const float sf = BF ? bf16_to_f32(sb) : __half2float(__builtin_bit_cast(__half, sb));
+    const uint32_t zg = ZP ? (static_cast<uint32_t>(zall[r]) >> (4 * (lane & 1))) & 15u : 8u;
+    const uint32_t n1024 = 0xE400u | zg, n64 = 0xD400u | (zg << 4);
+    const uint32_t pl = n1024 | (n1024 << 16), ph = n64 | (n64 << 16);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int g = 8 * c + (lane >> 3);
-      const uint16_t sb = static_cast<uint16_t>(__shfl(sall[r], g));
-      sv[r][c] = BF ? bf16_to_f32(sb) : __half2float(__builtin_bit_cast(__half, sb));
-      zv[r][c] = ZP ? ((__shfl(zall[r], g >> 1) >> (4 * (g & 1))) & 15) : 8;
+      sv[r][c] = __shfl(sf, g);
+      if (BF) {
+        zv[r][c] = ZP ? __shfl(static_cast<int>(zg), g) : 8;
+      } else if (ZP) {
+        nzl[r][c] = static_cast<uint32_t>(__shfl(static_cast<int>(pl), g));
+        nzh[r][c] = static_cast<uint32_t>(__shfl(static_cast<int>(ph), g));
+      } else {
+        nzl[r][c] = pl;
+        nzh[r][c] = ph;
+      }
     }
+  }
   float acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = 0.0f;
   if (!BF) {
-    // x pairs in the order the code pairs come out: (x_s, x_{s+4}) of each 8.
+    // x pairs in the order the code pairs come out: (x_s, x_{s+4}) of each 8
+    // (PERM: the gather wrote them in that order).
     h2 xp[CH][8];
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
 #pragma unroll
       for (int d = 0; d < 2; ++d) {
         const v4u v = xv[c][d];
-        xp[c][4 * d + 0] = __builtin_bit_cast(h2, perm_b32(v.z, v.x, 0x05040100u));
-        xp[c][4 * d + 1] = __builtin_bit_cast(h2, perm_b32(v.z, v.x, 0x07060302u));
-        xp[c][4 * d + 2] = __builtin_bit_cast(h2, perm_b32(v.w, v.y, 0x05040100u));
-        xp[c][4 * d + 3] = __builtin_bit_cast(h2, perm_b32(v.w, v.y, 0x07060302u));
+        if (PERM) {
+          // (components go through named scalars: this compiler bit-casts a
+          // vector component expression such as v.y as if it were v.x)
+          const uint32_t v0 = v.x, v1 = v.y, v2 = v.z, v3 = v.w;
+          xp[c][4 * d + 0] = __builtin_bit_cast(h2, v0);
+          xp[c][4 * d + 1] = __builtin_bit_cast(h2, v1);
+          xp[c][4 * d + 2] = __builtin_bit_cast(h2, v2);
+          xp[c][4 * d + 3] = __builtin_bit_cast(h2, v3);
+        } else {
+          xp[c][4 * d + 0] = __builtin_bit_cast(h2, perm_b32(v.z, v.x, 0x05040100u));
+          xp[c][4 * d + 1] = __builtin_bit_cast(h2, perm_b32(v.z, v.x, 0x07060302u));
+          xp[c][4 * d + 2] = __builtin_bit_cast(h2, perm_b32(v.w, v.y, 0x05040100u));
+          xp[c][4 * d + 3] = __builtin_bit_cast(h2, perm_b32(v.w, v.y, 0x07060302u));
+        }
       }
     }
     // Code pairs (s, s + 4) of a packed dword as exact fp16 code - zero: the
@@ -933,10 +969,8 @@ __global__ __launch_bounds__(PERM ? 64 * kRowW4PermWaves : 256) void gemv_w4_row
     for (int r = 0; r < R; ++r) {
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
-        const uint32_t z = static_cast<uint32_t>(zv[r][c]);
-        const uint32_t n1024 = 0xE400u | z, n64 = 0xD400u | (z << 4);   // fp16 -(1024 + z), -(64 + z)
-        const h2 nz1024 = __builtin_bit_cast(h2, n1024 | (n1024 << 16));
-        const h2 nz64 = __builtin_bit_cast(h2, n64 | (n64 << 16));
+        const h2 nz1024 = __builtin_bit_cast(h2, nzl[r][c]);   // fp16 -(1024 + z), twice
+        const h2 nz64 = __builtin_bit_cast(h2, nzh[r][c]);     // fp16 -(64 + z), twice
         const uint32_t wv[2] = {cw[r][c].x, cw[r][c].y};
         float p = 0.0f;
 #pragma unroll
@@ -964,8 +998,12 @@ __global__ __launch_bounds__(PERM ? 64 * kRowW4PermWaves : 256) void gemv_w4_row
       xsum[c] = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        xf[c][2 * e] = __uint_as_float(xw[e] << 16);
-        xf[c][2 * e + 1] = __uint_as_float(xw[e] & 0xFFFF0000u);
+        // dword e = 4d + s holds elements 8d + 2s, 8d + 2s + 1 (PERM: the
+        // pair-ordered gather put 8d + s and 8d + s + 4 there)
+        const int d = e >> 2, s4 = e & 3;
+        const int lo = PERM ? 8 * d + s4 : 2 * e, hi = PERM ? 8 * d + s4 + 4 : 2 * e + 1;
+        xf[c][lo] = __uint_as_float(xw[e] << 16);
+        xf[c][hi] = __uint_as_float(xw[e] & 0xFFFF0000u);
       }
 #pragma unroll
       for (int e = 0; e < 16; ++e) xsum[c] += xf[c][e];
@@ -1281,8 +1319,8 @@ void w4_row_go(const bpw_weights& w, const uint16_t* x, TOut* y, hipStream_t s) 
 template <int CH, bool BF, bool ZP, typename TOut>
 void w4_row_perm_go(const bpw_weights& w, const uint16_t* x, TOut* y, hipStream_t s) {
   const int n = static_cast<int>(w.n), k = static_cast<int>(w.k);
-  constexpr int rows = kRowW4 * kRowW4PermWaves;
-  gemv_w4_row_kernel<kRowW4, CH, BF, ZP, TOut, true>
+  constexpr int rows = kRowW4Perm * kRowW4PermWaves;
+  gemv_w4_row_kernel<kRowW4Perm, CH, BF, ZP, TOut, true>
       <<<(n + rows - 1) / rows, 64 * kRowW4PermWaves, 4ull * k, s>>>(
           static_cast<const uint8_t*>(w.codes), static_cast<const uint16_t*>(w.scales),
           static_cast<const uint8_t*>(w.zeros), x, w.perm, n, k, y);

@@ -131,3 +131,20 @@ def test_checker_flags_a_clobbered_destination():
     body = ["ds_read_b128 a[0:3], v1", "v_accvgpr_read_b32 v9, a6", "s_waitcnt lgkmcnt(0)",
             "v_mfma_i32_32x32x32_i8 v[0:15], a[0:3], v[20:23], 0"]
     assert not writes_before_wait(body)
+
+
+def test_no_bit_cast_of_a_vector_component():
+    # The ROCm clang used here miscompiles __builtin_bit_cast applied directly
+    # to an ext_vector component (v.y, v.z, ... are read as v.x); a component
+    # must pass through a named scalar first. The kernel sources must not
+    # contain the direct form.
+    bad = []
+    pat = re.compile(r"__builtin_bit_cast\(\s*[^,()]+,\s*[A-Za-z_][\w\[\]]*\.[xyzw]\s*\)")
+    for name in sorted(os.listdir(_build.CSRC)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(_build.CSRC, name)) as f:
+                for no, line in enumerate(f, 1):
+                    if pat.search(line):
+                        bad.append(f"{name}:{no}: {line.strip()}")
+    assert not bad, "\n".join(bad)
+    assert pat.search("x = __builtin_bit_cast(h2, v.y);") and not pat.search("__builtin_bit_cast(h2, v1)")
