@@ -195,7 +195,7 @@ int run_product(bool gemv, const bpw_weights* w, const void* x, int x_dtype, con
     return hip_status(launch_gemm_t2(*w, qp, x_scale, m, y, y_dtype, s), "ternary GEMM launch");
   }
   if (gemv && gemv_w4_perm_fits(*w, m, x))
-    return hip_status(launch_gemv_w4_perm(*w, x, x_dtype, y, y_dtype, s), "4-bit act-order GEMV launch");
+    return hip_status(launch_gemv_w4_perm(*w, x, x_dtype, m, y, y_dtype, s), "4-bit act-order GEMV launch");
   const void* xs = x;
   if (w->perm) {
     uint16_t* xp = static_cast<uint16_t*>(ws);

@@ -21,6 +21,7 @@
 
 #include "device.h"
 #include "launch.h"
+#include "lds_dma.h"
 
 namespace bpw {
 namespace {
@@ -486,18 +487,32 @@ __global__ __launch_bounds__(NW * 64) void gemv_t2_long_kernel(
 
 // ---------------------------------------------------------------- 4-bit GEMV
 
-// Eight codes of one packed dword -> the B operand in the order
-// [c0, c4, c1, c5, c2, c6, c3, c7] minus the zero point, exactly, as fp16.
-__device__ __forceinline__ v8h dequant_w4_f16(uint32_t w, uint32_t neg_magic_z) {
-  const h2 nz = __builtin_bit_cast(h2, neg_magic_z);
+// The fp16 constants -(1024 + z) and -(64 + z), each twice in a dword, for a
+// zero point z in 0..15.
+__device__ __forceinline__ uint32_t w4_nz1024(uint32_t z) { return (0xE400u | z) * 0x10001u; }
+__device__ __forceinline__ uint32_t w4_nz64(uint32_t z) { return (0xD400u | (z << 4)) * 0x10001u; }
+
+// The eight codes of one packed dword (byte b: code 2b in the low nibble,
+// 2b + 1 in the high one) as four fp16 pairs (c_s - z, c_{s+4} - z), s = 0..3,
+// exactly: a low nibble under the exponent of 1024 (0x6400 | c is 1024 + c),
+// a high nibble, left in place, under the exponent of 64 (0x5400 | c << 4 is
+// 64 + c); adding -(1024 + z) or -(64 + z) leaves c - z. One shift, four
+// and-or, four packed adds.
+__device__ __forceinline__ void w4_pairs_f16(uint32_t w, uint32_t nz1024, uint32_t nz64, h2 out[4]) {
+  const uint32_t w8 = w >> 8;
+  out[0] = __builtin_bit_cast(h2, and_or(w, 0x000F000Fu, 0x64006400u)) + __builtin_bit_cast(h2, nz1024);
+  out[1] = __builtin_bit_cast(h2, and_or(w, 0x00F000F0u, 0x54005400u)) + __builtin_bit_cast(h2, nz64);
+  out[2] = __builtin_bit_cast(h2, and_or(w8, 0x000F000Fu, 0x64006400u)) + __builtin_bit_cast(h2, nz1024);
+  out[3] = __builtin_bit_cast(h2, and_or(w8, 0x00F000F0u, 0x54005400u)) + __builtin_bit_cast(h2, nz64);
+}
+
+// The same as an MFMA B operand: [c0, c4, c1, c5, c2, c6, c3, c7] - z.
+__device__ __forceinline__ v8h dequant_w4_f16(uint32_t w, uint32_t nz1024, uint32_t nz64) {
   h2 r[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    // 0x6400 | c is the fp16 value 1024 + c; adding -(1024 + z) leaves c - z exactly.
-    const uint32_t v = ((w >> (4 * s)) & 0x000F000Fu) | 0x64006400u;
-    r[s] = __builtin_bit_cast(h2, v) + nz;
-  }
-  return v8h{r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
+  w4_pairs_f16(w, nz1024, nz64, r);
+  const uint32_t r0 = __builtin_bit_cast(uint32_t, r[0]), r1 = __builtin_bit_cast(uint32_t, r[1]);
+  const uint32_t r2 = __builtin_bit_cast(uint32_t, r[2]), r3 = __builtin_bit_cast(uint32_t, r[3]);
+  return __builtin_bit_cast(v8h, v4u{r0, r1, r2, r3});
 }
 
 // Same for bf16 (no packed bf16 arithmetic on gfx950: via exact fp32 values).
@@ -581,8 +596,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_w4_kernel(
       const int g = g0 + u;
       if (g < ge) {
         v16f d = {};
-        const uint32_t mz = 0xE400u | static_cast<uint32_t>(zc[u]);   // fp16 -(1024 + z)
-        const uint32_t nmz = mz | (mz << 16);
+        const uint32_t nzl = w4_nz1024(static_cast<uint32_t>(zc[u])), nzh = w4_nz64(static_cast<uint32_t>(zc[u]));
         const float zf = static_cast<float>(zc[u]);
 #pragma unroll
         for (int L = 0; L < 2; ++L) {
@@ -596,7 +610,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_w4_kernel(
               d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, d, 0, 0, 0);
             } else {
               const v8h a = __builtin_bit_cast(v8h, araw);
-              const v8h b = dequant_w4_f16(wv[s], nmz);
+              const v8h b = dequant_w4_f16(wv[s], nzl, nzh);
               d = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, d, 0, 0, 0);
             }
           }
@@ -626,6 +640,14 @@ __global__ __launch_bounds__(NW * 64) void gemv_w4_kernel(
 }
 
 // ---------------------------------------------------------------- 4-bit, 2 <= M <= 16
+// Bytes of the skinny 4-bit kernel's LDS before the act-order staging: the
+// reduction area (two tiles x NW waves x 4 registers x 64 lanes of fp32) and
+// the per-wave scale (2 bytes) and zero-point (1 byte) slices of blk elements,
+// rounded up to 16.
+__host__ __device__ inline int w4s_lds_head(int nw, int blk) {
+  return (2 * nw * 4 * 64 * 4 + 3 * nw * blk + 15) & ~15;
+}
+
 // Streaming form for the decode shapes: one workgroup per CU takes rpw weight
 // rows (16-row tiles) over the whole K; its NW waves split the groups, GPW
 // each. Every load is issued before the first MFMA: scales and zeros, the
@@ -635,11 +657,18 @@ __global__ __launch_bounds__(NW * 64) void gemv_w4_kernel(
 // 8-column chunk per MFMA; the activations are permuted inside each chunk to
 // the dequantiser's order). The group result is folded with its scale in
 // fp32; the waves' sums meet in LDS in a fixed order.
-template <int GPW, int MAXT, bool BF, bool ZP, typename TOut>
-__global__ __launch_bounds__(512) void gemv_w4_skinny_kernel(
+//
+// PERM (act order, the mate PR's "Act order" section): the activation gather
+// runs inside this kernel. After the scale loads the waves copy the M rows of
+// x and the permutation straight into LDS (global -> LDS, no registers), then
+// issue the code stream; they wait for the copies only (the code loads stay
+// in flight) and build each A operand from LDS, x[m][perm[k']], already in the
+// dequantiser's order. K % 512 == 0 and the LDS must hold M rows of x.
+template <int GPW, int MAXT, bool BF, bool ZP, typename TOut, bool PERM>
+__global__ __launch_bounds__(PERM ? 1024 : 512) void gemv_w4_skinny_kernel(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ wscale,
-    const uint8_t* __restrict__ zeros, const uint16_t* __restrict__ x, int M, int N, int K, int rpw,
-    TOut* __restrict__ y) {
+    const uint8_t* __restrict__ zeros, const uint16_t* __restrict__ x, const int32_t* __restrict__ perm,
+    int M, int N, int K, int rpw, TOut* __restrict__ y) {
   extern __shared__ float red4[];                          // [tile of a pair][wave][reg][lane]
   const int NW = blockDim.x >> 6;
   const int G = K >> 7, KB = K >> 1, ZB = (G + 1) >> 1;
@@ -676,42 +705,68 @@ __global__ __launch_bounds__(512) void gemv_w4_skinny_kernel(
     lrow[t] = min(16 * t + n, r1 - r0 - 1);
     crow[t] = codes + static_cast<size_t>(r0 + lrow[t]) * KB + 16 * j;
   }
-  __builtin_amdgcn_sched_barrier(0);
-  v4u cw[MAXT][GPW];
-#pragma unroll
-  for (int t = 0; t < MAXT; ++t)
-#pragma unroll
-    for (int u = 0; u < GPW; ++u) {
-      cw[t][u] = *reinterpret_cast<const v4u*>(crow[t] + min(gb + u, G - 1) * 64);
-      __builtin_amdgcn_sched_barrier(0);
+  // PERM: LDS after the reduction area and the scale slices holds x row m at
+  // byte xo + m * xs and the permutation at xo + M * xs.
+  const int xo = w4s_lds_head(NW, BLK), xs = 2 * K + 16;
+  if (PERM) {
+    const uint32_t lbase = static_cast<uint32_t>(reinterpret_cast<size_t>(red4)) + xo;
+    const int per_row = K >> 9;                 // 1 KB pieces of a row
+    const int total = M * per_row + (K >> 8);   // and of the 4K-byte permutation
+    for (int i = wave; i < total; i += NW) {
+      const bool isx = i < M * per_row;
+      const int m = isx ? i / per_row : 0;
+      const int piece = isx ? i - m * per_row : i - M * per_row;
+      const uint8_t* src = isx ? reinterpret_cast<const uint8_t*>(x) + static_cast<size_t>(m) * 2 * K + piece * 1024
+                               : reinterpret_cast<const uint8_t*>(perm) + piece * 1024;
+      const uint32_t dst = lbase + (isx ? m * xs : M * xs) + piece * 1024;
+      lds_dma16(src + lane * 16, __builtin_amdgcn_readfirstlane(dst));
     }
-  // Activations of token row n only where n < M (the other A rows are zero:
-  // their outputs are never stored). Issued after the code stream: measured
-  // a little faster than ahead of it.
-  v4u ain[GPW][4];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // The code stream, group-tile q = t * GPW + u. Without PERM every load is
+  // issued here. With PERM only the first PD are: each later one is issued
+  // PD group-tiles ahead of its use, so a wave keeps a few loads in flight
+  // while it computes (measured on the 4-bit decode shape, M=8, K=5120,
+  // N=13824: 2 ahead 14.6 us, 1 14.7-15.1, 3 14.6-15.3, 4 15.7, 6 16.4, all
+  // loads up front 17.2).
+  v4u cw[MAXT][GPW];
+  constexpr int NQ = MAXT * GPW, PD = PERM ? (NQ < 2 ? NQ : 2) : NQ;
+  auto issue = [&](int q) {
+    const int t = q / GPW, u = q % GPW;
+    cw[t][u] = *reinterpret_cast<const v4u*>(crow[t] + min(gb + u, G - 1) * 64);
+    __builtin_amdgcn_sched_barrier(0);
+  };
 #pragma unroll
-  for (int u = 0; u < GPW; ++u)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ain[u][i] = v4u{0, 0, 0, 0};
-  if (n < M) {
+  for (int q = 0; q < PD; ++q) issue(q);
+  // A operands: each 8-column chunk in the order [0, 4, 1, 5, 2, 6, 3, 7].
+  // Token rows n >= M read row M - 1 (their outputs are never stored).
+  v4u a[GPW][4];
+  const int mA = min(n, M - 1);
+  if (!PERM) {
+    // Activations, issued after the code stream (measured a little faster
+    // than ahead of it).
+    v4u ain[GPW][4];
 #pragma unroll
     for (int u = 0; u < GPW; ++u) {
       const int g = min(gb + u, G - 1);
-      const v4u* src = reinterpret_cast<const v4u*>(x + static_cast<size_t>(n) * K + g * 128 + 32 * j);
+      const v4u* src = reinterpret_cast<const v4u*>(x + static_cast<size_t>(mA) * K + g * 128 + 32 * j);
 #pragma unroll
       for (int i = 0; i < 4; ++i) ain[u][i] = src[i];
     }
+#pragma unroll
+    for (int u = 0; u < GPW; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const v4u v = ain[u][i];
+        a[u][i] = v4u{perm_b32(v.z, v.x, 0x05040100u), perm_b32(v.z, v.x, 0x07060302u),
+                      perm_b32(v.w, v.y, 0x05040100u), perm_b32(v.w, v.y, 0x07060302u)};
+      }
+  } else {
+    // the copies were issued before the last PD loads (the code stream)
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<PD>();
+    __builtin_amdgcn_sched_barrier(0);
   }
-  // A operands: each 8-column chunk in the order [0, 4, 1, 5, 2, 6, 3, 7].
-  v4u a[GPW][4];
-#pragma unroll
-  for (int u = 0; u < GPW; ++u)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const v4u v = ain[u][i];
-      a[u][i] = v4u{perm_b32(v.z, v.x, 0x05040100u), perm_b32(v.z, v.x, 0x07060302u),
-                    perm_b32(v.w, v.y, 0x05040100u), perm_b32(v.w, v.y, 0x07060302u)};
-    }
 #pragma unroll
   for (int c = 0; c < SPL; ++c) {
     const int e = lane + 64 * c;
@@ -734,6 +789,82 @@ __global__ __launch_bounds__(512) void gemv_w4_skinny_kernel(
       sreg[t][u] = ssc[lrow[t] * GPW + u];
       zreg[t][u] = ZP ? (szr[lrow[t] * GPW + u] >> (4 * (gc & 1))) & 15 : 8;
     }
+  // One group of one tile: the four-MFMA chain over the group's 128 columns,
+  // folded with the group scale (groups past the end, from a ragged split of
+  // K over the waves, count for nothing).
+  auto group_tile = [&](const v4u(&au)[4], int t, int u, float(&acc)[4]) {
+    const int g = gb + u;
+    const int z = zreg[t][u];
+    const uint32_t wv[4] = {cw[t][u].x, cw[t][u].y, cw[t][u].z, cw[t][u].w};
+    v4f d = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (BF) {
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, au[c]),
+                                                    dequant_w4_bf16(wv[c], static_cast<float>(z)), d, 0, 0, 0);
+      } else {
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            __builtin_bit_cast(v8h, au[c]),
+            dequant_w4_f16(wv[c], w4_nz1024(static_cast<uint32_t>(z)), w4_nz64(static_cast<uint32_t>(z))), d, 0, 0, 0);
+      }
+    }
+    const uint16_t sb = sreg[t][u];
+    const float sg = g < G ? (BF ? bf16_to_f32(sb) : __half2float(__builtin_bit_cast(__half, sb))) : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = fmaf(d[i], sg, acc[i]);
+  };
+  // PERM: the A operands of the wave's GPW groups come from LDS,
+  // x[m][perm[k']] in the dequantiser's order; then tile by tile, group by
+  // group, each group-tile's code load is consumed as the one PD ahead is
+  // issued. Each tile sums its groups in the order 0..GPW-1.
+  float accp[PERM ? MAXT : 1][4];
+  if (PERM) {
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) accp[t][i] = 0.0f;
+    __syncthreads();   // every wave's copies have landed
+    const uint8_t* lx = reinterpret_cast<const uint8_t*>(red4) + xo;
+    const uint8_t* xrow = lx + mA * xs;
+    // The permutation becomes byte offsets into a row, once per workgroup; an
+    // entry outside 0..K-1 reads column K - 1 (the prepare step stores a
+    // permutation; this only keeps every LDS read inside the row).
+    int32_t* pw = reinterpret_cast<int32_t*>(red4 + xo / 4 + M * xs / 4);
+    const uint32_t km = static_cast<uint32_t>(K - 1);
+    for (int i = tid; i < (K >> 2); i += NW * 64) {
+      const v4i p = reinterpret_cast<const v4i*>(pw)[i];
+      reinterpret_cast<v4i*>(pw)[i] = v4i{static_cast<int>(2 * min(static_cast<uint32_t>(p.x), km)),
+                                          static_cast<int>(2 * min(static_cast<uint32_t>(p.y), km)),
+                                          static_cast<int>(2 * min(static_cast<uint32_t>(p.z), km)),
+                                          static_cast<int>(2 * min(static_cast<uint32_t>(p.w), km))};
+    }
+    __syncthreads();
+    const int32_t* pl = pw;
+    v4u au[GPW][4];
+#pragma unroll
+    for (int u = 0; u < GPW; ++u) {
+      const int g = min(gb + u, G - 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kb = g * 128 + 32 * j + 8 * i;
+        const v4i p0 = *reinterpret_cast<const v4i*>(pl + kb);
+        const v4i p1 = *reinterpret_cast<const v4i*>(pl + kb + 4);
+        const int pe[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+        uint32_t e[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) e[q] = *reinterpret_cast<const uint16_t*>(xrow + pe[q]);
+        au[u][i] = v4u{e[0] | (e[4] << 16), e[1] | (e[5] << 16), e[2] | (e[6] << 16), e[3] | (e[7] << 16)};
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t)
+#pragma unroll
+      for (int u = 0; u < GPW; ++u) {
+        const int q = t * GPW + u;
+        if (q + PD < NQ) issue(q + PD);
+        group_tile(au[u], t, u, accp[t]);
+      }
+  }
   // Tiles in pairs: compute both, then one fixed-order reduction through LDS.
   // Every tile is computed (no branch, so the loads above stay hoisted).
 #pragma unroll
@@ -742,28 +873,12 @@ __global__ __launch_bounds__(512) void gemv_w4_skinny_kernel(
     for (int tt = 0; tt < 2; ++tt) {
       const int t = t0 + tt;
       float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (PERM) {
 #pragma unroll
-      for (int u = 0; u < GPW; ++u) {
-        const int g = gb + u;
-        const int z = zreg[t][u];
-        const uint32_t wv[4] = {cw[t][u].x, cw[t][u].y, cw[t][u].z, cw[t][u].w};
-        v4f d = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int i = 0; i < 4; ++i) acc[i] = accp[t][i];
+      } else {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          if (BF) {
-            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[u][c]),
-                                                        dequant_w4_bf16(wv[c], static_cast<float>(z)), d, 0, 0, 0);
-          } else {
-            const uint32_t mz = 0xE400u | static_cast<uint32_t>(z);   // fp16 -(1024 + z)
-            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a[u][c]),
-                                                       dequant_w4_f16(wv[c], mz | (mz << 16)), d, 0, 0, 0);
-          }
-        }
-        // groups past the end (ragged K over the waves) count for nothing
-        const uint16_t sb = sreg[t][u];
-        const float sg = g < G ? (BF ? bf16_to_f32(sb) : __half2float(__builtin_bit_cast(__half, sb))) : 0.0f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = fmaf(d[i], sg, acc[i]);
+        for (int u = 0; u < GPW; ++u) group_tile(a[u], t, u, acc);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) red4[((tt * NW + wave) * 4 + i) * 64 + lane] = acc[i];
@@ -915,8 +1030,7 @@ __global__ __launch_bounds__(PERM ? 64 * kRowW4PermWaves : 256) void gemv_w4_row
     const uint16_t sb = static_cast<uint16_t>(sall[r]);
     const float sf = BF ? bf16_to_f32(sb) : __half2float(__builtin_bit_cast(__half, sb));
     const uint32_t zg = ZP ? (static_cast<uint32_t>(zall[r]) >> (4 * (lane & 1))) & 15u : 8u;
-    const uint32_t n1024 = 0xE400u | zg, n64 = 0xD400u | (zg << 4);
-    const uint32_t pl = n1024 | (n1024 << 16), ph = n64 | (n64 << 16);
+    const uint32_t pl = w4_nz1024(zg), ph = w4_nz64(zg);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int g = 8 * c + (lane >> 3);
@@ -960,30 +1074,18 @@ __global__ __launch_bounds__(PERM ? 64 * kRowW4PermWaves : 256) void gemv_w4_row
         }
       }
     }
-    // Code pairs (s, s + 4) of a packed dword as exact fp16 code - zero: the
-    // low nibble of a byte under the exponent of 1024 (0x6400 | c = 1024 + c),
-    // the high nibble, left in place, under the exponent of 64
-    // (0x5400 | c << 4 = 64 + c); subtracting 1024 + z or 64 + z leaves c - z.
-    const uint32_t m1024 = 0x64006400u, m64 = 0x54005400u;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
-        const h2 nz1024 = __builtin_bit_cast(h2, nzl[r][c]);   // fp16 -(1024 + z), twice
-        const h2 nz64 = __builtin_bit_cast(h2, nzh[r][c]);     // fp16 -(64 + z), twice
         const uint32_t wv[2] = {cw[r][c].x, cw[r][c].y};
         float p = 0.0f;
 #pragma unroll
         for (int d = 0; d < 2; ++d) {
-          const uint32_t w8 = wv[d] >> 8;
-          const h2 c0 = __builtin_bit_cast(h2, and_or(wv[d], 0x000F000Fu, m1024)) + nz1024;   // codes 0, 4
-          const h2 c1 = __builtin_bit_cast(h2, and_or(wv[d], 0x00F000F0u, m64)) + nz64;      // codes 1, 5
-          const h2 c2 = __builtin_bit_cast(h2, and_or(w8, 0x000F000Fu, m1024)) + nz1024;     // codes 2, 6
-          const h2 c3 = __builtin_bit_cast(h2, and_or(w8, 0x00F000F0u, m64)) + nz64;         // codes 3, 7
-          p = __builtin_amdgcn_fdot2(c0, xp[c][4 * d + 0], p, false);
-          p = __builtin_amdgcn_fdot2(c1, xp[c][4 * d + 1], p, false);
-          p = __builtin_amdgcn_fdot2(c2, xp[c][4 * d + 2], p, false);
-          p = __builtin_amdgcn_fdot2(c3, xp[c][4 * d + 3], p, false);
+          h2 cz[4];
+          w4_pairs_f16(wv[d], nzl[r][c], nzh[r][c], cz);
+#pragma unroll
+          for (int s = 0; s < 4; ++s) p = __builtin_amdgcn_fdot2(cz[s], xp[c][4 * d + s], p, false);
         }
         acc[r] = fmaf(sv[r][c], p, acc[r]);
       }
@@ -1273,37 +1375,64 @@ hipError_t w4_go(const bpw_weights& w, const uint16_t* x, int m, TOut* y, hipStr
 // at these sizes)
 bool w4_skinny_ok(int64_t m, int64_t k) { return m >= 2 && m <= 16 && k / 128 >= 16 && k / 128 <= 48; }
 
-template <int GPW, int MAXT, bool BF, bool ZP, typename TOut>
+// LDS of the act-order staging: M rows of x (2K bytes + 16 of padding each)
+// and the 4K-byte permutation.
+size_t w4s_perm_lds(int64_t m, int64_t k) { return static_cast<size_t>(m) * (2 * k + 16) + 4 * k; }
+
+template <int GPW, int MAXT, bool BF, bool ZP, bool PERM, typename TOut>
 void w4_skinny_go(const bpw_weights& w, const uint16_t* x, int m, int rpw, int nw, TOut* y, hipStream_t s) {
   const int n = static_cast<int>(w.n), k = static_cast<int>(w.k);
-  auto kern = gemv_w4_skinny_kernel<GPW, MAXT, BF, ZP, TOut>;
-  const size_t lds = 2ull * nw * 4 * 64 * 4 + 3ull * nw * (MAXT * 16 * GPW);
+  auto kern = gemv_w4_skinny_kernel<GPW, MAXT, BF, ZP, TOut, PERM>;
+  const size_t lds = w4s_lds_head(nw, MAXT * 16 * GPW) + (PERM ? w4s_perm_lds(m, k) : 0);
   allow_lds(kern, lds);
   kern<<<(n + rpw - 1) / rpw, nw * 64, lds, s>>>(static_cast<const uint8_t*>(w.codes),
                                                  static_cast<const uint16_t*>(w.scales),
-                                                 static_cast<const uint8_t*>(w.zeros), x, m, n, k, rpw, y);
+                                                 static_cast<const uint8_t*>(w.zeros), x, w.perm, m, n, k, rpw, y);
 }
 
-template <bool BF, bool ZP, typename TOut>
-hipError_t w4_skinny(const bpw_weights& w, const uint16_t* x, int m, TOut* y, hipStream_t s) {
-  const int n = static_cast<int>(w.n), g = static_cast<int>(w.k / 128);
-  // rows split evenly over the CUs (multiple of 8, 16..64: at most four tiles)
+// Launch shape of the skinny 4-bit kernel: rows split evenly over the CUs
+// (multiple of 8, 16..64: at most four 16-row tiles), up to 8 waves of 4..6
+// groups (16 <= groups <= 48).
+struct W4SkinnyShape {
+  int rpw, nw, gpw, maxt;
+};
+
+W4SkinnyShape w4_skinny_shape(int64_t n, int64_t k, bool perm) {
+  const int g = static_cast<int>(k / 128);
   const int cus = cu_count();
-  int rpw = (n + cus - 1) / cus;
+  int rpw = static_cast<int>((n + cus - 1) / cus);
   rpw = min(64, max(16, (rpw + 7) & ~7));
-  // up to 8 waves of 4..6 groups (16 <= groups <= 48)
-  const int nw = min(8, (g + 3) / 4);
-  const int gpw = (g + nw - 1) / nw;
-  const bool two = rpw <= 32;
-#define BPW_W4S(GPW_)                                                                    \
-  if (gpw == GPW_) {                                                                    \
-    if (two) w4_skinny_go<GPW_, 2, BF, ZP>(w, x, m, rpw, nw, y, s);                     \
-    else w4_skinny_go<GPW_, 4, BF, ZP>(w, x, m, rpw, nw, y, s);                         \
-    return hipGetLastError();                                                           \
+  // act order: 3 groups per wave and up to 16 waves (the gathered operands
+  // are built group by group, so a wave needs fewer registers and more waves
+  // share the CU)
+  const int nw = perm ? (g + 2) / 3 : min(8, (g + 3) / 4);
+  return {rpw, nw, (g + nw - 1) / nw, rpw <= 32 ? 2 : 4};
+}
+
+template <bool BF, bool ZP, bool PERM, typename TOut>
+hipError_t w4_skinny(const bpw_weights& w, const uint16_t* x, int m, TOut* y, hipStream_t s) {
+  const W4SkinnyShape sh = w4_skinny_shape(w.n, w.k, PERM);
+#define BPW_W4S(GPW_)                                                                            \
+  if (sh.gpw == GPW_) {                                                                         \
+    if (sh.maxt == 2) w4_skinny_go<GPW_, 2, BF, ZP, PERM>(w, x, m, sh.rpw, sh.nw, y, s);        \
+    else w4_skinny_go<GPW_, 4, BF, ZP, PERM>(w, x, m, sh.rpw, sh.nw, y, s);                     \
+    return hipGetLastError();                                                                   \
   }
-  BPW_W4S(4) BPW_W4S(5) BPW_W4S(6)
+  if (PERM) {
+    BPW_W4S(3)
+  } else {
+    BPW_W4S(4) BPW_W4S(5) BPW_W4S(6)
+  }
 #undef BPW_W4S
   return hipErrorInvalidValue;
+}
+
+// The skinny kernel gathers the act-order activation itself when K is a
+// multiple of 512 and M rows of x fit in the LDS beside its other arrays.
+bool w4_skinny_perm_ok(int64_t m, int64_t k) {
+  if (!w4_skinny_ok(m, k) || k % 512 != 0) return false;
+  const W4SkinnyShape sh = w4_skinny_shape(1 << 20, k, true);   // the largest tile count
+  return w4s_lds_head(sh.nw, 4 * 16 * sh.gpw) + w4s_perm_lds(m, k) <= 160 * 1024;
 }
 
 template <int CH, bool BF, bool ZP, typename TOut>
@@ -1327,7 +1456,8 @@ void w4_row_perm_go(const bpw_weights& w, const uint16_t* x, TOut* y, hipStream_
 }
 
 template <bool BF, bool ZP, typename TOut>
-hipError_t w4_perm_dispatch_f(const bpw_weights& w, const uint16_t* x, TOut* y, hipStream_t s) {
+hipError_t w4_perm_dispatch_f(const bpw_weights& w, const uint16_t* x, int m, TOut* y, hipStream_t s) {
+  if (m > 1) return w4_skinny<BF, ZP, true>(w, x, m, y, s);
   switch (w.k / 1024) {
     case 1: w4_row_perm_go<1, BF, ZP>(w, x, y, s); break;
     case 2: w4_row_perm_go<2, BF, ZP>(w, x, y, s); break;
@@ -1356,7 +1486,7 @@ hipError_t w4_dispatch_f(const bpw_weights& w, const uint16_t* x, int m, TOut* y
     }
     return hipGetLastError();
   }
-  if (w4_skinny_ok(m, w.k)) return w4_skinny<BF, ZP>(w, x, m, y, s);
+  if (w4_skinny_ok(m, w.k)) return w4_skinny<BF, ZP, false>(w, x, m, y, s);
   const int nw = waves_for(w.k / 128);
   const int fold = fold_for(m);
 #define BPW_W4(NW_, F_) \
@@ -1419,19 +1549,20 @@ hipError_t launch_gemv_t2_partials(const bpw_weights& w, const int8_t* q, int64_
 }
 
 bool gemv_w4_perm_fits(const bpw_weights& w, int64_t m, const void* x) {
-  return w.perm != nullptr && w4_row_ok(m, w.k) && reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
-         reinterpret_cast<uintptr_t>(w.perm) % 16 == 0;
+  return w.perm != nullptr && (w4_row_ok(m, w.k) || w4_skinny_perm_ok(m, w.k)) &&
+         reinterpret_cast<uintptr_t>(x) % 16 == 0 && reinterpret_cast<uintptr_t>(w.perm) % 16 == 0;
 }
 
-hipError_t launch_gemv_w4_perm(const bpw_weights& w, const void* x, int x_dtype, void* y, int y_dtype,
-                               hipStream_t s) {
+hipError_t launch_gemv_w4_perm(const bpw_weights& w, const void* x, int x_dtype, int64_t m, void* y,
+                               int y_dtype, hipStream_t s) {
   const uint16_t* xh = static_cast<const uint16_t*>(x);
   const bool bf = x_dtype == BPW_BF16, zp = w.fmt == BPW_INT4_ZP;
-#define BPW_W4P(TOut_)                                                                           \
-  {                                                                                              \
-    TOut_* yo = static_cast<TOut_*>(y);                                                          \
-    if (bf) return zp ? w4_perm_dispatch_f<true, true>(w, xh, yo, s) : w4_perm_dispatch_f<true, false>(w, xh, yo, s); \
-    return zp ? w4_perm_dispatch_f<false, true>(w, xh, yo, s) : w4_perm_dispatch_f<false, false>(w, xh, yo, s);       \
+  const int mi = static_cast<int>(m);
+#define BPW_W4P(TOut_)                                                                                   \
+  {                                                                                                      \
+    TOut_* yo = static_cast<TOut_*>(y);                                                                  \
+    if (bf) return zp ? w4_perm_dispatch_f<true, true>(w, xh, mi, yo, s) : w4_perm_dispatch_f<true, false>(w, xh, mi, yo, s); \
+    return zp ? w4_perm_dispatch_f<false, true>(w, xh, mi, yo, s) : w4_perm_dispatch_f<false, false>(w, xh, mi, yo, s);       \
   }
   switch (y_dtype) {
     case BPW_F32: BPW_W4P(float)

@@ -49,11 +49,12 @@ hipError_t launch_gemv_t2(const bpw_weights& w, const int8_t* q, const float* x_
 hipError_t launch_gemv_t2_partials(const bpw_weights& w, const int8_t* q, int64_t m, int64_t m0,
                                    int64_t m1, int64_t n0, int64_t n1, int32_t* out,
                                    hipStream_t s);
-// M = 1 with act order, x in its original column order: the GEMV gathers
-// through w.perm itself (no workspace). Needs 16-byte aligned x and perm.
+// Act order with x in its original column order: the decode kernels gather
+// through w.perm themselves (no workspace) at M = 1 and, where M rows of x fit
+// in LDS, on the skinny path. Needs 16-byte aligned x and perm.
 bool gemv_w4_perm_fits(const bpw_weights& w, int64_t m, const void* x);
-hipError_t launch_gemv_w4_perm(const bpw_weights& w, const void* x, int x_dtype, void* y, int y_dtype,
-                               hipStream_t s);
+hipError_t launch_gemv_w4_perm(const bpw_weights& w, const void* x, int x_dtype, int64_t m, void* y,
+                               int y_dtype, hipStream_t s);
 bool gemv_w4_fits(int64_t m, int64_t k);
 hipError_t launch_gemv_w4(const bpw_weights& w, const void* x_sorted, int x_dtype, int64_t m,
                           void* y, int y_dtype, hipStream_t s);

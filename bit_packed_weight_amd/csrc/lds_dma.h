@@ -1,4 +1,4 @@
-// Direct global -> LDS copies for the prefill GEMMs.
+// Direct global -> LDS copies (prefill GEMMs, act-order decode staging).
 #pragma once
 
 #include <stdint.h>
@@ -25,6 +25,16 @@ __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
       : "=&s"(saved)
       : "s"(lds_base), "v"(src)
       : "memory");
+}
+
+// Wait until at most N vector memory operations of this wave are outstanding
+// (gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14; expcnt 7 and lgkmcnt 15 mean
+// no wait on those counters). Operations complete in issue order, so this
+// waits for everything issued before the last N.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 0..63");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
 }  // namespace bpw
