@@ -347,6 +347,212 @@ __global__ __launch_bounds__(NW * 64) void gemv_t2_skinny_kernel(
   }
 }
 
+// ---------------------------------------------------------------- ternary, M <= 16, K <= 4096, staged in LDS
+// One workgroup of 16 waves per CU takes rpw <= 64 weight rows (four 16-row
+// tiles) over the whole K; wave w owns groups GPW * w .. GPW * w + GPW - 1.
+// Every global read is a direct global -> LDS copy issued up front, so the
+// code stream leaves HBM in whole contiguous rows (one 1 KB copy per row of
+// K = 4096): the wave's activations (16 tokens of its groups), a share of the
+// scale block and of the activation scales, then one code row of each tile,
+// tile by tile. A tile is computed once every wave's copy of it has landed
+// (vmcnt over the copies issued after it, then a barrier), while the later
+// tiles stream in. MFMA i32_16x16x64_i8: lane (n, j) = (l % 16, l / 16) holds
+// token n of A and weight row n of the tile for B, 16 of the group's columns
+// per instruction (two instructions per 128-group). The codes are decoded
+// unsigned (each plane is one shift and one mask) and the code - 1 offset
+// enters as the MFMA's starting accumulator, -sum(q) over the group per token,
+// itself an MFMA of the activations against a B of all -1 ("Kernel
+// experiments: recorded evidence", Test 21: minus the group sum of q). The
+// per-wave fp32 results meet in LDS, summed in a fixed order.
+constexpr int kStageWaves = 16, kStageTiles = 4;
+
+struct T2StageLds {
+  int rs, oc, oa, os, ox, red, total;   // code row stride; byte offsets; bytes
+};
+
+__host__ __device__ inline T2StageLds t2_stage_lds(int K, int G, int gpw, int xs_bytes) {
+  T2StageLds l;
+  l.rs = (K >> 2) + 16;
+  l.oc = 0;
+  const int codes = kStageTiles * 16 * l.rs;
+  const int red = kStageTiles * kStageWaves * 4 * 64 * 4;   // fp32 partials, after the codes are read
+  l.red = 0;
+  l.oa = (codes > red ? codes : red);
+  l.os = l.oa + kStageWaves * gpw * 16 * 128;
+  l.ox = l.os + ((kStageTiles * 16 * G * 2 + 15) & ~15);
+  l.total = l.ox + ((xs_bytes + 15) & ~15);
+  return l;
+}
+
+template <int GPW, typename TOut, bool PARTIALS, bool GS>
+__global__ __launch_bounds__(64 * kStageWaves) void gemv_t2_stage_kernel(
+    const uint8_t* __restrict__ codes, const __half* __restrict__ wscale,
+    const int8_t* __restrict__ q, const float* __restrict__ x_scale, int M, int N, int K, int rpw,
+    TOut* __restrict__ y, int32_t* __restrict__ pout, int pm0, int pm1, int pn0, int pn1) {
+  constexpr int NW = kStageWaves, T = kStageTiles;
+  extern __shared__ __align__(16) uint8_t stg[];
+  const int G = K >> 7, KB = K >> 2;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, j = lane >> 4;
+  const int r0 = blockIdx.x * rpw;
+  const int nrow = min(rpw, N - r0);                       // >= 1
+  const int gb = wave * GPW;
+  const int xs_bytes = PARTIALS ? 0 : (GS ? M * G * 4 : M * 4);
+  const T2StageLds L = t2_stage_lds(K, G, GPW, xs_bytes);
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<size_t>(stg));
+
+  // ---- copies, in the order they are waited for
+  // activations of this wave's groups: 16 tokens x 128 bytes per group, two
+  // 1 KB copies (tokens past M repeat token M - 1; their outputs are dropped)
+#pragma unroll
+  for (int u = 0; u < GPW; ++u) {
+    const int g = min(gb + u, G - 1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      // token 8h + l / 8, its 16-byte unit (l % 8) ^ token % 8 lands in slot l % 8:
+      // the A reads below, eight tokens at one unit, then fall in distinct banks
+      const int tk = 8 * h + (lane >> 3), m = min(tk, M - 1);
+      lds_dma16(q + static_cast<size_t>(m) * K + g * 128 + 16 * ((lane & 7) ^ (tk & 7)),
+                __builtin_amdgcn_readfirstlane(lds0 + L.oa + ((wave * GPW + u) * 2 + h) * 1024));
+    }
+  }
+  // the workgroup's scale block (nrow x G fp16, contiguous; G % 8 == 0 keeps
+  // it whole 16-byte pieces) and the activation scales, one piece per wave
+  // from wave 0 on: 1 KB pieces, or M floats 4 bytes per lane. (A transposed
+  // copy, 4 bytes per lane, reads its scales without bank conflicts but
+  // measured slower: 7.23 against 7.06 us at M=16.)
+  if (!PARTIALS) {
+    const int sb = nrow * G * 2, npieces = (sb + 1023) >> 10;
+    const int xpieces = GS ? (xs_bytes + 1023) >> 10 : 1;
+    if (wave < npieces) {
+      const int off = wave * 1024 + lane * 16;
+      if (off < sb)
+        lds_dma16(reinterpret_cast<const uint8_t*>(wscale) + static_cast<size_t>(r0) * G * 2 + off,
+                  __builtin_amdgcn_readfirstlane(lds0 + L.os + wave * 1024));
+    } else if (wave < npieces + xpieces) {
+      const int pc = wave - npieces;
+      if (GS) {
+        const int off = pc * 1024 + lane * 16;           // M * G * 4 bytes, a multiple of 16
+        if (off < xs_bytes)
+          lds_dma16(reinterpret_cast<const uint8_t*>(x_scale) + off,
+                    __builtin_amdgcn_readfirstlane(lds0 + L.ox + pc * 1024));
+      } else if (lane < M) {
+        lds_dma4(x_scale + lane, __builtin_amdgcn_readfirstlane(lds0 + L.ox));
+      }
+    }
+  }
+  // one code row per tile (rows past the workgroup's share repeat its last
+  // row): tiles 0 and 1 now, each later one after the tile two before it is
+  // computed, so two tiles are in flight (PARTIALS: all four now)
+  auto copy_tile = [&](int t) {
+    const int row = min(16 * t + wave, nrow - 1);
+    if (lane * 16 < KB)
+      lds_dma16(codes + static_cast<size_t>(r0 + row) * KB + lane * 16,
+                __builtin_amdgcn_readfirstlane(lds0 + L.oc + (16 * t + wave) * L.rs));
+  };
+  static_assert(T == 4, "the copy schedule and the waits below count four tiles");
+  copy_tile(0);
+  copy_tile(1);
+  if (PARTIALS) {
+    copy_tile(2);
+    copy_tile(3);
+  }
+
+  // ---- tile 0, the activations and the scales have landed for every wave
+  // (PARTIALS stores inside the tile loop, and stores count in vmcnt too: that
+  // verification path waits for every copy here instead)
+  if (PARTIALS) wait_vmcnt<0>();
+  else wait_vmcnt<1>();
+  __syncthreads();
+  // A operands: token n, columns 32j + 16e .. + 15 of group u, as the 4x4
+  // byte transpose the code planes need (plane p, byte i <-> column 4i + p)
+  v4i a[GPW][2], cneg[GPW];
+  const v4i neg1 = {-1, -1, -1, -1};
+#pragma unroll
+  for (int u = 0; u < GPW; ++u) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const v4u v = *reinterpret_cast<const v4u*>(stg + L.oa + (wave * GPW + u) * 2048 + n * 128 +
+                                                   16 * ((2 * j + e) ^ (n & 7)));
+      uint32_t o0, o1, o2, o3;
+      transpose4x4(v.x, v.y, v.z, v.w, o0, o1, o2, o3);
+      a[u][e] = v4i{static_cast<int>(o0), static_cast<int>(o1), static_cast<int>(o2), static_cast<int>(o3)};
+    }
+    // -sum(q) of token 4j + r over the group, in every column
+    v4i c = {0, 0, 0, 0};
+    c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u][0], neg1, c, 0, 0, 0);
+    cneg[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u][1], neg1, c, 0, 0, 0);
+  }
+  float acc[T][4];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[t][r] = 0.0f;
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    if (t > 0 && !PARTIALS) {
+      // the copies of tile t: all but tile t + 1's, if issued
+      if (t < T - 1) wait_vmcnt<1>();
+      else wait_vmcnt<0>();
+      __syncthreads();
+    }
+    // (after the barrier: every wave is done with tile t - 1's rows; tile
+    // t + 2's slots were never read)
+    if (!PARTIALS && t + 2 < T) copy_tile(t + 2);
+    const uint8_t* crow = stg + L.oc + (16 * t + n) * L.rs;
+#pragma unroll
+    for (int u = 0; u < GPW; ++u) {
+      const int g = gb + u;
+      const int gc = min(g, G - 1);
+      const v2u w2 = *reinterpret_cast<const v2u*>(crow + gc * 32 + 8 * j);
+      v4i d = cneg[u];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const uint32_t w = e ? w2.y : w2.x;
+        const v4i b = {static_cast<int>(code_plane(w, 0)), static_cast<int>(code_plane(w, 1)),
+                       static_cast<int>(code_plane(w, 2)), static_cast<int>(code_plane(w, 3))};
+        d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u][e], b, d, 0, 0, 0);
+      }
+      const int nn = r0 + 16 * t + n;                      // weight row of this lane
+      if (PARTIALS) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int mm = 4 * j + r;
+          if (g < G && mm < M && mm >= pm0 && mm < pm1 && 16 * t + n < nrow && nn >= pn0 && nn < pn1)
+            pout[(static_cast<size_t>(mm - pm0) * (pn1 - pn0) + (nn - pn0)) * G + g] = d[r];
+        }
+      } else {
+        const __half hs = reinterpret_cast<const __half*>(stg + L.os)[min(16 * t + n, nrow - 1) * G + gc];
+        const float sg = g < G ? __half2float(hs) : 0.0f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float xg = GS ? reinterpret_cast<const float*>(stg + L.ox)[min(4 * j + r, M - 1) * G + gc] : 1.0f;
+          acc[t][r] = fmaf(static_cast<float>(d[r]), GS ? sg * xg : sg, acc[t][r]);
+        }
+      }
+    }
+  }
+  if (PARTIALS) return;
+  // ---- fixed-order sum over the waves (the code rows are no longer read)
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(stg + L.red);
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[((t * NW + wave) * 4 + r) * 64 + lane] = acc[t][r];
+  __syncthreads();
+  {
+    // one output per thread: tile t, register r, lane l
+    const int t = tid >> 8, r = (tid >> 6) & 3, l = tid & 63;
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) v += red[((t * NW + w) * 4 + r) * 64 + l];
+    const int mm = 4 * (l >> 4) + r, rl = 16 * t + (l & 15);
+    if (!GS) v *= reinterpret_cast<const float*>(stg + L.ox)[min(mm, M - 1)];
+    if (mm < M && rl < nrow) store_out(y + static_cast<size_t>(mm) * N + r0 + rl, v);
+  }
+}
+
 // ---------------------------------------------------------------- ternary, M <= 32, long K
 // The skinny kernel's scheme for K beyond what one wave's registers hold: the
 // waves step through K in phases of NW * 2 groups (2 per wave), loading a
@@ -1339,9 +1545,44 @@ hipError_t t2_long(const bpw_weights& w, const int8_t* q, const float* xs, int m
 // M = 1 up to K = 16384: the row kernel; M = 2..32 up to 32 groups: the
 // skinny kernel; any other M <= 32: the long-K kernel. The same routing with
 // per-(row, group) activation scales.
+// The staged kernel: 2 <= M <= 16, K a multiple of 1024 up to 4096 (the
+// scale rows and code rows then split into whole 16-byte copies), 16-byte
+// aligned activations and code plane, and (group activation scales) a
+// 16-byte aligned x_scale.
+bool t2_stage_ok(int64_t m, int64_t k, const void* q, const void* codes, const void* xs, bool gs) {
+  return m >= 2 && m <= 16 && k % 1024 == 0 && k <= 4096 && reinterpret_cast<uintptr_t>(q) % 16 == 0 &&
+         reinterpret_cast<uintptr_t>(codes) % 16 == 0 && (!gs || reinterpret_cast<uintptr_t>(xs) % 16 == 0);
+}
+
+template <typename TOut, bool PARTIALS, bool GS>
+hipError_t t2_stage(const bpw_weights& w, const int8_t* q, const float* xs, int m, TOut* y, int32_t* pout,
+                    int pm0, int pm1, int pn0, int pn1, hipStream_t s) {
+  const int n = static_cast<int>(w.n), k = static_cast<int>(w.k), g = k / 128;
+  const int cus = cu_count();
+  int rpw = (n + cus - 1) / cus;
+  rpw = min(16 * kStageTiles, max(16, (rpw + 7) & ~7));
+  const int gpw = (g + kStageWaves - 1) / kStageWaves;      // 1 or 2
+  const int xs_bytes = PARTIALS ? 0 : (GS ? m * g * 4 : m * 4);
+  const T2StageLds L = t2_stage_lds(k, g, gpw, xs_bytes);
+  const unsigned blocks = static_cast<unsigned>((n + rpw - 1) / rpw);
+  auto go = [&](auto kern) {
+    allow_lds(kern, L.total);
+    kern<<<blocks, 64 * kStageWaves, L.total, s>>>(static_cast<const uint8_t*>(w.codes),
+                                                     static_cast<const __half*>(w.scales), q, xs, m, n, k, rpw, y,
+                                                     pout, pm0, pm1, pn0, pn1);
+  };
+  if (gpw == 1) go(gemv_t2_stage_kernel<1, TOut, PARTIALS, GS>);
+  else go(gemv_t2_stage_kernel<2, TOut, PARTIALS, GS>);
+  return hipGetLastError();
+}
+
 template <typename TOut>
 hipError_t t2_dispatch(const bpw_weights& w, const int8_t* q, const float* xs, int m, TOut* y,
                        bool gs, float* part, hipStream_t s) {
+  if (t2_stage_ok(m, w.k, q, w.codes, xs, gs)) {
+    if (gs) return t2_stage<TOut, false, true>(w, q, xs, m, y, nullptr, 0, 0, 0, 0, s);
+    return t2_stage<TOut, false, false>(w, q, xs, m, y, nullptr, 0, 0, 0, 0, s);
+  }
   if (gs) {
     if (t2_row_ok(m, w.k)) return t2_row<TOut, false, true>(w, q, xs, y, nullptr, 0, 0, s);
     // (above 16 rows the skinny kernel's four-tile form would spill with the scales)
@@ -1539,6 +1780,9 @@ hipError_t launch_gemv_t2_partials(const bpw_weights& w, const int8_t* q, int64_
   const int mi = static_cast<int>(m);
   if (t2_row_ok(m, k))   // the product for M = 1 runs the row kernel: verify that core
     return t2_row<float, true>(w, q, nullptr, nullptr, out, static_cast<int>(n0), static_cast<int>(n1), s);
+  if (t2_stage_ok(m, k, q, w.codes, nullptr, false))   // the staged kernel where the product runs it
+    return t2_stage<float, true, false>(w, q, nullptr, mi, static_cast<float*>(nullptr), out, static_cast<int>(m0),
+                                        static_cast<int>(m1), static_cast<int>(n0), static_cast<int>(n1), s);
   if (t2_skinny_ok(m, k))   // the skinny kernel for 2 <= M <= 32 up to 32 groups
     return t2_skinny<float, true>(w, q, nullptr, mi, static_cast<float*>(nullptr), out, static_cast<int>(m0),
                                   static_cast<int>(m1), static_cast<int>(n0), static_cast<int>(n1), s);

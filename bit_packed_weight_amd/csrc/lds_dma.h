@@ -27,6 +27,21 @@ __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
       : "memory");
 }
 
+// The same with 4 bytes per lane (global_load_lds_dword): lane i's 4 bytes
+// land at lds_base + 4 * i.
+__device__ __forceinline__ void lds_dma4(const void* src, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_base), "v"(src)
+      : "memory");
+}
+
 // Wait until at most N vector memory operations of this wave are outstanding
 // (gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14; expcnt 7 and lgkmcnt 15 mean
 // no wait on those counters). Operations complete in issue order, so this
