@@ -379,6 +379,29 @@ def bench_w4_decode(bpw, synth, torch, np, steps, warmup, m=1):
     return decode_leg("w4a16_decode_gemv", m, w.k, w.n, copies[0].logical_bytes, ms, len(copies), act_order=True)
 
 
+def bench_w4_down(bpw, synth, torch, np, steps, warmup, m=1):
+    """The down projection of the W4A16 decode layer (K=13824, N=5120): at M = 1 the
+    row kernel with K split over two waves, at M = 8 split-K slices and their reduce.
+    Act order at this K adds a separate gather launch; the same weight without act
+    order times the GEMV alone."""
+    out = {}
+    for act in (True, False):
+        w = synth.w4a16_down(m, act_order=act)
+        planes = bpw.prepare_packed_host(bpw.INT4_ZP, w.codes, w.scales, w.zeros, w.g_idx)
+        copies = rotated_copies(bpw, planes, 1 << 30)
+        x = to_dev(w.x, "f16", torch, np)
+        y = torch.empty((m, w.n), dtype=torch.float16, device="cuda")
+        ws = torch.empty(max(bpw.workspace_size(copies[0], m, bpw.F16, bpw.PATH_GEMV), 1), dtype=torch.uint8,
+                         device="cuda")
+        ms = time_calls(torch, lambda c: bpw.gemv_packed(copies[c], x, out=y, workspace=ws), len(copies), steps,
+                        warmup)
+        out[act] = decode_leg("w4a16_down_gemv", m, w.k, w.n, copies[0].logical_bytes, ms, len(copies),
+                              act_order=act)
+        del copies
+    out[True]["without_act_order"] = out[False]
+    return out[True]
+
+
 def bench_w4_prefill(bpw, synth, torch, np, steps, warmup):
     w = synth.w4a16_prefill()
     planes = bpw.prepare_packed_host(bpw.INT4_SYM, w.codes, w.scales, scale_dtype=bpw.BF16)
@@ -578,6 +601,8 @@ LEGS = {
     "t2_groups_m16": (bench_ternary_decode_groups, 900, 300, {"m": 16}),
     "w4_m1": (bench_w4_decode, 900, 300, {"m": 1}),
     "w4_m8": (bench_w4_decode, 900, 300, {"m": 8}),
+    "w4_down_m1": (bench_w4_down, 900, 300, {"m": 1}),
+    "w4_down_m8": (bench_w4_down, 900, 300, {"m": 8}),
     "bf16_prefill": (bench_w4_prefill, 30, 6, {}),
     "w4a8_prefill": (bench_w4a8_prefill, 30, 6, {}),
     "t2_prefill": (bench_ternary_prefill, 12, 3, {}),

@@ -143,7 +143,10 @@ size_t workspace_need(const bpw_weights* w, int64_t m, int x_dtype, int entry) {
     return round_up(mk);                       // plane-ordered int8 activations
   }
   if (x_dtype == BPW_I8 || x_dtype == BPW_I8GS) return round_up(mk);  // nibble-ordered int8 activations
-  return w->perm ? round_up(mk * 2) : 0;       // gathered 16-bit activations
+  // gathered 16-bit activations, then the fp32 split-K slices of a long-K decode
+  const size_t gather = w->perm ? round_up(mk * 2) : 0;
+  if (entry == BPW_PATH_GEMV && gemv_w4_fits(m, w->k)) return gather + round_up(gemv_w4_split_bytes(m, w->n, w->k));
+  return gather;
 }
 
 namespace {
@@ -197,13 +200,18 @@ int run_product(bool gemv, const bpw_weights* w, const void* x, int x_dtype, con
   if (gemv && gemv_w4_perm_fits(*w, m, x))
     return hip_status(launch_gemv_w4_perm(*w, x, x_dtype, m, y, y_dtype, s), "4-bit act-order GEMV launch");
   const void* xs = x;
+  size_t used = 0;
   if (w->perm) {
     uint16_t* xp = static_cast<uint16_t*>(ws);
     if (int st = hip_status(launch_gather_cols(static_cast<const uint16_t*>(x), w->perm, m, w->k, xp, s), "act-order gather launch"))
       return st;
     xs = xp;
+    used = round_up(static_cast<size_t>(m) * w->k * 2);
   }
-  if (gemv && gemv_w4_fits(m, w->k)) return hip_status(launch_gemv_w4(*w, xs, x_dtype, m, y, y_dtype, s), "4-bit GEMV launch");
+  if (gemv && gemv_w4_fits(m, w->k)) {
+    float* part = gemv_w4_split_bytes(m, w->n, w->k) > 0 ? reinterpret_cast<float*>(static_cast<char*>(ws) + used) : nullptr;
+    return hip_status(launch_gemv_w4(*w, xs, x_dtype, m, y, y_dtype, part, s), "4-bit GEMV launch");
+  }
   return hip_status(launch_gemm_w4(*w, xs, x_dtype, m, y, y_dtype, s), "4-bit GEMM launch");
 }
 

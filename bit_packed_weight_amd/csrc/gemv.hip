@@ -870,11 +870,18 @@ __host__ __device__ inline int w4s_lds_head(int nw, int blk) {
 // issue the code stream; they wait for the copies only (the code loads stay
 // in flight) and build each A operand from LDS, x[m][perm[k']], already in the
 // dequantiser's order. K % 512 == 0 and the LDS must hold M rows of x.
-template <int GPW, int MAXT, bool BF, bool ZP, typename TOut, bool PERM>
+//
+// SPLIT (K beyond the groups one workgroup's waves can hold): blockIdx.y
+// picks a slice of NW * GPW groups, and the workgroup writes its fp32 sums
+// (group scales applied) to part[slice][m][n]; splitk_reduce_kernel adds the
+// slices in order (split-K as in "Kernel experiments: recorded evidence",
+// Tests 21 and 30, and the mate PR's dense kernel).
+template <int GPW, int MAXT, bool BF, bool ZP, typename TOut, bool PERM, bool SPLIT>
 __global__ __launch_bounds__(PERM ? 1024 : 512) void gemv_w4_skinny_kernel(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ wscale,
     const uint8_t* __restrict__ zeros, const uint16_t* __restrict__ x, const int32_t* __restrict__ perm,
-    int M, int N, int K, int rpw, TOut* __restrict__ y) {
+    int M, int N, int K, int rpw, TOut* __restrict__ y, float* __restrict__ part) {
+  static_assert(!(PERM && SPLIT), "the act-order gather runs without the K split");
   extern __shared__ float red4[];                          // [tile of a pair][wave][reg][lane]
   const int NW = blockDim.x >> 6;
   const int G = K >> 7, KB = K >> 1, ZB = (G + 1) >> 1;
@@ -882,7 +889,7 @@ __global__ __launch_bounds__(PERM ? 1024 : 512) void gemv_w4_skinny_kernel(
   const int n = lane & 15, j = lane >> 4;
   const int r0 = blockIdx.x * rpw;
   const int r1 = min(r0 + rpw, N);
-  const int gb = wave * GPW;
+  const int gb = ((SPLIT ? blockIdx.y * NW : 0) + wave) * GPW;
 
   // Scales and zero bytes of this wave's groups for the workgroup's rows: a
   // (rows x GPW) block per wave, element e = local row e / GPW, group
@@ -1096,16 +1103,23 @@ __global__ __launch_bounds__(PERM ? 1024 : 512) void gemv_w4_skinny_kernel(
       float v = 0.0f;
       for (int w = 0; w < NW; ++w) v += red4[((tt * NW + w) * 4 + i) * 64 + l];
       const int mm = 4 * (l >> 4) + i, nn = r0 + 16 * (t0 + tt) + (l & 15);
-      if (mm < M && nn < r1) store_out(y + static_cast<size_t>(mm) * N + nn, v);
+      if (mm < M && nn < r1) {
+        if (SPLIT) part[(static_cast<size_t>(blockIdx.y) * M + mm) * N + nn] = v;
+        else store_out(y + static_cast<size_t>(mm) * N + nn, v);
+      }
     }
     __syncthreads();
   }
 }
 
 // ---------------------------------------------------------------- 4-bit, M = 1
-// K a multiple of 1024. Each wave streams R whole rows, one 512-byte load
-// instruction per 1024 columns (lane l holds the 16 codes of columns
-// 16l..16l+15 of each 1024-column chunk, all inside one 128-group). The lane's
+// K a multiple of 128, up to 32768. Each wave streams R rows, one 512-byte
+// load instruction per 1024 columns (lane l holds the 16 codes of columns
+// 16l..16l+15 of each 1024-column chunk, all inside one 128-group); in a last,
+// partial chunk the lanes past K load clamped addresses and count zero.
+// Past 8 chunks KS = 2 or 4 waves of the workgroup share a row group's K
+// (the split-K change of the mate PR's dense kernel: fp32 partials summed in
+// a fixed order, here through LDS inside the same launch). The lane's
 // 16 activations sit in registers; fp16: the codes become the exact fp16
 // values code - zero (magic 1024 trick) and v_dot2_f32_f16 accumulates;
 // bf16: codes and activations go through exact fp32 values and the zero point
@@ -1121,31 +1135,49 @@ __global__ __launch_bounds__(PERM ? 1024 : 512) void gemv_w4_skinny_kernel(
 constexpr int kRowW4PermWaves = 4;
 constexpr int kRowW4Perm = 2;                 // rows per wave (4 spill into two waves per SIMD)
 
-template <int R, int CH, bool BF, bool ZP, typename TOut, bool PERM>
-__global__ __launch_bounds__(PERM ? 64 * kRowW4PermWaves : 256) void gemv_w4_row_kernel(
+template <int R, int CH, int KS, bool EXACT, bool BF, bool ZP, typename TOut, bool PERM>
+__global__ __launch_bounds__(256) void gemv_w4_row_kernel(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ wscale,
     const uint8_t* __restrict__ zeros, const uint16_t* __restrict__ x, const int32_t* __restrict__ perm,
     int N, int K, TOut* __restrict__ y) {
-  constexpr int NW = PERM ? kRowW4PermWaves : 4;
-  extern __shared__ __align__(16) uint16_t xstage[];      // PERM: [K] x, then [K] x[perm]
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int row0 = (blockIdx.x * NW + (tid >> 6)) * R;
-  if (!PERM && row0 >= N) return;               // whole wave (without PERM the kernel has no barriers)
+  constexpr int NW = 4, RG = NW / KS;           // waves; row groups per workgroup
+  static_assert(KS == 1 || KS == 2 || KS == 4, "a row group takes 1, 2 or 4 waves");
+  static_assert(!PERM || (KS == 1 && kRowW4PermWaves == NW), "the act-order gather runs without the K split");
+  extern __shared__ __align__(16) uint16_t xstage[];      // PERM: [K] x, then [K] x[perm]; then KS > 1 sums
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ks = wave % KS;                      // this wave's share of K: chunks ks * CH ..
+  const int row0 = (blockIdx.x * RG + wave / KS) * R;
+  // whole wave; without PERM and without the K split the kernel has no barriers
+  if (!PERM && KS == 1 && row0 >= N) return;
   const int KB = K >> 1, G = K >> 7, ZB = (G + 1) >> 1;
+  // This lane's columns of chunk cc: 1024 (ks * CH + cc) + 16 lane .. + 15.
+  // EXACT: K = 1024 KS CH. Otherwise, in a last, partial chunk (and in chunks
+  // past K) the lanes past K read clamped, in-bounds addresses and zero their
+  // activations, so they count nothing (no branch around any load;
+  // K % 128 == 0 keeps a lane's 16 columns in one group).
+  int cbase[CH];
+  bool ok[CH];
+#pragma unroll
+  for (int cc = 0; cc < CH; ++cc) {
+    cbase[cc] = (ks * CH + cc) * 1024 + lane * 16;
+    ok[cc] = EXACT || cbase[cc] < K;
+  }
+  const auto xcol = [&](int cc) { return EXACT ? cbase[cc] : min(cbase[cc], K - 16); };
+  const auto cbyte = [&](int cc) { return EXACT ? (ks * CH + cc) * 512 + lane * 8 : xcol(cc) >> 1; };
   // Activations of this lane: x[1024c + 16 lane + e], e = 0..15 (PERM: read
   // from LDS after the gather; the staging loads come first).
   v4u xv[CH][2];
   // PERM: 16-byte chunks per thread of x (K / 8 of them) and 32-byte chunks
-  // of the permutation (K / 8); here K = 1024 * CH exactly.
-  constexpr int NX = CH * 128;
-  constexpr int XPT = PERM ? (NX + 64 * NW - 1) / (64 * NW) : 1;
+  // of the permutation (K / 8).
+  constexpr int XPT = PERM ? (CH * KS * 128 + 64 * NW - 1) / (64 * NW) : 1;
+  const int NX = EXACT ? CH * KS * 128 : K >> 3;
   v4u xin[XPT];
   v4i pin[XPT][2];
   if (PERM) {
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
       const int idx = tid + i * 64 * NW;
-      if (i + 1 < XPT || NX % (64 * NW) == 0 || idx < NX) {
+      if ((i + 1) * 64 * NW <= NX || idx < NX) {
         xin[i] = reinterpret_cast<const v4u*>(x)[idx];
         pin[i][0] = reinterpret_cast<const v4i*>(perm)[2 * idx];
         pin[i][1] = reinterpret_cast<const v4i*>(perm)[2 * idx + 1];
@@ -1153,22 +1185,23 @@ __global__ __launch_bounds__(PERM ? 64 * kRowW4PermWaves : 256) void gemv_w4_row
     }
   } else {
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const v4u* src = reinterpret_cast<const v4u*>(x + c * 1024 + lane * 16);
-      xv[c][0] = src[0];
-      xv[c][1] = src[1];
+    for (int cc = 0; cc < CH; ++cc) {
+      const v4u* src = reinterpret_cast<const v4u*>(x + xcol(cc));
+      xv[cc][0] = src[0];
+      xv[cc][1] = src[1];
     }
   }
   __builtin_amdgcn_sched_barrier(0);
   v2u cw[R][CH];
-  // A row's scales and zero points (G <= 64) in one load each: lane l reads
-  // those of group l (its zero-point byte holds groups l and l ^ 1); each
-  // lane later takes its own groups' values from there by lane shuffles.
+  // The scales and zero points of a row's groups in this wave's share (8 CH
+  // <= 64 of them) in one load each: lane l reads those of group 8 ks CH + l
+  // (its zero-point byte holds that group and its neighbour); each lane later
+  // takes its own groups' values from there by lane shuffles.
   int sall[R], zall[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const size_t row = static_cast<size_t>(min(row0 + r, N - 1));
-    const int gl = min(lane, G - 1);
+    const int gl = min(8 * ks * CH + lane, G - 1);
     sall[r] = wscale[row * G + gl];
     zall[r] = ZP ? zeros[row * ZB + (gl >> 1)] : 0;
   }
@@ -1179,7 +1212,7 @@ __global__ __launch_bounds__(PERM ? 64 * kRowW4PermWaves : 256) void gemv_w4_row
     const size_t row = static_cast<size_t>(min(row0 + r, N - 1));
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      cw[r][c] = load_stream<v2u>(codes + row * KB + c * 512 + lane * 8);
+      cw[r][c] = load_stream<v2u>(codes + row * KB + cbyte(c));
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -1189,7 +1222,7 @@ __global__ __launch_bounds__(PERM ? 64 * kRowW4PermWaves : 256) void gemv_w4_row
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
       const int idx = tid + i * 64 * NW;
-      if (i + 1 < XPT || NX % (64 * NW) == 0 || idx < NX) reinterpret_cast<v4u*>(xr)[idx] = xin[i];
+      if ((i + 1) * 64 * NW <= NX || idx < NX) reinterpret_cast<v4u*>(xr)[idx] = xin[i];
     }
     __syncthreads();
     // x[perm[k']] for 8 consecutive k', written in the pair order of the
@@ -1197,7 +1230,7 @@ __global__ __launch_bounds__(PERM ? 64 * kRowW4PermWaves : 256) void gemv_w4_row
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
       const int idx = tid + i * 64 * NW;
-      if (i + 1 < XPT || NX % (64 * NW) == 0 || idx < NX) {
+      if ((i + 1) * 64 * NW <= NX || idx < NX) {
         // an entry outside 0..K-1 reads column K - 1 (the prepare step stores a
         // permutation; this only keeps every LDS read inside x)
         const uint32_t km = static_cast<uint32_t>(K - 1);
@@ -1213,7 +1246,7 @@ __global__ __launch_bounds__(PERM ? 64 * kRowW4PermWaves : 256) void gemv_w4_row
     __syncthreads();
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const v4u* src = reinterpret_cast<const v4u*>(xg + c * 1024 + lane * 16);
+      const v4u* src = reinterpret_cast<const v4u*>(xg + xcol(c));
       xv[c][0] = src[0];
       xv[c][1] = src[1];
     }
@@ -1225,6 +1258,11 @@ __global__ __launch_bounds__(PERM ? 64 * kRowW4PermWaves : 256) void gemv_w4_row
       asm volatile("" : "+v"(xv[c][1]));
     }
   }
+  if (!EXACT) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+      if (!ok[c]) xv[c][0] = xv[c][1] = v4u{0, 0, 0, 0};
+  }
   // Per group (lane l = group l): the fp32 scale, the zero point and, for
   // fp16, the packed fp16 constants -(1024 + z) and -(64 + z) of the decode
   // below; each lane then takes those of its chunk's group.
@@ -1235,11 +1273,11 @@ __global__ __launch_bounds__(PERM ? 64 * kRowW4PermWaves : 256) void gemv_w4_row
   for (int r = 0; r < R; ++r) {
     const uint16_t sb = static_cast<uint16_t>(sall[r]);
     const float sf = BF ? bf16_to_f32(sb) : __half2float(__builtin_bit_cast(__half, sb));
-    const uint32_t zg = ZP ? (static_cast<uint32_t>(zall[r]) >> (4 * (lane & 1))) & 15u : 8u;
+    const uint32_t zg = ZP ? (static_cast<uint32_t>(zall[r]) >> (4 * (lane & 1))) & 15u : 8u;   // 8 ks CH is even
     const uint32_t pl = w4_nz1024(zg), ph = w4_nz64(zg);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const int g = 8 * c + (lane >> 3);
+      const int g = 8 * c + (lane >> 3);          // lane holding this chunk's group
       sv[r][c] = __shfl(sf, g);
       if (BF) {
         zv[r][c] = ZP ? __shfl(static_cast<int>(zg), g) : 8;
@@ -1332,10 +1370,27 @@ __global__ __launch_bounds__(PERM ? 64 * kRowW4PermWaves : 256) void gemv_w4_row
       }
     }
   }
+  if (KS == 1) {
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const float v = wave_sum(acc[r]);
-    if (lane == r && row0 + r < N) store_out(y + row0 + r, v);
+    for (int r = 0; r < R; ++r) {
+      const float v = wave_sum(acc[r]);
+      if (lane == r && row0 + r < N) store_out(y + row0 + r, v);
+    }
+  } else {
+    // the KS waves of a row group meet in LDS and are added in share order
+    float* part = reinterpret_cast<float*>(xstage);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float v = wave_sum(acc[r]);
+      if (lane == 0) part[wave * R + r] = v;
+    }
+    __syncthreads();
+    if (ks == 0 && lane < R && row0 + lane < N) {
+      float v = 0.0f;
+#pragma unroll
+      for (int k2 = 0; k2 < KS; ++k2) v += part[(wave + k2) * R + lane];
+      store_out(y + row0 + lane, v);
+    }
   }
 }
 
@@ -1349,7 +1404,20 @@ constexpr int kRowT2 = 2;
 constexpr int kRowW4 = 2;
 
 bool t2_row_ok(int64_t m, int64_t k) { return m == 1 && k <= 4 * 4096; }
-bool w4_row_ok(int64_t m, int64_t k) { return m == 1 && k % 1024 == 0 && k / 1024 <= 8; }
+// The M = 1 4-bit kernel takes K in chunks of 1024 columns, the last one
+// possibly partial (K % 128 == 0), at most 8 chunks per wave; past 8 chunks
+// 2 or 4 waves share a row group's K.
+bool w4_row_ok(int64_t m, int64_t k) { return m == 1 && k > 0 && k % 128 == 0 && k <= 4 * 8 * 1024; }
+bool w4_row_perm_ok(int64_t m, int64_t k) { return m == 1 && k > 0 && k % 128 == 0 && k <= 8 * 1024; }
+int w4_row_split(int64_t k) {
+  const int64_t c = (k + 1023) / 1024;
+  if (c <= 8) return 1;
+  return c <= 16 ? 2 : 4;
+}
+int w4_row_chunks(int64_t k) {
+  const int ks = w4_row_split(k);
+  return static_cast<int>(((k + 1023) / 1024 + ks - 1) / ks);
+}
 
 unsigned row_blocks(int n, int rows_per_wave) {
   return static_cast<unsigned>(((n + rows_per_wave - 1) / rows_per_wave + 3) / 4);
@@ -1464,7 +1532,8 @@ hipError_t t2_skinny(const bpw_weights& w, const int8_t* q, const float* xs, int
   return hipErrorInvalidValue;
 }
 
-// y[m][n] = x_scale[m] * (part[0][m][n] + part[1][m][n] + ...), slices in order.
+// y[m][n] = x_scale[m] * (part[0][m][n] + part[1][m][n] + ...), slices in
+// order; without x_scale (4-bit weights) the sum itself.
 template <typename TOut>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int splits, int M,
                                                             int N, const float* __restrict__ x_scale,
@@ -1473,7 +1542,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   for (size_t i = blockIdx.x * 256ull + threadIdx.x; i < total; i += gridDim.x * 256ull) {
     float v = part[i];
     for (int sl = 1; sl < splits; ++sl) v += part[sl * total + i];
-    store_out(y + i, v * x_scale[i / N]);
+    store_out(y + i, x_scale ? v * x_scale[i / N] : v);
   }
 }
 
@@ -1615,20 +1684,22 @@ hipError_t w4_go(const bpw_weights& w, const uint16_t* x, int m, TOut* y, hipStr
 // still far ahead of the LDS-tiled kernel, whose staging does not fit M * K
 // at these sizes)
 bool w4_skinny_ok(int64_t m, int64_t k) { return m >= 2 && m <= 16 && k / 128 >= 16 && k / 128 <= 48; }
+bool w4_split_ok(int64_t m, int64_t k) { return m >= 2 && m <= 16 && k / 128 > 48; }
 
 // LDS of the act-order staging: M rows of x (2K bytes + 16 of padding each)
 // and the 4K-byte permutation.
 size_t w4s_perm_lds(int64_t m, int64_t k) { return static_cast<size_t>(m) * (2 * k + 16) + 4 * k; }
 
-template <int GPW, int MAXT, bool BF, bool ZP, bool PERM, typename TOut>
-void w4_skinny_go(const bpw_weights& w, const uint16_t* x, int m, int rpw, int nw, TOut* y, hipStream_t s) {
+template <int GPW, int MAXT, bool BF, bool ZP, bool PERM, typename TOut, bool SPLIT = false>
+void w4_skinny_go(const bpw_weights& w, const uint16_t* x, int m, int rpw, int nw, TOut* y, hipStream_t s,
+                  int splits = 1, float* part = nullptr) {
   const int n = static_cast<int>(w.n), k = static_cast<int>(w.k);
-  auto kern = gemv_w4_skinny_kernel<GPW, MAXT, BF, ZP, TOut, PERM>;
+  auto kern = gemv_w4_skinny_kernel<GPW, MAXT, BF, ZP, TOut, PERM, SPLIT>;
   const size_t lds = w4s_lds_head(nw, MAXT * 16 * GPW) + (PERM ? w4s_perm_lds(m, k) : 0);
   allow_lds(kern, lds);
-  kern<<<(n + rpw - 1) / rpw, nw * 64, lds, s>>>(static_cast<const uint8_t*>(w.codes),
-                                                 static_cast<const uint16_t*>(w.scales),
-                                                 static_cast<const uint8_t*>(w.zeros), x, w.perm, m, n, k, rpw, y);
+  kern<<<dim3((n + rpw - 1) / rpw, splits), nw * 64, lds, s>>>(
+      static_cast<const uint8_t*>(w.codes), static_cast<const uint16_t*>(w.scales),
+      static_cast<const uint8_t*>(w.zeros), x, w.perm, m, n, k, rpw, y, part);
 }
 
 // Launch shape of the skinny 4-bit kernel: rows split evenly over the CUs
@@ -1668,6 +1739,35 @@ hipError_t w4_skinny(const bpw_weights& w, const uint16_t* x, int m, TOut* y, hi
   return hipErrorInvalidValue;
 }
 
+// Split-K of the skinny kernel for 2 <= M <= 16 beyond 48 groups: slices of
+// at most 16 groups (up to 4 waves of 4), as even as 4-group waves allow, and
+// 32 rows per workgroup, then a fixed-order reduce of the slices. Measured on
+// K=13824, N=5120, M=8 (108 groups): 16-group slices and 32 rows 18.0 us;
+// 16-group slices with 64 rows 19.6; 32-group slices with 32 rows 22.6, with
+// 16 rows 30.9, with 64 rows 25.0; 12-group slices 20.1; 8-group 22.1.
+struct W4SplitShape {
+  int splits, nw, rpw;
+};
+
+int w4_split_waves(int64_t k) {
+  const int g = static_cast<int>(k / 128), s0 = (g + 15) / 16;
+  return ((g + s0 - 1) / s0 + 3) / 4;                            // 4-group waves per slice
+}
+int w4_splits(int64_t k) { return static_cast<int>((k / 128 + 4 * w4_split_waves(k) - 1) / (4 * w4_split_waves(k))); }
+
+W4SplitShape w4_split_shape(int64_t k) { return {w4_splits(k), w4_split_waves(k), 32}; }
+
+template <bool BF, bool ZP, typename TOut>
+hipError_t w4_split(const bpw_weights& w, const uint16_t* x, int m, TOut* y, float* part, hipStream_t s) {
+  const W4SplitShape sh = w4_split_shape(w.k);
+  w4_skinny_go<4, 2, BF, ZP, false, TOut, true>(w, x, m, sh.rpw, sh.nw, y, s, sh.splits, part);
+  const int n = static_cast<int>(w.n);
+  const size_t total = static_cast<size_t>(m) * n;
+  const int rblocks = static_cast<int>(std::min<size_t>((total + 255) / 256, 4096));
+  splitk_reduce_kernel<TOut><<<rblocks, 256, 0, s>>>(part, sh.splits, m, n, nullptr, y);
+  return hipGetLastError();
+}
+
 // The skinny kernel gathers the act-order activation itself when K is a
 // multiple of 512 and M rows of x fit in the LDS beside its other arrays.
 bool w4_skinny_perm_ok(int64_t m, int64_t k) {
@@ -1676,21 +1776,23 @@ bool w4_skinny_perm_ok(int64_t m, int64_t k) {
   return w4s_lds_head(sh.nw, 4 * 16 * sh.gpw) + w4s_perm_lds(m, k) <= 160 * 1024;
 }
 
-template <int CH, bool BF, bool ZP, typename TOut>
+template <int CH, int KS, bool EXACT, bool BF, bool ZP, typename TOut>
 void w4_row_go(const bpw_weights& w, const uint16_t* x, TOut* y, hipStream_t s) {
   const int n = static_cast<int>(w.n), k = static_cast<int>(w.k);
-  gemv_w4_row_kernel<kRowW4, CH, BF, ZP, TOut, false><<<row_blocks(n, kRowW4), 256, 0, s>>>(
-      static_cast<const uint8_t*>(w.codes), static_cast<const uint16_t*>(w.scales),
-      static_cast<const uint8_t*>(w.zeros), x, nullptr, n, k, y);
+  const int groups = (n + kRowW4 - 1) / kRowW4, per_block = 4 / KS;
+  gemv_w4_row_kernel<kRowW4, CH, KS, EXACT, BF, ZP, TOut, false>
+      <<<(groups + per_block - 1) / per_block, 256, KS > 1 ? 4 * kRowW4 * sizeof(float) : 0, s>>>(
+          static_cast<const uint8_t*>(w.codes), static_cast<const uint16_t*>(w.scales),
+          static_cast<const uint8_t*>(w.zeros), x, nullptr, n, k, y);
 }
 
 // Act order at M = 1: x in its original column order and the permutation go
 // to the kernel, which gathers in LDS (2 * K halfwords).
-template <int CH, bool BF, bool ZP, typename TOut>
+template <int CH, bool EXACT, bool BF, bool ZP, typename TOut>
 void w4_row_perm_go(const bpw_weights& w, const uint16_t* x, TOut* y, hipStream_t s) {
   const int n = static_cast<int>(w.n), k = static_cast<int>(w.k);
   constexpr int rows = kRowW4Perm * kRowW4PermWaves;
-  gemv_w4_row_kernel<kRowW4Perm, CH, BF, ZP, TOut, true>
+  gemv_w4_row_kernel<kRowW4Perm, CH, 1, EXACT, BF, ZP, TOut, true>
       <<<(n + rows - 1) / rows, 64 * kRowW4PermWaves, 4ull * k, s>>>(
           static_cast<const uint8_t*>(w.codes), static_cast<const uint16_t*>(w.scales),
           static_cast<const uint8_t*>(w.zeros), x, w.perm, n, k, y);
@@ -1699,35 +1801,64 @@ void w4_row_perm_go(const bpw_weights& w, const uint16_t* x, TOut* y, hipStream_
 template <bool BF, bool ZP, typename TOut>
 hipError_t w4_perm_dispatch_f(const bpw_weights& w, const uint16_t* x, int m, TOut* y, hipStream_t s) {
   if (m > 1) return w4_skinny<BF, ZP, true>(w, x, m, y, s);
-  switch (w.k / 1024) {
-    case 1: w4_row_perm_go<1, BF, ZP>(w, x, y, s); break;
-    case 2: w4_row_perm_go<2, BF, ZP>(w, x, y, s); break;
-    case 3: w4_row_perm_go<3, BF, ZP>(w, x, y, s); break;
-    case 4: w4_row_perm_go<4, BF, ZP>(w, x, y, s); break;
-    case 5: w4_row_perm_go<5, BF, ZP>(w, x, y, s); break;
-    case 6: w4_row_perm_go<6, BF, ZP>(w, x, y, s); break;
-    case 7: w4_row_perm_go<7, BF, ZP>(w, x, y, s); break;
-    default: w4_row_perm_go<8, BF, ZP>(w, x, y, s); break;
+#define BPW_W4RP(E_)                                                    \
+  switch ((w.k + 1023) / 1024) {                                        \
+    case 1: w4_row_perm_go<1, E_, BF, ZP>(w, x, y, s); break;           \
+    case 2: w4_row_perm_go<2, E_, BF, ZP>(w, x, y, s); break;           \
+    case 3: w4_row_perm_go<3, E_, BF, ZP>(w, x, y, s); break;           \
+    case 4: w4_row_perm_go<4, E_, BF, ZP>(w, x, y, s); break;           \
+    case 5: w4_row_perm_go<5, E_, BF, ZP>(w, x, y, s); break;           \
+    case 6: w4_row_perm_go<6, E_, BF, ZP>(w, x, y, s); break;           \
+    case 7: w4_row_perm_go<7, E_, BF, ZP>(w, x, y, s); break;           \
+    default: w4_row_perm_go<8, E_, BF, ZP>(w, x, y, s); break;          \
   }
+  if (w.k % 1024 == 0) {
+    BPW_W4RP(true)
+  } else {
+    BPW_W4RP(false)
+  }
+#undef BPW_W4RP
   return hipGetLastError();
 }
 
 template <bool BF, bool ZP, typename TOut>
-hipError_t w4_dispatch_f(const bpw_weights& w, const uint16_t* x, int m, TOut* y, hipStream_t s) {
+hipError_t w4_dispatch_f(const bpw_weights& w, const uint16_t* x, int m, TOut* y, float* part, hipStream_t s) {
   if (w4_row_ok(m, w.k)) {
-    switch (w.k / 1024) {
-      case 1: w4_row_go<1, BF, ZP>(w, x, y, s); break;
-      case 2: w4_row_go<2, BF, ZP>(w, x, y, s); break;
-      case 3: w4_row_go<3, BF, ZP>(w, x, y, s); break;
-      case 4: w4_row_go<4, BF, ZP>(w, x, y, s); break;
-      case 5: w4_row_go<5, BF, ZP>(w, x, y, s); break;
-      case 6: w4_row_go<6, BF, ZP>(w, x, y, s); break;
-      case 7: w4_row_go<7, BF, ZP>(w, x, y, s); break;
-      default: w4_row_go<8, BF, ZP>(w, x, y, s); break;
+    const int ks = w4_row_split(w.k), ch = w4_row_chunks(w.k);
+    const bool exact = w.k == static_cast<int64_t>(ks) * ch * 1024;
+    // a split K has 5..8 chunks per wave (9..16 chunks over 2 waves, 17..32 over 4)
+#define BPW_W4R1(E_)                                                    \
+  switch (ch) {                                                         \
+    case 1: w4_row_go<1, 1, E_, BF, ZP>(w, x, y, s); break;             \
+    case 2: w4_row_go<2, 1, E_, BF, ZP>(w, x, y, s); break;             \
+    case 3: w4_row_go<3, 1, E_, BF, ZP>(w, x, y, s); break;             \
+    case 4: w4_row_go<4, 1, E_, BF, ZP>(w, x, y, s); break;             \
+    case 5: w4_row_go<5, 1, E_, BF, ZP>(w, x, y, s); break;             \
+    case 6: w4_row_go<6, 1, E_, BF, ZP>(w, x, y, s); break;             \
+    case 7: w4_row_go<7, 1, E_, BF, ZP>(w, x, y, s); break;             \
+    default: w4_row_go<8, 1, E_, BF, ZP>(w, x, y, s); break;            \
+  }
+#define BPW_W4RS(KS_, E_)                                               \
+  switch (ch) {                                                         \
+    case 5: w4_row_go<5, KS_, E_, BF, ZP>(w, x, y, s); break;           \
+    case 6: w4_row_go<6, KS_, E_, BF, ZP>(w, x, y, s); break;           \
+    case 7: w4_row_go<7, KS_, E_, BF, ZP>(w, x, y, s); break;           \
+    case 8: w4_row_go<8, KS_, E_, BF, ZP>(w, x, y, s); break;           \
+    default: return hipErrorInvalidValue;                               \
+  }
+    if (ks == 1) {
+      if (exact) { BPW_W4R1(true) } else { BPW_W4R1(false) }
+    } else if (ks == 2) {
+      if (exact) { BPW_W4RS(2, true) } else { BPW_W4RS(2, false) }
+    } else {
+      if (exact) { BPW_W4RS(4, true) } else { BPW_W4RS(4, false) }
     }
+#undef BPW_W4R1
+#undef BPW_W4RS
     return hipGetLastError();
   }
   if (w4_skinny_ok(m, w.k)) return w4_skinny<BF, ZP, false>(w, x, m, y, s);
+  if (w4_split_ok(m, w.k)) return part ? w4_split<BF, ZP>(w, x, m, y, part, s) : hipErrorInvalidValue;
   const int nw = waves_for(w.k / 128);
   const int fold = fold_for(m);
 #define BPW_W4(NW_, F_) \
@@ -1739,11 +1870,11 @@ hipError_t w4_dispatch_f(const bpw_weights& w, const uint16_t* x, int m, TOut* y
 }
 
 template <typename TOut>
-hipError_t w4_dispatch(const bpw_weights& w, const uint16_t* x, bool bf, int m, TOut* y,
+hipError_t w4_dispatch(const bpw_weights& w, const uint16_t* x, bool bf, int m, TOut* y, float* part,
                        hipStream_t s) {
   const bool zp = w.fmt == BPW_INT4_ZP;
-  if (bf) return zp ? w4_dispatch_f<true, true>(w, x, m, y, s) : w4_dispatch_f<true, false>(w, x, m, y, s);
-  return zp ? w4_dispatch_f<false, true>(w, x, m, y, s) : w4_dispatch_f<false, false>(w, x, m, y, s);
+  if (bf) return zp ? w4_dispatch_f<true, true>(w, x, m, y, part, s) : w4_dispatch_f<true, false>(w, x, m, y, part, s);
+  return zp ? w4_dispatch_f<false, true>(w, x, m, y, part, s) : w4_dispatch_f<false, false>(w, x, m, y, part, s);
 }
 
 }  // namespace
@@ -1751,7 +1882,13 @@ hipError_t w4_dispatch(const bpw_weights& w, const uint16_t* x, bool bf, int m, 
 bool gemv_t2_fits(int64_t m, int64_t k) { return m >= 1 && m <= 32; }
 
 bool gemv_w4_fits(int64_t m, int64_t k) {
-  return m >= 1 && m <= 32 && (w4_row_ok(m, k) || w4_skinny_ok(m, k) || static_cast<size_t>(m) * k * 2 <= kLdsBudget);
+  return m >= 1 && m <= 32 &&
+         (w4_row_ok(m, k) || w4_skinny_ok(m, k) || w4_split_ok(m, k) || static_cast<size_t>(m) * k * 2 <= kLdsBudget);
+}
+
+size_t gemv_w4_split_bytes(int64_t m, int64_t n, int64_t k) {
+  if (!w4_split_ok(m, k)) return 0;
+  return static_cast<size_t>(w4_splits(k)) * static_cast<size_t>(m) * static_cast<size_t>(n) * sizeof(float);
 }
 
 bool gemv_t2_group_fits(int64_t m, int64_t k) { return m >= 1 && m <= 32; }
@@ -1793,7 +1930,7 @@ hipError_t launch_gemv_t2_partials(const bpw_weights& w, const int8_t* q, int64_
 }
 
 bool gemv_w4_perm_fits(const bpw_weights& w, int64_t m, const void* x) {
-  return w.perm != nullptr && (w4_row_ok(m, w.k) || w4_skinny_perm_ok(m, w.k)) &&
+  return w.perm != nullptr && (w4_row_perm_ok(m, w.k) || w4_skinny_perm_ok(m, w.k)) &&
          reinterpret_cast<uintptr_t>(x) % 16 == 0 && reinterpret_cast<uintptr_t>(w.perm) % 16 == 0;
 }
 
@@ -1817,14 +1954,14 @@ hipError_t launch_gemv_w4_perm(const bpw_weights& w, const void* x, int x_dtype,
 }
 
 hipError_t launch_gemv_w4(const bpw_weights& w, const void* x_sorted, int x_dtype, int64_t m,
-                          void* y, int y_dtype, hipStream_t s) {
+                          void* y, int y_dtype, float* part, hipStream_t s) {
   const uint16_t* x = static_cast<const uint16_t*>(x_sorted);
   const bool bf = x_dtype == BPW_BF16;
   const int mi = static_cast<int>(m);
   switch (y_dtype) {
-    case BPW_F32: return w4_dispatch(w, x, bf, mi, static_cast<float*>(y), s);
-    case BPW_F16: return w4_dispatch(w, x, bf, mi, static_cast<__half*>(y), s);
-    default: return w4_dispatch(w, x, bf, mi, static_cast<uint16_t*>(y), s);
+    case BPW_F32: return w4_dispatch(w, x, bf, mi, static_cast<float*>(y), part, s);
+    case BPW_F16: return w4_dispatch(w, x, bf, mi, static_cast<__half*>(y), part, s);
+    default: return w4_dispatch(w, x, bf, mi, static_cast<uint16_t*>(y), part, s);
   }
 }
 

@@ -56,8 +56,11 @@ bool gemv_w4_perm_fits(const bpw_weights& w, int64_t m, const void* x);
 hipError_t launch_gemv_w4_perm(const bpw_weights& w, const void* x, int x_dtype, int64_t m, void* y,
                                int y_dtype, hipStream_t s);
 bool gemv_w4_fits(int64_t m, int64_t k);
+// Bytes of fp32 split-K slices the 4-bit decode needs (2 <= M <= 16 beyond 48
+// groups), 0 otherwise; `part` of launch_gemv_w4 must hold that many.
+size_t gemv_w4_split_bytes(int64_t m, int64_t n, int64_t k);
 hipError_t launch_gemv_w4(const bpw_weights& w, const void* x_sorted, int x_dtype, int64_t m,
-                          void* y, int y_dtype, hipStream_t s);
+                          void* y, int y_dtype, float* part, hipStream_t s);
 
 // Prefill GEMMs (gemm_i8.hip, gemm_w4.hip). x operands already in the order
 // the kernels read (int8: plane order; 16-bit: act-order gathered).

@@ -249,6 +249,12 @@ int bpw_workspace_size(const bpw_weights* w, int64_t m, int x_dtype, int entry, 
  * (deterministic). "Kernel experiments: recorded evidence", Test 21: split-K
  * gives the small-output down projection more blocks, and a second kernel adds
  * the partial sums in a fixed order; Test 30: split-K for small-output shapes.
+ * The same for INT4_SYM / INT4_ZP x F16 / BF16 with 2 <= M <= 16 and more than
+ * 48 groups (slices of at most 16 groups); with act order the workspace holds
+ * the gathered activations first, then the slices. At M = 1 a 4-bit K longer
+ * than 8192 is split over the waves of one workgroup instead (no workspace;
+ * the mate PR splits K of its small-M kernel with fp32 partials and a fixed
+ * reduction order).
  */
 int bpw_gemv_packed(const bpw_weights* w, const void* x, int x_dtype, const float* x_scale,
                     int64_t m, void* y, int y_dtype, void* workspace, size_t workspace_bytes,

@@ -159,6 +159,13 @@ def w4a16_decode(m: int = 1) -> Workload:
     return leading_rows(w, m)
 
 
+def w4a16_down(m: int = 1, act_order: bool = True) -> Workload:
+    """The down projection paired with the W4A16 decode layer: K and N swapped
+    (K=13824, N=5120), the same code, zero-point, scale and activation recipe."""
+    w = int4_zp_actorder("w4a16_down", 6, 8, 13824, 5120, act_order=act_order)
+    return leading_rows(w, m)
+
+
 def w4a16_prefill() -> Workload:
     return int4_sym("w4a16_prefill", 3, 2048, 4096, 14336)
 

@@ -258,7 +258,14 @@ def w4_reference(w: synth.Workload, rounded: bool):
 @pytest.mark.parametrize("m,k,n", [(1, 640, 333), (1, 2048, 301), (1, 8192, 66), (1, 3072, 13), (3, 128, 64), (8, 5120, 200),
                                    (16, 1024, 97), (32, 256, 130),
                                    # streaming skinny kernel: 16..48 groups, 4..6 per wave, ragged waves and tiles
-                                   (2, 2048, 1000), (16, 6144, 777), (5, 4224, 3000), (12, 2560, 9000)])
+                                   (2, 2048, 1000), (16, 6144, 777), (5, 4224, 3000), (12, 2560, 9000),
+                                   # M = 1: a partial last 1024-column chunk, and K split over 2 or 4 waves
+                                   # (9088: 5 chunks per wave, the second wave's last one partial and one
+                                   # past K; 20608: 6 per wave; 32768: the longest K, 8 per wave)
+                                   (1, 1152, 77), (1, 9088, 130), (1, 13824, 300), (1, 20608, 50), (1, 32768, 70),
+                                   # 2 <= M <= 16 beyond 48 groups: split-K slices (49 groups: 28 + 21;
+                                   # 108: 28, 28, 28, 24; 256: 8 x 32) and the fixed-order reduce
+                                   (2, 6272, 70), (8, 13824, 300), (16, 8192, 500), (5, 32768, 40)])
 def test_gemv_w4_parity(fmt, x_dtype, act_order, m, k, n):
     w = w4_case(fmt, m, k, n, 300 + m + k + n, act_order, x_dtype)
     pw = prepare(w)
@@ -415,6 +422,20 @@ def test_workload_w4a16_decode_full(m):
     y = bpw.gemv_packed(pw, to_dev(w.x, "f16"))
     torch.cuda.synchronize()
     assert_close(host(y), w4_reference(w, rounded=False), "f16", f"w4a16_decode m={m}")
+
+
+@pytest.mark.parametrize("m", [1, 8])
+@pytest.mark.parametrize("act_order", [True, False])
+def test_w4a16_down_projection_full(m, act_order):
+    # The down projection of the W4A16 decode layer (K=13824, N=5120): at
+    # M = 1 the row kernel with K split over two waves per row pair, at M = 8
+    # the skinny kernel's split-K slices and the reduce; act order gathers in
+    # a separate launch at this K.
+    w = synth.w4a16_down(m, act_order=act_order)
+    pw = prepare(w)
+    y = bpw.gemv_packed(pw, to_dev(w.x, "f16"))
+    torch.cuda.synchronize()
+    assert_close(host(y), w4_reference(w, rounded=False), "f16", f"w4a16 down projection m={m} act_order={act_order}")
 
 
 def test_workload_w4a16_prefill_sampled():

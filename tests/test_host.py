@@ -259,6 +259,18 @@ def test_workspace_sizes():
     wp = _weights(bpw.INT4_ZP, k=5120, zeros=True, perm=True)
     assert lib.bpw_workspace_size(ctypes.byref(wp), 8, bpw.F16, bpw.PATH_GEMV, ctypes.byref(need)) == 0
     assert need.value == 8 * 5120 * 2
+    # 4-bit decode beyond 48 groups, 2 <= M <= 16: the gathered rows (act order), then
+    # fp32 slices; 108 groups make 7 slices of 4 four-group waves (6 x 16, 12)
+    wd = _weights(bpw.INT4_ZP, k=13824, n=5120, zeros=True, perm=True)
+    assert lib.bpw_workspace_size(ctypes.byref(wd), 8, bpw.F16, bpw.PATH_GEMV, ctypes.byref(need)) == 0
+    assert need.value == 8 * 13824 * 2 + 7 * 8 * 5120 * 4
+    wd = _weights(bpw.INT4_SYM, k=6272, n=100)                       # 49 groups: 4 slices of 13 -> 16, 16, 16, 1
+    assert lib.bpw_workspace_size(ctypes.byref(wd), 3, bpw.BF16, bpw.PATH_GEMV, ctypes.byref(need)) == 0
+    assert need.value == 4 * 3 * 100 * 4 + 256 - (4 * 3 * 100 * 4) % 256
+    assert lib.bpw_workspace_size(ctypes.byref(wd), 1, bpw.BF16, bpw.PATH_GEMV, ctypes.byref(need)) == 0
+    assert need.value == 0                                             # M = 1: the row kernel
+    assert lib.bpw_workspace_size(ctypes.byref(wd), 2, bpw.BF16, bpw.PATH_GEMM, ctypes.byref(need)) == 0
+    assert need.value == 0
 
 
 def test_partials_and_probe_validation():
