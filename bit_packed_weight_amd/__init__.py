@@ -384,8 +384,9 @@ def _product(entry: int, w: PackedWeights, x, x_scale=None, out_dtype=None, out=
         raise ValueError("x must be a contiguous [M, K] tensor")
     m = x.shape[0]
     xd = dtype_code(x.dtype)
-    if xd not in (F16, BF16, I8):
-        raise ValueError(f"activations of dtype {x.dtype} are not supported (fp16, bf16 or int8)")
+    if xd not in (F16, BF16, I8) and not (xd == F32 and w.fmt == TERNARY2):
+        raise ValueError(f"activations of dtype {x.dtype} are not supported (fp16, bf16 or int8; fp32 for "
+                         "ternary weights)")
     if xd == I8 and x_scale is not None and x_scale.dim() == 2:
         xd = I8G                                   # one scale per (row, 128-group)
     elif xd == I8 and x_scale is not None and x_scale.dim() == 3:
@@ -401,9 +402,10 @@ def _product(entry: int, w: PackedWeights, x, x_scale=None, out_dtype=None, out=
     elif xd == I8GS:
         _check_tensor("x_scale", x_scale, (m, w.k // 128, 2), (torch.float32,), x.device)
     elif x_scale is not None:
-        raise ValueError("x_scale must be None for fp16/bf16 activations")
+        raise ValueError("x_scale must be None for fp32/fp16/bf16 activations")
     if out is None:
-        out_dtype = out_dtype if out_dtype is not None else (torch.float16 if xd in (I8, I8G, I8GS) else x.dtype)
+        ternary_out = xd in (I8, I8G, I8GS) or w.fmt == TERNARY2
+        out_dtype = out_dtype if out_dtype is not None else (torch.float16 if ternary_out else x.dtype)
         out = torch.empty((m, w.n), dtype=out_dtype, device=x.device)
     _check_tensor("out", out, (m, w.n), (torch.float32, torch.float16, torch.bfloat16), x.device)
     if scratch:

@@ -96,7 +96,15 @@ int check_product(const bpw_weights* w, const void* x, int x_dtype, const float*
   if (m < 1 || m > (int64_t(1) << 30)) return fail(BPW_ESHAPE, "M=%lld outside 1..2^30", (long long)m);
   if (!x || !y) return fail(BPW_EINVAL, "x / y is NULL");
   if (!is_out_dtype(y_dtype)) return fail(BPW_EUNSUPPORTED, "output dtype %d unsupported (F32, F16, BF16)", y_dtype);
-  if (w->fmt == BPW_TERNARY2) {
+  if (w->fmt == BPW_TERNARY2 && (x_dtype == BPW_F32 || x_dtype == BPW_F16 || x_dtype == BPW_BF16)) {
+    // the complete one-token call: the row quantiser fused into the decode GEMV
+    if (x_scale) return fail(BPW_EINVAL, "x_scale must be NULL: the call quantises the activations itself");
+    if (!gemv_t2_fused_fits(m, w->k))
+      return fail(BPW_EUNSUPPORTED,
+                  "ternary weights quantise fp32/fp16/bf16 activations inside the call only at M = 1, K <= 16384 "
+                  "(M=%lld, K=%lld given); quantise with bpw_quantize_rows first",
+                  (long long)m, (long long)w->k);
+  } else if (w->fmt == BPW_TERNARY2) {
     if (x_dtype != BPW_I8 && x_dtype != BPW_I8G)
       return fail(BPW_EUNSUPPORTED, "ternary weights take int8 activations (x_dtype %d given)", x_dtype);
     if (!x_scale) return fail(BPW_EINVAL, x_dtype == BPW_I8 ? "int8 activations need x_scale [M]"
@@ -135,6 +143,8 @@ int check_current_device(void* stream) { return check_device(static_cast<hipStre
 // Workspace bytes for (weights, M, activation type, entry).
 size_t workspace_need(const bpw_weights* w, int64_t m, int x_dtype, int entry) {
   const size_t mk = static_cast<size_t>(m) * static_cast<size_t>(w->k);
+  if (w->fmt == BPW_TERNARY2 && (x_dtype == BPW_F32 || x_dtype == BPW_F16 || x_dtype == BPW_BF16))
+    return 0;                                  // quantised inside the decode kernel
   if (w->fmt == BPW_TERNARY2) {
     if (x_dtype == BPW_I8G && entry == BPW_PATH_GEMV && gemv_t2_group_fits(m, w->k))
       return 0;                                // decode kernels, no staging
@@ -168,6 +178,9 @@ int run_product(bool gemv, const bpw_weights* w, const void* x, int x_dtype, con
   if (int st = check_product(w, x, x_dtype, x_scale, m, y, y_dtype)) return st;
   if (is_int4(w->fmt) && (x_dtype == BPW_I8 || x_dtype == BPW_I8GS) && gemv)
     return fail(BPW_EUNSUPPORTED, "4-bit weights with int8 activations run through bpw_gemm_packed only");
+  const bool t2_float = w->fmt == BPW_TERNARY2 && (x_dtype == BPW_F32 || x_dtype == BPW_F16 || x_dtype == BPW_BF16);
+  if (t2_float && !gemv)
+    return fail(BPW_EUNSUPPORTED, "ternary weights with fp32/fp16/bf16 activations run through bpw_gemv_packed only");
   if (int st = check_workspace(w, m, x_dtype, entry, ws, ws_bytes)) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (int st = check_device(s)) return st;
@@ -180,6 +193,8 @@ int run_product(bool gemv, const bpw_weights* w, const void* x, int x_dtype, con
       return hip_status(launch_gemm_g(*w, qn, x_scale, m, y, y_dtype, s), "4-bit x int8 affine GEMM launch");
     return hip_status(launch_gemm_w4a8(*w, qn, x_scale, m, y, y_dtype, s), "4-bit x int8 GEMM launch");
   }
+  if (t2_float)
+    return hip_status(launch_gemv_t2_fused(*w, x, x_dtype, y, y_dtype, s), "ternary quantise-and-GEMV launch");
   if (w->fmt == BPW_TERNARY2) {
     const int8_t* q = static_cast<const int8_t*>(x);
     if (x_dtype == BPW_I8G && gemv && gemv_t2_group_fits(m, w->k))

@@ -37,6 +37,12 @@ hipError_t launch_gather_cols(const uint16_t* x, const int32_t* perm, int64_t m,
 // Decode GEMVs (gemv.hip). Return hipErrorInvalidValue when the staged
 // activations do not fit the kernel's LDS budget (caller then routes to GEMM).
 bool gemv_t2_fits(int64_t m, int64_t k);
+// The complete decode call for one token on ternary weights: fp32, fp16 or
+// bf16 activations quantised with the row rule inside the M = 1 GEMV (no
+// workspace); M = 1 and K <= 16384.
+bool gemv_t2_fused_fits(int64_t m, int64_t k);
+hipError_t launch_gemv_t2_fused(const bpw_weights& w, const void* x, int x_dtype, void* y, int y_dtype,
+                                hipStream_t s);
 // group_scales: x_scale is [M][K/128] (one scale per row and group) instead of
 // [M]; only the shapes gemv_t2_group_fits accepts.
 bool gemv_t2_group_fits(int64_t m, int64_t k);

@@ -15,6 +15,7 @@
 // and then take the block's maximum as +inf.
 #include "device.h"
 #include "launch.h"
+#include "qrule.h"
 
 namespace bpw {
 namespace {
@@ -86,40 +87,6 @@ __global__ __launch_bounds__(kQThreads) void quantize_rows_kernel(const T* __res
   if (threadIdx.x == 0) x_scale[row] = scale;
 }
 
-// Max over the 64 lanes of a wave (exact in any order): DPP steps within each
-// 16-lane row, then the four row maxima read into scalars.
-__device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)));
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false)));
-  const int vi = __builtin_bit_cast(int, v);
-  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(vi, 0));
-  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(vi, 16));
-  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(vi, 32));
-  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(vi, 48));
-  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
-}
-
-__device__ __forceinline__ void ld4(const float* p, float (&v)[4]) {
-  const v4f t = *reinterpret_cast<const v4f*>(p);
-  v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
-}
-__device__ __forceinline__ void ld4(const __half* p, float (&v)[4]) {
-  const v2u t = *reinterpret_cast<const v2u*>(p);
-  v[0] = __half2float(__builtin_bit_cast(__half, static_cast<uint16_t>(t.x)));
-  v[1] = __half2float(__builtin_bit_cast(__half, static_cast<uint16_t>(t.x >> 16)));
-  v[2] = __half2float(__builtin_bit_cast(__half, static_cast<uint16_t>(t.y)));
-  v[3] = __half2float(__builtin_bit_cast(__half, static_cast<uint16_t>(t.y >> 16)));
-}
-__device__ __forceinline__ void ld4(const uint16_t* p, float (&v)[4]) {
-  const v2u t = *reinterpret_cast<const v2u*>(p);
-  v[0] = __uint_as_float(t.x << 16);
-  v[1] = __uint_as_float(t.x & 0xFFFF0000u);
-  v[2] = __uint_as_float(t.y << 16);
-  v[3] = __uint_as_float(t.y & 0xFFFF0000u);
-}
-
 // The row quantiser for rows whose K is a multiple of 4 with 4-element-aligned
 // vector access: one workgroup of 1024 threads per row, thread t holding the
 // 4 elements at 4t + 4096 j (j < V4), so a 4096-column row is one 16-byte (fp32)
@@ -169,20 +136,12 @@ __global__ __launch_bounds__(1024) void quantize_rows_vec_kernel(const T* __rest
     if (tid == 0) x_scale[row] = __builtin_nanf("");
     return;
   }
-  const float scale = amax * (1.0f / 127.0f);      // fp32 reciprocal constant, one rounding
+  const float scale = row_scale(amax);
   const float div = scale > 0.0f ? scale : 1.0f;
 #pragma unroll
   for (int j = 0; j < V4; ++j) {
     const int64_t i = 4 * static_cast<int64_t>(tid) + 4096 * j;
-    if (i < k) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float r = fminf(fmaxf(rintf(v[j][e] / div), -127.0f), 127.0f);   // IEEE division, ties to even
-        word |= (static_cast<uint32_t>(static_cast<int>(r)) & 0xFFu) << (8 * e);
-      }
-      *reinterpret_cast<uint32_t*>(qr + i) = word;
-    }
+    if (i < k) *reinterpret_cast<uint32_t*>(qr + i) = quantize_word(v[j], div);
   }
   if (tid == 0) x_scale[row] = scale;
 }

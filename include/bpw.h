@@ -232,7 +232,13 @@ int bpw_workspace_size(const bpw_weights* w, int64_t m, int x_dtype, int entry, 
  * GEMM entry return BPW_EUNSUPPORTED), INT4_SYM / INT4_ZP x F16 or BF16
  * (scale_dtype == x_dtype, x_scale NULL). INT4_SYM / INT4_ZP x I8 (either
  * scale dtype, x_scale device fp32 [M]) runs through bpw_gemm_packed only
- * (here BPW_EUNSUPPORTED).
+ * (here BPW_EUNSUPPORTED). TERNARY2 x F32, F16 or BF16 (x_scale NULL) is the
+ * complete decode call for one token: M = 1 and K <= 16384 only (other shapes
+ * BPW_EUNSUPPORTED; quantise with bpw_quantize_rows first), no workspace. The
+ * row is quantised with bpw_quantize_rows' rule inside the GEMV launch, and
+ * y is bit for bit what bpw_quantize_rows followed by the TERNARY2 x I8 call
+ * gives ("Kernel experiments", Test 6: the activation quantiser is part of
+ * the timed decode call; Test 18).
  * Anything else returns BPW_EUNSUPPORTED. y: device [M][N] of y_dtype
  * (F32, F16 or BF16; round-to-nearest-even from fp32).
  * Numerics: int8 -> exact int32 group partials, fp32 fold

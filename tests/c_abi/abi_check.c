@@ -83,9 +83,12 @@ int main(void) {
                         (void*)(uintptr_t)131072, BPW_F16, NULL, 0, NULL) == BPW_ESHAPE,
         "product with K = 200 is refused");
   w.k = K;
-  check(bpw_gemv_packed(&w, (const void*)(uintptr_t)65536, BPW_F16, NULL, 1, (void*)(uintptr_t)131072, BPW_F16,
+  check(bpw_gemv_packed(&w, (const void*)(uintptr_t)65536, BPW_F16, NULL, 2, (void*)(uintptr_t)131072, BPW_F16,
                         NULL, 0, NULL) == BPW_EUNSUPPORTED,
-        "ternary weights with fp16 activations are refused by name");
+        "ternary weights with fp16 activations beyond one token are refused by name");
+  check(bpw_gemv_packed(&w, (const void*)(uintptr_t)65536, BPW_I32, NULL, 1, (void*)(uintptr_t)131072, BPW_F16,
+                        NULL, 0, NULL) == BPW_EUNSUPPORTED,
+        "ternary weights with int32 activations are refused by name");
 
   size_t need = 0;
   check(bpw_workspace_size(&w, 1, BPW_I8, BPW_PATH_GEMV, &need) == BPW_OK && need == 0,

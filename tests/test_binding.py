@@ -52,7 +52,11 @@ def test_activation_width_must_be_k():
 
 
 def test_activation_dtype_and_layout():
-    _refuses("not supported", bpw.gemv_packed, _ternary(), torch.zeros((M, K), dtype=torch.float32))
+    _refuses("not supported", bpw.gemv_packed, _int4_zp(), torch.zeros((M, K), dtype=torch.float32))
+    _refuses("not supported", bpw.gemv_packed, _ternary(), torch.zeros((M, K), dtype=torch.int32))
+    # fp32 rows for ternary weights are the fused one-token call: no x_scale
+    _refuses("x_scale must be None", bpw.gemv_packed, _ternary(), torch.zeros((M, K), dtype=torch.float32),
+             torch.ones(M))
     _refuses("contiguous", bpw.gemv_packed, _ternary(), _q(k=2 * K)[:, ::2], torch.ones(M))
 
 

@@ -704,6 +704,69 @@ def test_products_of_non_finite_rows_are_nan(entry, fmt, m, k, n):
         _check_flagged_rows(outs[0], outs[1], bad_rows)
 
 
+# ------------------------------------------------------------------ one-token complete call
+# Ternary weights with fp32 / fp16 / bf16 activations at M = 1: the row quantiser
+# runs inside the GEMV launch. q, the row scale and the fold are those of the
+# quantiser launch followed by the int8 call, so the output bits must be equal;
+# against the oracle (its quantiser, then its product) the usual rule holds.
+@pytest.mark.parametrize("x_dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("k,n", [(4096, 14336), (512, 256), (1152, 333), (8192, 130), (12288, 77), (16384, 500),
+                                 # N >= 16384: four rows per wave; ragged last workgroup
+                                 (4096, 16387), (640, 3)])
+def test_fused_quantise_gemv_matches_two_launches(x_dtype, k, n):
+    w = ternary_case(1, k, n, 900 + k + n)
+    pw = prepare(w)
+    x_np = w.x.astype(np.float16).astype(np.float32) if x_dtype == "f16" else w.x
+    if x_dtype == "bf16":
+        x_np = (w.x.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)   # exact bf16 values
+    x32 = to_dev(x_np, "f32")
+    x = x32.to(TORCH[x_dtype])
+    assert torch.equal(x.float(), x32)
+    y1 = torch.full((1, n), float("nan"), dtype=torch.float16, device=DEV)
+    bpw.gemv_packed(pw, x, out=y1)
+    q, xs = bpw.quantize_rows(x)
+    y2 = bpw.gemv_packed(pw, q, xs)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    q_ref, xs_ref = quant.quantize_rows(x_np)
+    _, y_ref = reference.ternary_int8_product(q_ref, xs_ref, w.codes, w.scales)
+    assert_close(host(y1), y_ref, "f16", f"fused quantise + GEMV {x_dtype} k={k} n={n}")
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_fused_quantise_gemv_outputs_and_special_rows(out):
+    # every output dtype; an all-zero row gives zeros; a row with a NaN or an
+    # infinity gives a NaN row, as the two-launch call does
+    k, n = 4096, 700
+    w = ternary_case(1, k, n, 931)
+    pw = prepare(w)
+    x = to_dev(w.x, "f32")
+    y = bpw.gemv_packed(pw, x, out_dtype=TORCH[out])
+    q, xs = bpw.quantize_rows(x)
+    y2 = bpw.gemv_packed(pw, q, xs, out_dtype=TORCH[out])
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    z = bpw.gemv_packed(pw, torch.zeros_like(x))
+    torch.cuda.synchronize()
+    assert not torch.any(z.float() != 0)
+    for bad in (float("nan"), float("inf"), float("-inf")):
+        xb = x.clone()
+        xb[0, 1234] = bad
+        yb = bpw.gemv_packed(pw, xb)
+        torch.cuda.synchronize()
+        assert torch.isnan(yb).all()
+
+
+def test_fused_quantise_gemv_through_scratch_entry():
+    w = ternary_case(1, 4096, 1000, 932)
+    pw = prepare(w)
+    x = to_dev(w.x, "f32")
+    y1 = bpw.gemv_packed_scratch(pw, x)
+    y2 = bpw.gemv_packed(pw, x)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
 # ------------------------------------------------------------------ graph replay
 def _graph_cases():
     cases = []

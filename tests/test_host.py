@@ -158,7 +158,7 @@ def test_product_validation_statuses():
     assert _gemv(_weights(), m=0) == bpw.ESHAPE
     assert _gemv(_weights(), x=None) == bpw.EINVAL
     assert _gemv(_weights(), xs=None) == bpw.EINVAL                      # int8 needs row scales
-    assert _gemv(_weights(), x_dtype=bpw.F16, xs=None) == bpw.EUNSUPPORTED
+    assert _gemv(_weights(), x_dtype=bpw.F16, xs=None, m=2) == bpw.EUNSUPPORTED    # fused quantiser: M = 1 only
     assert _gemv(_weights(), y_dtype=bpw.I32) == bpw.EUNSUPPORTED
     assert _gemv(_weights(codes=4100)) == bpw.EALIGN
     assert _gemv(_weights(), x=65540) == bpw.EALIGN
@@ -183,6 +183,26 @@ def test_product_validation_statuses():
     assert "workspace" in bpw.last_error()
     assert _gemv(wp, x_dtype=bpw.F16, xs=None, m=4, ws=1 << 20, ws_bytes=16) == bpw.ESHAPE
     assert _gemv(wp, x_dtype=bpw.F16, xs=None, m=4, ws=(1 << 20) + 16, ws_bytes=1 << 20) == bpw.EALIGN
+
+
+def test_fused_quantise_validation():
+    # ternary weights with fp32 / fp16 / bf16 activations: the one-token complete
+    # call (M = 1, K <= 16384, no x_scale, no workspace, decode entry only)
+    lib = bpw.lib()
+    need = ctypes.c_size_t(7)
+    w = _weights(k=4096, n=300)
+    for xd in (bpw.F32, bpw.F16, bpw.BF16):
+        assert lib.bpw_workspace_size(ctypes.byref(w), 1, xd, bpw.PATH_GEMV, ctypes.byref(need)) == 0
+        assert need.value == 0
+        assert _gemv(w, x_dtype=xd) == bpw.EINVAL                             # x_scale given
+        assert "quantises the activations itself" in bpw.last_error()
+        assert _gemv(w, x_dtype=xd, xs=None, m=2) == bpw.EUNSUPPORTED
+        assert "bpw_quantize_rows first" in bpw.last_error()
+        assert _gemv(_weights(k=16512, n=300), x_dtype=xd, xs=None) == bpw.EUNSUPPORTED
+        assert _gemv(w, x_dtype=xd, xs=None, x=65544) == bpw.EALIGN
+        st = lib.bpw_gemm_packed(ctypes.byref(w), 65536, xd, None, 1, 131072, bpw.F16, None, 0, None)
+        assert st == bpw.EUNSUPPORTED and "bpw_gemv_packed only" in bpw.last_error()
+    assert _gemv(w, x_dtype=bpw.I32, xs=None) == bpw.EUNSUPPORTED
 
 
 def test_group_scale_validation():
