@@ -480,20 +480,6 @@ __global__ __launch_bounds__(64 * kStageWaves) void gemv_t2_stage_kernel(
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<size_t>(stg));
 
   // ---- copies, in the order they are waited for
-  // activations of this wave's groups: 16 tokens x 128 bytes per group, two
-  // 1 KB copies (tokens past M repeat token M - 1; their outputs are dropped)
-#pragma unroll
-  for (int u = 0; u < GPW; ++u) {
-    const int g = min(gb + u, G - 1);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      // token 8h + l / 8, its 16-byte unit (l % 8) ^ token % 8 lands in slot l % 8:
-      // the A reads below, eight tokens at one unit, then fall in distinct banks
-      const int tk = 8 * h + (lane >> 3), m = min(tk, M - 1);
-      lds_dma16(q + static_cast<size_t>(m) * K + g * 128 + 16 * ((lane & 7) ^ (tk & 7)),
-                __builtin_amdgcn_readfirstlane(lds0 + L.oa + ((wave * GPW + u) * 2 + h) * 1024));
-    }
-  }
   // the workgroup's scale block (nrow x G fp16, contiguous; G % 8 == 0 keeps
   // it whole 16-byte pieces) and the activation scales, one piece per wave
   // from wave 0 on: 1 KB pieces, or M floats 4 bytes per lane. (A transposed
@@ -519,6 +505,25 @@ __global__ __launch_bounds__(64 * kStageWaves) void gemv_t2_stage_kernel(
       }
     }
   }
+  // activations of this wave's groups: 16 tokens x 128 bytes per group, two
+  // 1 KB copies (tokens past M repeat token M - 1; their outputs are dropped)
+#pragma unroll
+  for (int u = 0; u < GPW; ++u) {
+    const int g = min(gb + u, G - 1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      // token 8h + l / 8, its 16-byte unit (l % 8) ^ token % 8 lands in slot l % 8:
+      // the A reads below, eight tokens at one unit, then fall in distinct banks
+      const int tk = 8 * h + (lane >> 3), m = min(tk, M - 1);
+      lds_dma16(q + static_cast<size_t>(m) * K + g * 128 + 16 * ((lane & 7) ^ (tk & 7)),
+                __builtin_amdgcn_readfirstlane(lds0 + L.oa + ((wave * GPW + u) * 2 + h) * 1024));
+    }
+  }
+  // every wave's scale and activation copies go out before any wave's code
+  // rows (an execution barrier; it waits for no copy)
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
   // one code row per tile (rows past the workgroup's share repeat its last
   // row): tiles 0 and 1 now, each later one after the tile two before it is
   // computed, so two tiles are in flight (PARTIALS: all four now)
@@ -536,12 +541,20 @@ __global__ __launch_bounds__(64 * kStageWaves) void gemv_t2_stage_kernel(
     copy_tile(3);
   }
 
-  // ---- tile 0, the activations and the scales have landed for every wave
+  // ---- this wave's activations have landed (tiles 0 and 1 are in flight)
   // (PARTIALS stores inside the tile loop, and stores count in vmcnt too: that
   // verification path waits for every copy here instead)
-  if (PARTIALS) wait_vmcnt<0>();
-  else wait_vmcnt<1>();
-  __syncthreads();
+  if (PARTIALS) {
+    wait_vmcnt<0>();
+    __syncthreads();
+  } else {
+    // (the compiler sees neither the copies nor this wait as LDS traffic:
+    // the reads below are pinned after it)
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<2>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  }
   // A operands: token n, columns 32j + 16e .. + 15 of group u, as the 4x4
   // byte transpose the code planes need (plane p, byte i <-> column 4i + p)
   v4i a[GPW][2], cneg[GPW];
@@ -560,6 +573,11 @@ __global__ __launch_bounds__(64 * kStageWaves) void gemv_t2_stage_kernel(
     v4i c = {0, 0, 0, 0};
     c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u][0], neg1, c, 0, 0, 0);
     cneg[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u][1], neg1, c, 0, 0, 0);
+  }
+  // ---- tile 0 and every wave's scales have landed
+  if (!PARTIALS) {
+    wait_vmcnt<1>();
+    __syncthreads();
   }
   float acc[T][4];
 #pragma unroll
@@ -1012,6 +1030,11 @@ __global__ __launch_bounds__(PERM ? 1024 : 512) void gemv_w4_skinny_kernel(
       const uint32_t dst = lbase + (isx ? m * xs : M * xs) + piece * 1024;
       lds_dma16(src + lane * 16, __builtin_amdgcn_readfirstlane(dst));
     }
+    // every wave's copies go out before any wave's code stream (an execution
+    // barrier; it waits for no load): measured at M=8, K=5120, N=13824
+    // 15.0-15.2 -> 14.3-14.5 us
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
   }
   __builtin_amdgcn_sched_barrier(0);
   // The code stream, group-tile q = t * GPW + u. Without PERM every load is
@@ -1027,16 +1050,18 @@ __global__ __launch_bounds__(PERM ? 1024 : 512) void gemv_w4_skinny_kernel(
     cw[t][u] = *reinterpret_cast<const v4u*>(crow[t] + min(gb + u, G - 1) * 64);
     __builtin_amdgcn_sched_barrier(0);
   };
-#pragma unroll
-  for (int q = 0; q < PD; ++q) issue(q);
   // A operands: each 8-column chunk in the order [0, 4, 1, 5, 2, 6, 3, 7].
   // Token rows n >= M read row M - 1 (their outputs are never stored).
   v4u a[GPW][4];
   const int mA = min(n, M - 1);
+  v4u ain[GPW][4];
   if (!PERM) {
-    // Activations, issued after the code stream (measured a little faster
-    // than ahead of it).
-    v4u ain[GPW][4];
+    // Activations first, every wave's ahead of any wave's code stream (an
+    // execution barrier; it waits for no load), so the L2-resident rows do
+    // not queue behind HBM code loads and tile 0 can start as its codes land
+    // (measured on the split form at M=8, K=13824, N=5120: 17.9 -> 17.2 us;
+    // without the barrier, activations issued after the code stream had been
+    // a little faster than ahead of it).
 #pragma unroll
     for (int u = 0; u < GPW; ++u) {
       const int g = min(gb + u, G - 1);
@@ -1044,6 +1069,13 @@ __global__ __launch_bounds__(PERM ? 1024 : 512) void gemv_w4_skinny_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) ain[u][i] = src[i];
     }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int q = 0; q < PD; ++q) issue(q);
+  if (!PERM) {
 #pragma unroll
     for (int u = 0; u < GPW; ++u)
 #pragma unroll
