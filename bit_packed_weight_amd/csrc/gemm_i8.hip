@@ -269,6 +269,15 @@ __global__ __launch_bounds__(NT, 1) void gemm_t2_kernel(
   auto group = [&](int g, auto BUFC) __attribute__((always_inline)) {
     constexpr int BUF = decltype(BUFC)::value;
     const int gn = min(g + 1, G - 1);
+    // The next group's raw weights: 4-bit codes (32 bytes a lane) go out first
+    // in the group, ternary codes after the first chain (measured: 4-bit at
+    // M=2048, K=4096, N=14336 200.6 -> 195.4 us; ternary at M=4096, K=8192,
+    // N=28672 1148 -> 1199 us if moved too).
+    Raw nraw;
+    if (W4) {
+      raw_load(nraw, gn);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     a_read(IntC<BUF>{}, IntC<0>{}, aop[0]);
     // The other buffer was last read before the previous barrier.
     a_load(gn, BUF ^ 1);
@@ -288,9 +297,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_t2_kernel(
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    Raw nraw;
-    raw_load(nraw, gn);
-    __builtin_amdgcn_sched_barrier(0);
+    if (!W4) {
+      raw_load(nraw, gn);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // Chains (0,1) (1,0) (1,1) ... (3,1); each folds its predecessor. Token
     // tile i + 1 is read during chain (i, 0), into the registers that chain
     // (i - 1, 1) used, and waited for before chain (i + 1, 0).
