@@ -2,8 +2,8 @@
 scratch in place of a caller workspace. Its output must equal bpw_gemv_packed's
 bit for bit (same kernels, fixed-order sums) and meet the oracle's parity rule,
 on two calls in a row whose second input is smaller, for each workload that
-needs a workspace (ternary split-K slices, the 4-bit act-order gather) and one
-that needs none. A call whose workspace would exceed the scratch is refused
+needs a workspace (ternary split-K slices, the 4-bit act-order gather, 4-bit
+split-K slices behind the gather) and one that needs none. A call whose workspace would exceed the scratch is refused
 before any launch (CPU test)."""
 import ctypes
 
@@ -53,6 +53,26 @@ def test_scratch_matches_workspace_entry_w4_act_order():
     for m, k, n, seed in [(8, 5120, 2000, 63), (1, 1024, 300, 64)]:
         print(f"[scratch] w4 act-order m={m} k={k} n={n}", flush=True)
         w = synth.int4_zp_actorder(f"scratch_w{m}_{k}_{n}", seed, m, k, n)
+        pw = bpw.prepare_packed(bpw.INT4_ZP, w.codes, w.scales, w.zeros, w.g_idx)
+        x = torch.from_numpy(w.x).to(DEV)
+        assert 0 < bpw.workspace_size(pw, m, bpw.F16, bpw.PATH_GEMV) <= bpw.SCRATCH_BYTES
+        y_ws = bpw.gemv_packed(pw, x)
+        y = torch.full((m, n), float("nan"), dtype=torch.float16, device=DEV)
+        bpw.gemv_packed_scratch(pw, x, out=y)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(_host(y), _host(y_ws))
+        wd = reference.weights_int4(w.codes, w.scales_f64(), w.zeros, w.g_idx)
+        r = compare.compare(_host(y), reference.product(w.x_f32(), wd), "f16")
+        assert r["ok"], r
+
+
+@pytest.mark.gpu
+def test_scratch_matches_workspace_entry_w4_split_k():
+    # 4-bit beyond 48 groups at 2 <= M <= 16: the gathered rows, then the fp32 slices in the
+    # scratch; the second call is smaller and has no act order (slices only)
+    for m, k, n, seed, act in [(8, 13824, 1500, 66, True), (3, 6272, 700, 67, False)]:
+        print(f"[scratch] w4 split-K m={m} k={k} n={n} act_order={act}", flush=True)
+        w = synth.int4_zp_actorder(f"scratch_ws{m}_{k}_{n}", seed, m, k, n, act_order=act)
         pw = bpw.prepare_packed(bpw.INT4_ZP, w.codes, w.scales, w.zeros, w.g_idx)
         x = torch.from_numpy(w.x).to(DEV)
         assert 0 < bpw.workspace_size(pw, m, bpw.F16, bpw.PATH_GEMV) <= bpw.SCRATCH_BYTES
