@@ -780,6 +780,11 @@ def _graph_cases():
     cases.append(("w4 gemv act", w4_case("int4_zp", 8, 5120, 700, 712, True, "f16"), "gemv", "float"))
     cases.append(("w4 gemm", w4_case("int4_sym", 300, 1024, 520, 713, False, "bf16"), "gemm", "float"))
     cases.append(("w4a8 gemm", w4_case("int4_zp", 200, 1024, 520, 714, True, "f16"), "gemm", "rows"))
+    # the one-launch complete call (fp32 row quantised in the GEMV); 4-bit long K: the M = 1
+    # K split over waves, and split-K slices + reduce behind the act-order gather at M = 8
+    cases.append(("t2 fused", ternary_case(1, 4096, 1000, 715), "gemv", "fp32"))
+    cases.append(("w4 gemv long k", w4_case("int4_zp", 1, 13824, 500, 716, False, "f16"), "gemv", "float"))
+    cases.append(("w4 gemv split", w4_case("int4_zp", 8, 13824, 700, 717, True, "f16"), "gemv", "float"))
     return cases
 
 
@@ -793,6 +798,9 @@ def test_graph_replay_matches_eager():
         if act == "float":
             args = (to_dev(w.x, w.x_dtype),)
             xd = bpw.dtype_code(TORCH[w.x_dtype])
+        elif act == "fp32":
+            args = (to_dev(w.x_f32(), "f32"),)
+            xd = bpw.F32
         else:
             x = to_dev(w.x_f32(), "f32")
             args = bpw.quantize_rows(x) if act == "rows" else bpw.quantize_groups(x)
