@@ -360,7 +360,11 @@ def test_ternary_degenerate_shapes(entry, m, k, n):
 
 
 @pytest.mark.parametrize("fmt,x_dtype,entry,m,k,n", [("int4_zp", "f16", "gemv", 1, 1024, 1), ("int4_sym", "bf16", "gemv", 16, 2048, 1),
-                                                     ("int4_zp", "f16", "gemv", 33, 128, 40), ("int4_sym", "bf16", "gemm", 1, 128, 1)])
+                                                     ("int4_zp", "f16", "gemv", 33, 128, 40), ("int4_sym", "bf16", "gemm", 1, 128, 1),
+                                                     # one output row: K split over waves (M = 1), one
+                                                     # split-K slice holding a single group (M = 2, 49 groups)
+                                                     ("int4_zp", "f16", "gemv", 1, 9088, 1), ("int4_sym", "bf16", "gemv", 1, 32768, 3),
+                                                     ("int4_zp", "f16", "gemv", 2, 6272, 1), ("int4_sym", "bf16", "gemv", 16, 16384, 17)])
 def test_w4_degenerate_shapes(fmt, x_dtype, entry, m, k, n):
     w = w4_case(fmt, m, k, n, 1200 + m + k + n, fmt == "int4_zp", x_dtype)
     pw = prepare(w)
