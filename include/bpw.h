@@ -309,6 +309,8 @@ int bpw_gemv_packed_scratch(const bpw_weights* w, const void* x, int x_dtype, co
  * Ternary x I8G (one activation scale per (row, 128-group), "Kernel
  * experiments", Test 7's fold partial * x_scale * w_scale per group):
  * y = sum_g x_scale[m,g] * scale[n,g] * P[m,n,g]; workspace M * K bytes.
+ * Ternary x F32 / F16 / BF16 (the one-token complete call) runs through
+ * bpw_gemv_packed only (here BPW_EUNSUPPORTED).
  */
 int bpw_gemm_packed(const bpw_weights* w, const void* x, int x_dtype, const float* x_scale,
                     int64_t m, void* y, int y_dtype, void* workspace, size_t workspace_bytes,
