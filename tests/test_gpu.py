@@ -119,7 +119,10 @@ def run_ternary(w: synth.Workload, entry: str):
                                    (32, 8192, 3000), (9, 3072, 20000), (24, 6144, 9000), (16, 14336, 4096),
                                    (4, 11008, 700), (1, 20480, 500), (1, 14336, 1000), (1, 1152, 333),
                                    # M = 1, N >= 16384: four rows per wave, ragged last wave, one and four chunks
-                                   (1, 4096, 16387), (1, 16384, 16390)])
+                                   (1, 4096, 16387), (1, 16384, 16390),
+                                   # 2 <= M <= 16 up to K = 4096: one 16-row tile per wave, a last workgroup
+                                   # with one row or half a tile, waves without rows, 56-row shares
+                                   (2, 2048, 33), (16, 1024, 5000), (13, 4096, 14001)])
 @pytest.mark.parametrize("out", ["f32", "f16", "bf16"])
 def test_gemv_ternary_parity(m, k, n, out):
     w = ternary_case(m, k, n, 100 + m + k + n, out)
@@ -193,7 +196,8 @@ def test_gemm_ternary_parity(m, k, n):
                                        (1, 128, 40, (0, 1, 7, 9)), (1, 4096, 77, (0, 1, 3, 70)),
                                        (1, 8192, 9, (0, 1, 0, 9)), (16, 8192, 600, (3, 14, 100, 580)),
                                        (12, 3072, 20000, (0, 12, 9000, 9777)), (3, 12288, 500, (0, 3, 17, 463)),
-                                       (1, 5248, 300, (0, 1, 0, 300)), (1, 2048, 16400, (0, 1, 15990, 16400))])
+                                       (1, 5248, 300, (0, 1, 0, 300)), (1, 2048, 16400, (0, 1, 15990, 16400)),
+                                       (16, 4096, 1000, (0, 16, 0, 1000)), (2, 1024, 33, (1, 2, 5, 30))])
 def test_partials_bit_exact(path, m, k, n, win):
     # stress inputs: full int8 range and every 2-bit code including 3
     rng = np.random.default_rng(m + k + n)
