@@ -527,7 +527,10 @@ def w4a8_reference(w, q_ref, xs_ref, rows=None, cols=None):
 @pytest.mark.parametrize("fmt,scale_dtype,act_order", [("int4_sym", "bf16", False), ("int4_zp", "f16", True),
                                                        ("int4_zp", "f16", False), ("int4_sym", "f16", True)])
 @pytest.mark.parametrize("m,k,n", [(1, 256, 300), (130, 1024, 520), (300, 640, 257), (64, 128, 256),
-                                   (129, 2048, 1000)])
+                                   (129, 2048, 1000),
+                                   # K % 1024 == 0: codes two groups ahead through LDS, scale and zero-point
+                                   # rows staged per tile; ragged last weight tile, 32 and 64 groups
+                                   (257, 4096, 300), (40, 8192, 513)])
 def test_gemm_w4a8_parity(fmt, scale_dtype, act_order, m, k, n):
     w, q_ref, xs_ref = w4a8_case(fmt, m, k, n, 400 + m + k + n, act_order, scale_dtype)
     pw = prepare(w)
@@ -551,7 +554,8 @@ def test_gemm_w4a8_output_dtypes(out):
 
 @pytest.mark.parametrize("fmt,act_order", [("int4_sym", False), ("int4_zp", True), ("int4_zp", False)])
 @pytest.mark.parametrize("m,k,n,win", [(3, 256, 70, (0, 3, 0, 70)), (300, 640, 520, (5, 290, 33, 510)),
-                                       (130, 1024, 260, (128, 130, 255, 260))])
+                                       (130, 1024, 260, (128, 130, 255, 260)), (129, 4096, 300, (1, 129, 250, 300)),
+                                       (64, 2048, 257, (0, 64, 0, 257))])
 def test_partials_w4a8_bit_exact(fmt, act_order, m, k, n, win):
     # stress inputs: the full int8 range, every code and zero point
     rng = np.random.default_rng(m + k + n + 5)
