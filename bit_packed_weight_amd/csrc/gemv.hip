@@ -462,21 +462,31 @@ __host__ __device__ inline T2StageLds t2_stage_lds(int K, int G, int gpw, int xs
   return l;
 }
 
-template <int GPW, typename TOut, bool PARTIALS, bool GS>
+// SPLIT: slice blockIdx.y of 32 groups (4096 columns; the last slice what is
+// left, a multiple of 1024) per workgroup, its fp32 sums before the activation
+// scale written to part[slice][m][n] for splitk_reduce_kernel, which adds the
+// slices in slice order and applies x_scale.
+template <int GPW, typename TOut, bool PARTIALS, bool GS, bool SPLIT = false>
 __global__ __launch_bounds__(64 * kStageWaves) void gemv_t2_stage_kernel(
     const uint8_t* __restrict__ codes, const __half* __restrict__ wscale,
     const int8_t* __restrict__ q, const float* __restrict__ x_scale, int M, int N, int K, int rpw,
-    TOut* __restrict__ y, int32_t* __restrict__ pout, int pm0, int pm1, int pn0, int pn1) {
+    TOut* __restrict__ y, int32_t* __restrict__ pout, int pm0, int pm1, int pn0, int pn1, float* __restrict__ part) {
   constexpr int NW = kStageWaves, T = kStageTiles;
+  static_assert(!SPLIT || (!PARTIALS && !GS), "the K-sliced form takes row scales only");
   extern __shared__ __align__(16) uint8_t stg[];
-  const int G = K >> 7, KB = K >> 2;
+  // G, KB: groups and code bytes per row of this workgroup's K range (the
+  // whole K, or one slice); GA, KBA: of the whole row
+  const int GA = K >> 7, KBA = K >> 2;
+  const int sl = SPLIT ? static_cast<int>(blockIdx.y) : 0;
+  const int g0 = 32 * sl;                                   // first group of the slice
+  const int G = SPLIT ? min(32, GA - g0) : GA, KB = 32 * G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, j = lane >> 4;
   const int r0 = blockIdx.x * rpw;
   const int nrow = min(rpw, N - r0);                       // >= 1
   const int gb = wave * GPW;
-  const int xs_bytes = PARTIALS ? 0 : (GS ? M * G * 4 : M * 4);
-  const T2StageLds L = t2_stage_lds(K, G, GPW, xs_bytes);
+  const int xs_bytes = (PARTIALS || SPLIT) ? 0 : (GS ? M * G * 4 : M * 4);
+  const T2StageLds L = t2_stage_lds(128 * G, G, GPW, xs_bytes);
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<size_t>(stg));
 
   // ---- copies, in the order they are waited for
@@ -487,12 +497,17 @@ __global__ __launch_bounds__(64 * kStageWaves) void gemv_t2_stage_kernel(
   // measured slower: 7.23 against 7.06 us at M=16.)
   if (!PARTIALS) {
     const int sb = nrow * G * 2, npieces = (sb + 1023) >> 10;
-    const int xpieces = GS ? (xs_bytes + 1023) >> 10 : 1;
+    const int xpieces = SPLIT ? 0 : GS ? (xs_bytes + 1023) >> 10 : 1;
     if (wave < npieces) {
       const int off = wave * 1024 + lane * 16;
-      if (off < sb)
-        lds_dma16(reinterpret_cast<const uint8_t*>(wscale) + static_cast<size_t>(r0) * G * 2 + off,
+      if (off < sb) {
+        // (a slice's rows are G of the row's GA scales: row off / (2G), piece
+        // of it (off % (2G)) / 16; 2G is a multiple of 16)
+        const size_t src = SPLIT ? (static_cast<size_t>(r0) + off / (2 * G)) * GA * 2 + g0 * 2 + off % (2 * G)
+                                 : static_cast<size_t>(r0) * G * 2 + off;
+        lds_dma16(reinterpret_cast<const uint8_t*>(wscale) + src,
                   __builtin_amdgcn_readfirstlane(lds0 + L.os + wave * 1024));
+      }
     } else if (wave < npieces + xpieces) {
       const int pc = wave - npieces;
       if (GS) {
@@ -515,7 +530,7 @@ __global__ __launch_bounds__(64 * kStageWaves) void gemv_t2_stage_kernel(
       // token 8h + l / 8, its 16-byte unit (l % 8) ^ token % 8 lands in slot l % 8:
       // the A reads below, eight tokens at one unit, then fall in distinct banks
       const int tk = 8 * h + (lane >> 3), m = min(tk, M - 1);
-      lds_dma16(q + static_cast<size_t>(m) * K + g * 128 + 16 * ((lane & 7) ^ (tk & 7)),
+      lds_dma16(q + static_cast<size_t>(m) * K + (g0 + g) * 128 + 16 * ((lane & 7) ^ (tk & 7)),
                 __builtin_amdgcn_readfirstlane(lds0 + L.oa + ((wave * GPW + u) * 2 + h) * 1024));
     }
   }
@@ -530,7 +545,7 @@ __global__ __launch_bounds__(64 * kStageWaves) void gemv_t2_stage_kernel(
   auto copy_tile = [&](int t) {
     const int row = min(16 * t + wave, nrow - 1);
     if (lane * 16 < KB)
-      lds_dma16(codes + static_cast<size_t>(r0 + row) * KB + lane * 16,
+      lds_dma16(codes + static_cast<size_t>(r0 + row) * KBA + 32 * g0 + lane * 16,
                 __builtin_amdgcn_readfirstlane(lds0 + L.oc + (16 * t + wave) * L.rs));
   };
   static_assert(T == 4, "the copy schedule and the waits below count four tiles");
@@ -644,8 +659,12 @@ __global__ __launch_bounds__(64 * kStageWaves) void gemv_t2_stage_kernel(
 #pragma unroll
     for (int w = 0; w < NW; ++w) v += red[((t * NW + w) * 4 + r) * 64 + l];
     const int mm = 4 * (l >> 4) + r, rl = 16 * t + (l & 15);
-    if (!GS) v *= reinterpret_cast<const float*>(stg + L.ox)[min(mm, M - 1)];
-    if (mm < M && rl < nrow) store_out(y + static_cast<size_t>(mm) * N + r0 + rl, v);
+    if (SPLIT) {
+      if (mm < M && rl < nrow) part[(static_cast<size_t>(sl) * M + mm) * N + r0 + rl] = v;
+    } else {
+      if (!GS) v *= reinterpret_cast<const float*>(stg + L.ox)[min(mm, M - 1)];
+      if (mm < M && rl < nrow) store_out(y + static_cast<size_t>(mm) * N + r0 + rl, v);
+    }
   }
 }
 
@@ -1770,10 +1789,40 @@ hipError_t t2_stage(const bpw_weights& w, const int8_t* q, const float* xs, int 
     allow_lds(kern, L.total);
     kern<<<blocks, 64 * kStageWaves, L.total, s>>>(static_cast<const uint8_t*>(w.codes),
                                                      static_cast<const __half*>(w.scales), q, xs, m, n, k, rpw, y,
-                                                     pout, pm0, pm1, pn0, pn1);
+                                                     pout, pm0, pm1, pn0, pn1, nullptr);
   };
   if (gpw == 1) go(gemv_t2_stage_kernel<1, TOut, PARTIALS, GS>);
   else go(gemv_t2_stage_kernel<2, TOut, PARTIALS, GS>);
+  return hipGetLastError();
+}
+
+// The staged kernel over K slices of 32 groups (2 <= M <= 16, K > 4096 a
+// multiple of 1024, row scales), then the fixed-order reduce of the slices.
+// Rows per workgroup: the fewest (a multiple of 8, 16..64) whose row blocks
+// times slices fit one workgroup per CU.
+bool t2_stage_split_ok(int64_t m, int64_t k, const void* q, const void* codes) {
+  return m >= 2 && m <= 16 && k > 4096 && k % 1024 == 0 && reinterpret_cast<uintptr_t>(q) % 16 == 0 &&
+         reinterpret_cast<uintptr_t>(codes) % 16 == 0;
+}
+
+template <typename TOut>
+hipError_t t2_stage_split(const bpw_weights& w, const int8_t* q, const float* xs, int m, TOut* y, float* part,
+                          hipStream_t s) {
+  const int n = static_cast<int>(w.n), k = static_cast<int>(w.k);
+  const int splits = t2_splits(k);                          // slices of 32 groups
+  const int cus = cu_count();
+  int rpw = 16;
+  while (rpw < 16 * kStageTiles && static_cast<int64_t>((n + rpw - 1) / rpw) * splits > cus) rpw += 8;
+  const T2StageLds L = t2_stage_lds(4096, 32, 2, 0);
+  const dim3 grid((n + rpw - 1) / rpw, splits);
+  auto kern = gemv_t2_stage_kernel<2, TOut, false, false, true>;
+  allow_lds(kern, L.total);
+  kern<<<grid, 64 * kStageWaves, L.total, s>>>(static_cast<const uint8_t*>(w.codes),
+                                               static_cast<const __half*>(w.scales), q, xs, m, n, k, rpw, y,
+                                               nullptr, 0, 0, 0, 0, part);
+  const size_t total = static_cast<size_t>(m) * n;
+  const int rblocks = static_cast<int>(std::min<size_t>((total + 255) / 256, 4096));
+  splitk_reduce_kernel<TOut><<<rblocks, 256, 0, s>>>(part, splits, m, n, xs, y);
   return hipGetLastError();
 }
 
@@ -1793,6 +1842,7 @@ hipError_t t2_dispatch(const bpw_weights& w, const int8_t* q, const float* xs, i
   }
   if (t2_row_ok(m, w.k)) return t2_row<TOut, false>(w, q, xs, y, nullptr, 0, 0, s);
   if (t2_skinny_ok(m, w.k)) return t2_skinny<TOut, false>(w, q, xs, m, y, nullptr, 0, 0, 0, 0, s);
+  if (part && t2_stage_split_ok(m, w.k, q, w.codes)) return t2_stage_split<TOut>(w, q, xs, m, y, part, s);
   if (part && t2_split_ok(m, w.k)) return t2_split<TOut>(w, q, xs, m, y, part, s);
   if (t2_long_ok(m, w.k)) return t2_long<TOut, false>(w, q, xs, m, y, nullptr, 0, 0, 0, 0, s);
   return hipErrorInvalidValue;

@@ -133,7 +133,10 @@ def test_gemv_ternary_parity(m, k, n, out):
 # Split-K decode (2 <= M <= 32 beyond 32 groups): slices of 32 groups side by
 # side, fp32 partials summed in slice order. Ragged last slices (2 and 1
 # groups), M past 16, and a repeat that must be bit-identical.
-@pytest.mark.parametrize("m,k,n", [(16, 14336, 4096), (5, 4352, 1000), (32, 8320, 777), (2, 16384, 64)])
+@pytest.mark.parametrize("m,k,n", [(16, 14336, 4096), (5, 4352, 1000), (32, 8320, 777), (2, 16384, 64),
+                                   # K a multiple of 1024, M <= 16: the staged kernel over 32-group slices
+                                   # (last slice of 8 and 16 groups, one-row and ragged workgroups)
+                                   (16, 5120, 300), (3, 8192, 1000), (16, 14336, 33), (7, 30720, 2000)])
 def test_gemv_ternary_split_k(m, k, n):
     w = ternary_case(m, k, n, 900 + m + k + n, "f16")
     pw = prepare(w)
