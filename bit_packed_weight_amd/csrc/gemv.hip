@@ -172,17 +172,22 @@ __global__ __launch_bounds__((std::is_same<TX, int8_t>::value ? 256 : 64 * kFuse
     const bool bad = __builtin_isinf(amax);
     fused_scale = bad ? __builtin_nanf("") : row_scale(amax);
     const float div = fused_scale > 0.0f ? fused_scale : 1.0f;
+    // q word w of 64-byte slot l = w / 16 (the 64 bytes one lane reads) goes to
+    // 16-byte unit ((w / 4) % 4) ^ (l / 4 % 4) of the slot: the 16 lanes of
+    // one 16-byte LDS read then cover all 64 banks (a 4-way conflict
+    // unswizzled)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int i = 4 * tid + 256 * NW * j;
-      if (i < K) qlds[i >> 2] = bad ? 0u : quantize_word(xf[j], div);
+      const int w = i >> 2;
+      if (i < K) qlds[(w & ~15) | ((((w >> 2) ^ (w >> 6)) & 3) << 2) | (w & 3)] = bad ? 0u : quantize_word(xf[j], div);
     }
     __syncthreads();
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const v4u* src = reinterpret_cast<const v4u*>(reinterpret_cast<const uint8_t*>(qlds) + min(c * 4096 + lane * 64, K - 64));
+      const int l = min(c * 64 + lane, (K >> 6) - 1);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) qin[c][i] = src[i];
+      for (int i = 0; i < 4; ++i) qin[c][i] = *reinterpret_cast<const v4u*>(qlds + 16 * l + 4 * (i ^ ((l >> 2) & 3)));
     }
   }
   v4u qp[CH][4];
