@@ -198,8 +198,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_t2_kernel(
   // of a wave's slot keeps its four 16-byte units at r * 64 + 16 (u ^ ((r >>
   // 2) & 3)): the 16 rows that one quarter-wave reads then cover all 64 banks.
   // (Measured at M=2048, K=4096, N=14336, symmetric codes: 196 -> 189-190 us
-  // per call; two slots, with a wait for the next group's codes in the middle
-  // of each group, 192-193 us.)
+  // per call, then 182 us with the LDS read placed as below; two slots, with a
+  // wait for the next group's codes in the middle of each group, 192-193 us.)
   const int G8 = G >> 3;                                   // DEEP: K % 1024 == 0
   const uint32_t lds_code = static_cast<uint32_t>(reinterpret_cast<size_t>(smem)) + DEEP_OC + wave * 4096;
   auto code_copy = [&](int g, int slot) __attribute__((always_inline)) {
@@ -389,7 +389,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_t2_kernel(
       constexpr int pi = (c - 1) >> 1, pj = (c - 1) & 1;
       fold(dprev, pi, pj, pj ? s1 : s0, g);
       if (j == 0 && i < 3) a_read(IntC<BUF>{}, IntC<i + 1>{}, aop[(i + 1) & 1]);
-      if (DEEP && c == 5) {
+      if (DEEP && c == 6) {
+        // (read during chain (3,0): measured at M=2048, K=4096, N=14336,
+        // 181.6-182.8 us; during chain (1,1), (2,1) or (3,1), 187-189 us)
         // group g + 1's codes landed before the end of group g - 1 (PARTIALS
         // stores in fold, and stores count in vmcnt too: that path waits for
         // every copy here and at the end of the group)
